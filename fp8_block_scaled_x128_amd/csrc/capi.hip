@@ -1,0 +1,272 @@
+// C ABI of libfp8bs: argument validation, device check and dispatch to the
+// kernel launchers.  Declarations and the contract of every entry point are
+// in include/fp8bs.h.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fp8bs.h"
+#include "internal.h"
+
+using namespace fp8bs;
+
+namespace {
+
+thread_local char g_detail[512];
+
+fp8bs_status fail(fp8bs_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fp8bs_status ok() {
+    g_detail[0] = '\0';
+    return FP8BS_OK;
+}
+
+// Per-device result of the gfx950 check: 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_dev_ok[64];
+
+fp8bs_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(FP8BS_ERR_DEVICE, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(FP8BS_ERR_DEVICE, "device index %d out of range", dev);
+    int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(FP8BS_ERR_DEVICE, "hipGetDeviceProperties failed");
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    if (st != 1) return fail(FP8BS_ERR_DEVICE, "current device %d is not gfx950", dev);
+    return FP8BS_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fp8bs_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FP8BS_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr int64_t kMaxRuns = (int64_t)1 << 30;   // row-group kernels index runs with int32
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8bs_status_string(fp8bs_status s) {
+    switch (s) {
+        case FP8BS_OK: return "FP8BS_OK";
+        case FP8BS_ERR_NULL: return "FP8BS_ERR_NULL";
+        case FP8BS_ERR_SHAPE: return "FP8BS_ERR_SHAPE";
+        case FP8BS_ERR_STRIDE: return "FP8BS_ERR_STRIDE";
+        case FP8BS_ERR_ALIGN: return "FP8BS_ERR_ALIGN";
+        case FP8BS_ERR_UNSUPPORTED: return "FP8BS_ERR_UNSUPPORTED";
+        case FP8BS_ERR_DEVICE: return "FP8BS_ERR_DEVICE";
+    }
+    return "FP8BS_UNKNOWN_STATUS";
+}
+
+const char* fp8bs_last_error_detail(void) { return g_detail; }
+
+fp8bs_status fp8_quant_rowblock(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, fp8bs_axis axis,
+                                uint8_t* q, int64_t ld_q, float* s, int64_t s_stride_row, int64_t s_stride_group,
+                                hipStream_t stream) {
+    if (axis != FP8BS_AXIS_ROW && axis != FP8BS_AXIS_COL) return fail(FP8BS_ERR_UNSUPPORTED, "axis %d", (int)axis);
+    if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    if (cols % 8) return fail(FP8BS_ERR_SHAPE, "cols %% 8 != 0 (cols=%lld)", (long long)cols);
+    if (axis == FP8BS_AXIS_COL && rows % 16) return fail(FP8BS_ERR_SHAPE, "AXIS_COL needs rows %% 16 == 0");
+    if (rows * ((cols + 127) / 128) > kMaxRuns || rows > INT32_MAX / 2 || cols > INT32_MAX / 2)
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || cols == 0) return ok();
+    if (!x || !q || !s) return fail(FP8BS_ERR_NULL, "x, q and s are required");
+    if (ld_x < cols) return fail(FP8BS_ERR_STRIDE, "ld_x < cols");
+    if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (axis == FP8BS_AXIS_ROW) {
+        if (ld_q < cols) return fail(FP8BS_ERR_STRIDE, "ld_q < cols");
+        if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    } else {
+        if (ld_q < rows) return fail(FP8BS_ERR_STRIDE, "ld_q < rows (transposed output)");
+        if (ld_q % 16 || !aligned(q, 16)) return fail(FP8BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
+    }
+    if (!aligned(s, 4)) return fail(FP8BS_ERR_ALIGN, "s must be 4-byte aligned");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    if (axis == FP8BS_AXIS_ROW)
+        return launched(launch_quant_1x128(x, rows, cols, ld_x, q, ld_q, s, s_stride_row, s_stride_group, stream),
+                        "fp8_quant_rowblock");
+    return launched(launch_quant_128x1_t(x, rows, cols, ld_x, q, ld_q, s, s_stride_row, s_stride_group, stream),
+                    "fp8_quant_rowblock");
+}
+
+fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, int64_t cols, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt, float* s, hipStream_t stream) {
+    if (batch < 1 || rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "batch=%lld rows=%lld cols=%lld",
+                                                      (long long)batch, (long long)rows, (long long)cols);
+    if (cols % 8) return fail(FP8BS_ERR_SHAPE, "cols %% 8 != 0");
+    if (q_t && rows % 16) return fail(FP8BS_ERR_SHAPE, "a transposed copy needs rows %% 16 == 0");
+    if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2 || batch > 65535 || (rows + 127) / 128 > 65535)
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || cols == 0) return ok();
+    if (!w || !q || !s) return fail(FP8BS_ERR_NULL, "w, q and s are required");
+    if (ld_w < cols || ld_q < cols) return fail(FP8BS_ERR_STRIDE, "ld_w and ld_q must be >= cols");
+    if (q_t && ld_qt < rows) return fail(FP8BS_ERR_STRIDE, "ld_qt < rows");
+    if (ld_w % 8 || !aligned(w, 16)) return fail(FP8BS_ERR_ALIGN, "w must be 16-byte aligned with ld_w %% 8 == 0");
+    if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    if (q_t && (ld_qt % 16 || !aligned(q_t, 16))) return fail(FP8BS_ERR_ALIGN, "q_t must be 16-byte aligned with ld_qt %% 16 == 0");
+    if (!aligned(s, 4)) return fail(FP8BS_ERR_ALIGN, "s must be 4-byte aligned");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_quant_128x128(w, batch, rows, cols, ld_w, q, ld_q, q_t, ld_qt, s, stream),
+                    "fp8_quant_block2d");
+}
+
+static fp8bs_status check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda, const void* b,
+                                      int64_t ldb, const void* c, int64_t ldc, int out, int kmul) {
+    if (M < 0 || N < 0 || K < 0) return fail(FP8BS_ERR_SHAPE, "negative size");
+    if (K % kmul) return fail(FP8BS_ERR_SHAPE, "K %% %d != 0 (K=%lld)", kmul, (long long)K);
+    if (N % 128) return fail(FP8BS_ERR_SHAPE, "N %% 128 != 0 (N=%lld)", (long long)N);
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return fail(FP8BS_ERR_SHAPE, "size too large");
+    if (out != FP8BS_OUT_BF16 && out != FP8BS_OUT_FP32) return fail(FP8BS_ERR_UNSUPPORTED, "out %d", out);
+    if (M == 0 || N == 0) return FP8BS_OK;
+    if (K == 0) return fail(FP8BS_ERR_SHAPE, "K == 0");
+    if (!a || !b || !c) return fail(FP8BS_ERR_NULL, "a, b and c are required");
+    if (lda < K || ldb < K || ldc < N) return fail(FP8BS_ERR_STRIDE, "lda, ldb must be >= K and ldc >= N");
+    if (lda % 16 || ldb % 16 || !aligned(a, 16) || !aligned(b, 16))
+        return fail(FP8BS_ERR_ALIGN, "a, b must be 16-byte aligned with lda, ldb %% 16 == 0");
+    if (ldc % 8 || !aligned(c, 16)) return fail(FP8BS_ERR_ALIGN, "c must be 16-byte aligned with ldc %% 8 == 0");
+    return FP8BS_OK;
+}
+
+fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                                  int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                                  const float* sb, int64_t sb_stride_n, int64_t sb_stride_k, fp8bs_bscale bscale,
+                                  void* c, int64_t ldc, fp8bs_out out, hipStream_t stream) {
+    if (bscale != FP8BS_BSCALE_BLOCK128 && bscale != FP8BS_BSCALE_ROW128)
+        return fail(FP8BS_ERR_UNSUPPORTED, "bscale %d", (int)bscale);
+    fp8bs_status v = check_gemm_common(M, N, K, a, lda, b, ldb, c, ldc, out, 128);
+    if (v != FP8BS_OK) return v;
+    if (M == 0 || N == 0) return ok();
+    if (!sa || !sb) return fail(FP8BS_ERR_NULL, "sa and sb are required");
+    if (!aligned(sa, 4) || !aligned(sb, 4)) return fail(FP8BS_ERR_ALIGN, "scales must be 4-byte aligned");
+    if ((uint64_t)M * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
+        return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.a = a; g.lda = lda; g.sa = sa; g.sa_sm = sa_stride_m; g.sa_sk = sa_stride_k;
+    g.b = b; g.ldb = ldb; g.b_sg = 0; g.sb = sb; g.sb_sg = 0; g.sb_sn = sb_stride_n; g.sb_sk = sb_stride_k;
+    g.bscale_row = bscale == FP8BS_BSCALE_ROW128; g.c = c; g.ldc = ldc; g.out_f32 = out == FP8BS_OUT_FP32;
+    return launched(launch_gemm_blockscaled(g, stream), "fp8_blockscaled_gemm");
+}
+
+fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t G, const int32_t* offsets,
+                              const int32_t* a_rows, int64_t a_count, const uint8_t* a, int64_t lda, const float* sa,
+                              int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                              int64_t b_stride_g, const float* sb, int64_t sb_stride_g, int64_t sb_stride_n,
+                              int64_t sb_stride_k, void* c, int64_t ldc, fp8bs_out out, hipStream_t stream) {
+    if (G < 1) return fail(FP8BS_ERR_SHAPE, "G must be >= 1");
+    fp8bs_status v = check_gemm_common(total_rows, N, K, a, lda, b, ldb, c, ldc, out, 128);
+    if (v != FP8BS_OK) return v;
+    if (total_rows == 0 || N == 0) return ok();
+    if (!offsets || !sa || !sb) return fail(FP8BS_ERR_NULL, "offsets, sa and sb are required");
+    if (b_stride_g % 16) return fail(FP8BS_ERR_ALIGN, "b_stride_g %% 16 != 0");
+    if (!aligned(sa, 4) || !aligned(sb, 4) || !aligned(offsets, 4)) return fail(FP8BS_ERR_ALIGN, "misaligned scales/offsets");
+    const int64_t arows = a_rows ? a_count : total_rows;
+    if (a_rows && a_count < 1) return fail(FP8BS_ERR_SHAPE, "a_count must be >= 1 with a_rows");
+    if ((uint64_t)arows * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
+        return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
+    if ((total_rows + 255) / 256 + G > 65535) return fail(FP8BS_ERR_SHAPE, "too many row tiles");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    GemmArgs g{};
+    g.M = total_rows; g.N = N; g.K = K; g.a = a; g.lda = lda; g.sa = sa; g.sa_sm = sa_stride_m; g.sa_sk = sa_stride_k;
+    g.b = b; g.ldb = ldb; g.b_sg = b_stride_g; g.sb = sb; g.sb_sg = sb_stride_g; g.sb_sn = sb_stride_n;
+    g.sb_sk = sb_stride_k; g.bscale_row = 0; g.c = c; g.ldc = ldc; g.out_f32 = out == FP8BS_OUT_FP32;
+    g.G = G; g.offsets = offsets; g.a_rows = a_rows;
+    return launched(launch_gemm_grouped(g, stream), "fp8_grouped_gemm");
+}
+
+fp8bs_status fp8_silu_mul_quant(const uint16_t* gate_up, int64_t rows, int64_t I, int64_t ld_in, int mx, uint8_t* q,
+                                int64_t ld_q, void* s, int64_t s_stride_row, int64_t s_stride_group, uint16_t* h_out,
+                                int64_t ld_h, hipStream_t stream) {
+    if (mx != 0 && mx != 1) return fail(FP8BS_ERR_UNSUPPORTED, "mx %d", mx);
+    if (rows < 0 || I < 0) return fail(FP8BS_ERR_SHAPE, "negative size");
+    if (I % (mx ? 32 : 128)) return fail(FP8BS_ERR_SHAPE, "I %% %d != 0", mx ? 32 : 128);
+    if (rows * ((I + 127) / 128) > kMaxRuns || rows > INT32_MAX / 2 || I > INT32_MAX / 4)
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || I == 0) return ok();
+    if (!gate_up || !q || !s) return fail(FP8BS_ERR_NULL, "gate_up, q and s are required");
+    if (ld_in < 2 * I || ld_q < I || (h_out && ld_h < I)) return fail(FP8BS_ERR_STRIDE, "leading dimension too small");
+    if (ld_in % 8 || !aligned(gate_up, 16)) return fail(FP8BS_ERR_ALIGN, "gate_up must be 16-byte aligned, ld_in %% 8 == 0");
+    if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    if (h_out && (ld_h % 8 || !aligned(h_out, 16))) return fail(FP8BS_ERR_ALIGN, "h_out must be 16-byte aligned, ld_h %% 8 == 0");
+    if (!mx && !aligned(s, 4)) return fail(FP8BS_ERR_ALIGN, "s must be 4-byte aligned");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_silu_mul_quant(gate_up, rows, I, ld_in, mx, q, ld_q, s, s_stride_row, s_stride_group, h_out,
+                                          ld_h, stream),
+                    "fp8_silu_mul_quant");
+}
+
+fp8bs_status mxfp8_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                         uint8_t* s, int64_t s_stride_row, int64_t s_stride_group, hipStream_t stream) {
+    if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "negative size");
+    if (cols % 32) return fail(FP8BS_ERR_SHAPE, "cols %% 32 != 0");
+    if (rows * ((cols + 127) / 128) > kMaxRuns || rows > INT32_MAX / 2 || cols > INT32_MAX / 2)
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || cols == 0) return ok();
+    if (!x || !q || !s) return fail(FP8BS_ERR_NULL, "x, q and s are required");
+    if (ld_x < cols || ld_q < cols) return fail(FP8BS_ERR_STRIDE, "ld_x and ld_q must be >= cols");
+    if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_mx_quant(x, rows, cols, ld_x, q, ld_q, s, s_stride_row, s_stride_group, stream), "mxfp8_quant");
+}
+
+fp8bs_status mxfp8_gemm(int64_t rows, int64_t N, int64_t K, int32_t G, const int32_t* offsets, const int32_t* a_rows,
+                        int64_t a_count, const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t lds_a,
+                        const uint8_t* b, int64_t ldb, int64_t b_stride_g, const uint8_t* sb, int64_t lds_b,
+                        int64_t sb_stride_g, void* c, int64_t ldc, fp8bs_out out, hipStream_t stream) {
+    if (G < 0) return fail(FP8BS_ERR_SHAPE, "G < 0");
+    fp8bs_status v = check_gemm_common(rows, N, K, a, lda, b, ldb, c, ldc, out, 128);
+    if (v != FP8BS_OK) return v;
+    if (rows == 0 || N == 0) return ok();
+    if (!sa || !sb) return fail(FP8BS_ERR_NULL, "sa and sb are required");
+    if (G > 0 && !offsets) return fail(FP8BS_ERR_NULL, "offsets required when G > 0");
+    if (lds_a < K / 32 || lds_b < K / 32) return fail(FP8BS_ERR_STRIDE, "scale leading dimension < K/32");
+    if (lds_a % 4 || lds_b % 4 || !aligned(sa, 4) || !aligned(sb, 4))
+        return fail(FP8BS_ERR_ALIGN, "scale arrays must be 4-byte aligned with lds %% 4 == 0");
+    if (G > 0 && b_stride_g % 16) return fail(FP8BS_ERR_ALIGN, "b_stride_g %% 16 != 0");
+    const int64_t arows = (G > 0 && a_rows) ? a_count : rows;
+    if (G > 0 && a_rows && a_count < 1) return fail(FP8BS_ERR_SHAPE, "a_count must be >= 1 with a_rows");
+    if ((uint64_t)arows * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
+        return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
+    if ((rows + 255) / 256 + G > 65535) return fail(FP8BS_ERR_SHAPE, "too many row tiles");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    MxGemmArgs g{};
+    g.M = rows; g.N = N; g.K = K; g.a = a; g.lda = lda; g.sa = sa; g.lds_a = lds_a;
+    g.b = b; g.ldb = ldb; g.b_sg = G > 0 ? b_stride_g : 0; g.sb = sb; g.lds_b = lds_b; g.sb_sg = G > 0 ? sb_stride_g : 0;
+    g.c = c; g.ldc = ldc; g.out_f32 = out == FP8BS_OUT_FP32; g.G = G; g.offsets = G > 0 ? offsets : nullptr;
+    g.a_rows = G > 0 ? a_rows : nullptr;
+    return launched(launch_gemm_mx(g, stream), "mxfp8_gemm");
+}
+
+fp8bs_status fp8bs_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+    if (n < 0) return fail(FP8BS_ERR_SHAPE, "n < 0");
+    if (n == 0) return ok();
+    if (!in || !out) return fail(FP8BS_ERR_NULL, "in and out are required");
+    if (!aligned(in, 4)) return fail(FP8BS_ERR_ALIGN, "in must be 4-byte aligned");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_e4m3_encode(in, out, n, stream), "fp8bs_e4m3_encode");
+}
+
+}  // extern "C"

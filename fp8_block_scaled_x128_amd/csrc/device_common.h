@@ -1,0 +1,97 @@
+// Device helpers shared by the HIP kernels of libfp8bs (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+// bf16 halves of a 32-bit word -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Largest finite OCP E4M3FN value.
+constexpr float kE4M3Max = 448.0f;
+
+// gfx950's v_cvt_pk_fp8_f32 produces OCP E4M3FN codes with round-to-nearest-
+// even, but maps |v| >= 464 to NaN instead of saturating.  Clamping to +-448
+// first gives the saturating encoding for every finite input (clamping
+// leaves values inside the range untouched and sends the rest to +-448,
+// which is what saturating rounding returns for them).
+__device__ __forceinline__ float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max); }
+
+// Encode 4 fp32 values into one 32-bit word of E4M3 codes (byte i = value i).
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+    return (uint32_t)w;
+}
+
+// Quotient x / s rounded to nearest fp32, given y = RN(1 / s) and s >= 2^-80:
+// q0 = RN(x y), r = RN(x - s q0) (one FMA), q = RN(q0 + r y) (one FMA).  For
+// binary32 operands whose significands are those of bf16 values (x) and of
+// RN(bf16 / 448) (s), this sequence returns exactly RN(x / s): the rounding
+// depends only on the two significands when nothing under- or overflows,
+// and all 128 x 128 significand pairs were checked against the exact
+// quotient.  Quotients small enough for intermediates to underflow lie far
+// below the smallest E4M3 subnormal and encode to a signed zero either way;
+// copysign keeps the sign of x (and of -0).
+__device__ __forceinline__ float div_by_scale(float x, float s, float y) {
+    float q0 = x * y;
+    float r = __builtin_fmaf(-q0, s, x);
+    float q1 = __builtin_fmaf(r, y, q0);
+    return __builtin_copysignf(q1, x);
+}
+
+// Scale threshold above which div_by_scale is exact (see above).
+constexpr float kFastDivMinScale = 0x1p-80f;
+
+// Max of |v| over the 16 lanes of an aligned lane group (xor butterfly inside
+// a DPP row).
+__device__ __forceinline__ float group16_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1, 16));
+    v = fmaxf(v, __shfl_xor(v, 2, 16));
+    v = fmaxf(v, __shfl_xor(v, 4, 16));
+    v = fmaxf(v, __shfl_xor(v, 8, 16));
+    return v;
+}
+__device__ __forceinline__ float group4_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1, 4));
+    v = fmaxf(v, __shfl_xor(v, 2, 4));
+    return v;
+}
+
+// MX block exponent: smallest e with amax <= 448 * 2^e, clamped to
+// [-127, 127]; -127 for amax == 0.  Exact, on the fp32 bit pattern.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    uint32_t a = __float_as_uint(amax) & 0x7fffffffu;
+    if (a == 0) return -127;
+    int ea;
+    uint32_t frac;
+    if ((a >> 23) == 0) {                       // subnormal: normalize
+        int p = 31 - __clz((int)a);             // highest set bit, value = 2^(p - 149) * 1.f
+        ea = p - 149;
+        frac = (a << (23 - p)) & 0x7fffffu;
+    } else {
+        ea = (int)(a >> 23) - 127;
+        frac = a & 0x7fffffu;
+    }
+    int e = (frac <= 0x600000u) ? ea - 8 : ea - 7;   // 448 = 1.75 * 2^8
+    e = e < -127 ? -127 : e;
+    e = e > 127 ? 127 : e;
+    return e;
+}
+
+// 2^-e as an fp32 (e in [-127, 127]; 2^-127 is an fp32 subnormal).
+__device__ __forceinline__ float pow2_neg(int e) {
+    int be = 127 - e;
+    return be >= 1 ? __uint_as_float((uint32_t)be << 23) : __uint_as_float(1u << (22 + be));
+}
+
+}  // namespace fp8bs

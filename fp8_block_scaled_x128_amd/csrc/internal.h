@@ -1,0 +1,46 @@
+// Internal launch interface between the C-ABI layer (capi.hip) and the kernel
+// files.  Launchers assume their arguments were validated by capi.hip.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+// quant.hip
+hipError_t launch_quant_1x128(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                              int64_t ld_q, float* s, int64_t ssr, int64_t ssg, hipStream_t st);
+hipError_t launch_quant_128x1_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt,
+                                int64_t ld_qt, float* s, int64_t ssr, int64_t ssg, hipStream_t st);
+hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, int64_t cols, int64_t ld_w,
+                                uint8_t* q, int64_t ld_q, uint8_t* qt, int64_t ld_qt, float* s, hipStream_t st);
+hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                           uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st);
+hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t rows, int64_t I, int64_t ld_in, int mx, uint8_t* q,
+                                 int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint16_t* h, int64_t ld_h,
+                                 hipStream_t st);
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st);
+
+// gemm.hip
+struct GemmArgs {
+    int64_t M, N, K;                 // M = total rows (grouped: rows of all groups)
+    const uint8_t* a; int64_t lda;
+    const float* sa; int64_t sa_sm, sa_sk;
+    const uint8_t* b; int64_t ldb; int64_t b_sg;          // b_sg: expert stride (grouped)
+    const float* sb; int64_t sb_sg, sb_sn, sb_sk;
+    int bscale_row;                  // 0: sb indexed by n/128, 1: by n
+    void* c; int64_t ldc; int out_f32;
+    int32_t G; const int32_t* offsets; const int32_t* a_rows;   // grouped only
+};
+hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st);
+
+struct MxGemmArgs {
+    int64_t M, N, K;
+    const uint8_t* a; int64_t lda; const uint8_t* sa; int64_t lds_a;
+    const uint8_t* b; int64_t ldb; int64_t b_sg; const uint8_t* sb; int64_t lds_b; int64_t sb_sg;
+    void* c; int64_t ldc; int out_f32;
+    int32_t G; const int32_t* offsets; const int32_t* a_rows;
+};
+hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st);
+
+}  // namespace fp8bs

@@ -1,0 +1,390 @@
+// Quantization kernels of libfp8bs (gfx950).
+//
+// Each group of values gets S = max|x| / 448 (IEEE fp32 division) and codes
+// E4M3(x / S) with round-to-nearest-even and saturation, the two-step
+// quantizer of "Unified FP8: Beyond Mixed Precision..." (section "FP8
+// Quantization", Steps 1 and 2), with the groupings of "Low Precision RL"
+// (table "Choose a precision"): 1x128 per-token groups, 128x1 token-axis
+// groups for the weight-gradient operands, 128x128 weight blocks, and 1x32
+// MXFP8 blocks with power-of-two (UE8M0) scales.
+//
+// All kernels are HBM-bound.  They read bf16 with 16-byte loads (8 values
+// per lane), reduce the group maximum with lane shuffles inside the 16-lane
+// DPP row that owns a 1x128 group, and write codes with 8- or 16-byte stores.
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8bs {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Codes of 8 values of one group given its scale s (S == 0 -> all 0x00).
+__device__ __forceinline__ void encode8(const float v[8], float s, uint32_t& w0, uint32_t& w1) {
+    float qv[8];
+    if (s >= kFastDivMinScale) {
+        const float y = 1.0f / s;                 // IEEE division: y = RN(1/s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = div_by_scale(v[i], s, y);
+    } else if (s > 0.0f) {                        // subnormal-range scales: plain IEEE division
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = v[i] / s;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = 0.0f;
+    }
+    w0 = enc4(qv[0], qv[1], qv[2], qv[3]);
+    w1 = enc4(qv[4], qv[5], qv[6], qv[7]);
+}
+
+__device__ __forceinline__ void unpack8(const uint4 raw, float v[8]) {
+    v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x);
+    v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
+    v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z);
+    v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+}
+
+__device__ __forceinline__ float absmax8(const float v[8]) {
+    float m = fabsf(v[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    return m;
+}
+
+// silu(g) * u rounded to bf16 and widened back (the value the next GEMM consumes).
+__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+    float sg = g / (1.0f + expf(-g));
+    return f32_to_bf16_rne(sg * u);
+}
+
+// ---------------------------------------------------------------------------
+// Row-group quantizer.  A 16-lane DPP row owns one 128-wide run of a row
+// (8 values per lane); it holds one 1x128 FP32-scale group, or four 1x32 MX
+// blocks (4 lanes each).  SILU: the run is h = silu(gate) * up computed from
+// the gate (columns [0, I)) and up (columns [I, 2I)) halves of the input row.
+// ROW_FAST: consecutive runs go down a column of groups (so that M-major
+// scale arrays are written contiguously); otherwise along a row.
+// Each 16-lane row processes U runs per loop trip with all loads issued first.
+// ---------------------------------------------------------------------------
+struct RowArgs {
+    const uint16_t* x; int64_t ld_x;
+    int32_t rows, cols;          // cols: width of the quantized matrix (I for SILU)
+    int64_t up_off;              // SILU: column offset of the up half
+    uint8_t* q; int64_t ld_q;
+    void* s; int64_t ssr, ssg;
+    uint16_t* h; int64_t ld_h;   // SILU: optional bf16 h output
+    int32_t runs_per_row, total_runs;
+};
+
+template <bool SILU, bool MX, bool ROW_FAST, int U>
+__global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
+    const int sub = threadIdx.x & 15;
+    const int32_t rid = (int32_t)blockIdx.x * (kThreads / 16) + (int32_t)(threadIdx.x >> 4);
+    const int32_t nr = (int32_t)gridDim.x * (kThreads / 16);
+    for (int32_t base = rid; base < p.total_runs; base += nr * U) {
+        uint4 raw[U], raw_u[U];
+        int32_t rr[U], gg[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t run = base + u * nr;
+            int32_t r, g;
+            if (ROW_FAST) { g = run / p.rows; r = run - g * p.rows; }
+            else { r = run / p.runs_per_row; g = run - r * p.runs_per_row; }
+            rr[u] = r; gg[u] = g;
+            const int32_t c = g * 128 + sub * 8;
+            raw[u] = make_uint4(0, 0, 0, 0);
+            raw_u[u] = make_uint4(0, 0, 0, 0);
+            if (run < p.total_runs && c < p.cols) {
+                const uint16_t* src = p.x + (int64_t)r * p.ld_x + c;
+                raw[u] = *reinterpret_cast<const uint4*>(src);
+                if (SILU) raw_u[u] = *reinterpret_cast<const uint4*>(src + p.up_off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t run = base + u * nr;
+            const int32_t r = rr[u], g = gg[u];
+            const int32_t c = g * 128 + sub * 8;
+            const bool valid = run < p.total_runs && c < p.cols;
+            float v[8];
+            unpack8(raw[u], v);
+            if (SILU) {
+                float up[8];
+                unpack8(raw_u[u], up);
+                uint32_t hb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    hb[i] = silu_mul_bf16(v[i], up[i]);
+                    v[i] = __uint_as_float(hb[i] << 16);
+                }
+                if (p.h != nullptr && valid) {
+                    uint4 hw = make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
+                                          hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16));
+                    *reinterpret_cast<uint4*>(p.h + (int64_t)r * p.ld_h + c) = hw;
+                }
+            }
+            uint32_t w0, w1;
+            if (!MX) {
+                const float amax = group16_max(absmax8(v));
+                const float s = amax / kE4M3Max;
+                encode8(v, s, w0, w1);
+                if (valid && sub == 0)
+                    static_cast<float*>(p.s)[(int64_t)r * p.ssr + (int64_t)g * p.ssg] = s;
+            } else {
+                const float amax = group4_max(absmax8(v));
+                const int e = mx_exponent(amax);
+                const float f = pow2_neg(e);
+                if (amax == 0.0f) {
+                    w0 = 0u; w1 = 0u;
+                } else {
+                    w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+                    w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+                }
+                if (valid && (sub & 3) == 0)
+                    static_cast<uint8_t*>(p.s)[(int64_t)r * p.ssr + (int64_t)(g * 4 + (sub >> 2)) * p.ssg] =
+                        (uint8_t)(e + 127);
+            }
+            if (valid) *reinterpret_cast<uint2*>(p.q + (int64_t)r * p.ld_q + c) = make_uint2(w0, w1);
+        }
+    }
+}
+
+template <bool SILU, bool MX>
+hipError_t launch_rowgroup(RowArgs p, bool row_fast, hipStream_t st) {
+    constexpr int U = 4;
+    if (p.total_runs == 0) return hipSuccess;
+    const int64_t rows16 = ((int64_t)p.total_runs + U - 1) / U;            // 16-lane rows needed
+    int64_t blocks = (rows16 + (kThreads / 16) - 1) / (kThreads / 16);
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    if (row_fast)
+        hipLaunchKernelGGL((k_rowgroup<SILU, MX, true, U>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_rowgroup<SILU, MX, false, U>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 128x1 token-axis groups with transposed output.  Tile: 128 rows x 64 cols,
+// staged in LDS as [column pair][row] words (a word is a bf16 pair of one
+// row).  Thread t then owns column t/4 and rows 32*(t%4) .. +32; the four
+// threads of a column reduce the 128-row maximum with shuffles and each
+// writes 32 contiguous codes of the transposed row.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) k_quant_128x1_t(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
+                                                            int64_t ld_x, uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                            float* __restrict__ s, int64_t ssr, int64_t ssg) {
+    __shared__ __attribute__((aligned(16))) uint32_t tile[32][132];
+    const int t = threadIdx.x;
+    const int32_t r0 = (int32_t)blockIdx.y * 128;
+    const int32_t c0 = (int32_t)blockIdx.x * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rl = (t >> 3) + 32 * i;
+        const int cc = t & 7;
+        const int32_t r = r0 + rl, c = c0 + cc * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(x + (int64_t)r * ld_x + c);
+        tile[cc * 4 + 0][rl] = v.x;
+        tile[cc * 4 + 1][rl] = v.y;
+        tile[cc * 4 + 2][rl] = v.z;
+        tile[cc * 4 + 3][rl] = v.w;
+    }
+    __syncthreads();
+    const int cl = t >> 2, rq = t & 3;
+    const bool hi = (cl & 1) != 0;
+    float v[32];
+    const uint4* src = reinterpret_cast<const uint4*>(&tile[cl >> 1][rq * 32]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 w = src[i];
+        v[4 * i + 0] = hi ? bf16_hi(w.x) : bf16_lo(w.x);
+        v[4 * i + 1] = hi ? bf16_hi(w.y) : bf16_lo(w.y);
+        v[4 * i + 2] = hi ? bf16_hi(w.z) : bf16_lo(w.z);
+        v[4 * i + 3] = hi ? bf16_hi(w.w) : bf16_lo(w.w);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = group4_max(m);
+    const float sc = m / kE4M3Max;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) encode8(&v[8 * i], sc, w[2 * i], w[2 * i + 1]);
+    const int32_t c = c0 + cl;
+    if (c < cols) {
+        const int32_t rs = r0 + rq * 32;
+        uint8_t* dst = qt + (int64_t)c * ld_qt + rs;
+        if (rs < rows) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (rs + 16 < rows) *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        if (rq == 0) s[(int64_t)c * ssr + (int64_t)blockIdx.y * ssg] = sc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 block quantizer, one workgroup per block, one HBM read of the
+// block.  Optional transposed copy: the block's codes are staged in LDS and
+// re-read as 4x4 byte squares that are transposed in registers (v_perm).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t o[4]) {
+    // byte i of __builtin_amdgcn_perm(a, b, sel) is byte sel_i of {a:b}
+    // (selectors 0-3 pick b's bytes, 4-7 pick a's bytes).
+    const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+    o[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+template <bool TRANS>
+__global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __restrict__ w, int32_t rows, int32_t cols,
+                                                            int64_t ld_w, uint8_t* __restrict__ q, int64_t ld_q,
+                                                            uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                            float* __restrict__ s, int32_t nbr, int32_t nbc) {
+    __shared__ float red[kThreads / 64];
+    __shared__ __attribute__((aligned(16))) uint32_t ctile[TRANS ? 128 : 1][33];
+    const int t = threadIdx.x;
+    const int64_t bz = blockIdx.z;
+    w += bz * (int64_t)rows * ld_w;
+    q += bz * (int64_t)rows * ld_q;
+    if (TRANS) qt += bz * (int64_t)cols * ld_qt;
+    s += bz * (int64_t)nbr * nbc;
+    const int32_t r0 = (int32_t)blockIdx.y * 128, c0 = (int32_t)blockIdx.x * 128;
+    const int cc = t & 15;
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int32_t r = r0 + (t >> 4) + 16 * i, c = c0 + cc * 8;
+        raw[i] = make_uint4(0, 0, 0, 0);
+        if (r < rows && c < cols) raw[i] = *reinterpret_cast<const uint4*>(w + (int64_t)r * ld_w + c);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float v[8];
+        unpack8(raw[i], v);
+        m = fmaxf(m, absmax8(v));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = m / kE4M3Max;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float v[8];
+        unpack8(raw[i], v);
+        uint32_t w0, w1;
+        encode8(v, sc, w0, w1);
+        const int rl = (t >> 4) + 16 * i;
+        const int32_t r = r0 + rl, c = c0 + cc * 8;
+        if (r < rows && c < cols) *reinterpret_cast<uint2*>(q + (int64_t)r * ld_q + c) = make_uint2(w0, w1);
+        if (TRANS) { ctile[rl][2 * cc] = w0; ctile[rl][2 * cc + 1] = w1; }
+    }
+    if (t == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = sc;
+    if (TRANS) {
+        __syncthreads();
+        // thread -> 4 columns (cb) x 16 rows (rb); 8 consecutive lanes cover one
+        // 128-byte row segment of the transposed output.
+        const int rb = t & 7, cb = t >> 3;
+        uint32_t col[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = rb * 16 + 4 * j;
+            uint32_t o[4];
+            transpose4x4(ctile[rr][cb], ctile[rr + 1][cb], ctile[rr + 2][cb], ctile[rr + 3][cb], o);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) col[k][j] = o[k];
+        }
+        const int32_t rs = r0 + rb * 16;
+        if (rs < rows) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int32_t c = c0 + cb * 4 + k;
+                if (c < cols)
+                    *reinterpret_cast<uint4*>(qt + (int64_t)c * ld_qt + rs) =
+                        make_uint4(col[k][0], col[k][1], col[k][2], col[k][3]);
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) k_e4m3_encode(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                                          int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        const uint32_t w = enc4(in[i], in[i + 1], in[i + 2], in[i + 3]);
+        out[i] = (uint8_t)w; out[i + 1] = (uint8_t)(w >> 8); out[i + 2] = (uint8_t)(w >> 16); out[i + 3] = (uint8_t)(w >> 24);
+    } else {
+        for (int64_t j = i; j < n; ++j) out[j] = (uint8_t)enc4(in[j], 0.f, 0.f, 0.f);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_1x128(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                              float* s, int64_t ssr, int64_t ssg, hipStream_t st) {
+    RowArgs p{};
+    p.x = x; p.ld_x = ld_x; p.rows = (int32_t)rows; p.cols = (int32_t)cols; p.up_off = 0;
+    p.q = q; p.ld_q = ld_q; p.s = s; p.ssr = ssr; p.ssg = ssg; p.h = nullptr; p.ld_h = 0;
+    p.runs_per_row = (int32_t)((cols + 127) / 128);
+    p.total_runs = (int32_t)(rows * p.runs_per_row);
+    return launch_rowgroup<false, false>(p, ssr == 1 && ssg != 1, st);
+}
+
+hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                           uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st) {
+    RowArgs p{};
+    p.x = x; p.ld_x = ld_x; p.rows = (int32_t)rows; p.cols = (int32_t)cols; p.up_off = 0;
+    p.q = q; p.ld_q = ld_q; p.s = s; p.ssr = ssr; p.ssg = ssg; p.h = nullptr; p.ld_h = 0;
+    p.runs_per_row = (int32_t)((cols + 127) / 128);
+    p.total_runs = (int32_t)(rows * p.runs_per_row);
+    return launch_rowgroup<false, true>(p, ssr == 1 && ssg != 1, st);
+}
+
+hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t rows, int64_t I, int64_t ld_in, int mx, uint8_t* q,
+                                 int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint16_t* h, int64_t ld_h,
+                                 hipStream_t st) {
+    RowArgs p{};
+    p.x = gu; p.ld_x = ld_in; p.rows = (int32_t)rows; p.cols = (int32_t)I; p.up_off = I;
+    p.q = q; p.ld_q = ld_q; p.s = s; p.ssr = ssr; p.ssg = ssg; p.h = h; p.ld_h = ld_h;
+    p.runs_per_row = (int32_t)((I + 127) / 128);
+    p.total_runs = (int32_t)(rows * p.runs_per_row);
+    const bool rf = ssr == 1 && ssg != 1;
+    return mx ? launch_rowgroup<true, true>(p, rf, st) : launch_rowgroup<true, false>(p, rf, st);
+}
+
+hipError_t launch_quant_128x1_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt,
+                                int64_t ld_qt, float* s, int64_t ssr, int64_t ssg, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
+    hipLaunchKernelGGL(k_quant_128x1_t, grid, dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, qt, ld_qt,
+                       s, ssr, ssg);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, int64_t cols, int64_t ld_w,
+                                uint8_t* q, int64_t ld_q, uint8_t* qt, int64_t ld_qt, float* s, hipStream_t st) {
+    if (rows == 0 || cols == 0 || batch == 0) return hipSuccess;
+    const int32_t nbr = (int32_t)((rows + 127) / 128), nbc = (int32_t)((cols + 127) / 128);
+    dim3 grid((unsigned)nbc, (unsigned)nbr, (unsigned)batch);
+    if (qt)
+        hipLaunchKernelGGL(k_quant_128x128<true>, grid, dim3(kThreads), 0, st, w, (int32_t)rows, (int32_t)cols, ld_w, q,
+                           ld_q, qt, ld_qt, s, nbr, nbc);
+    else
+        hipLaunchKernelGGL(k_quant_128x128<false>, grid, dim3(kThreads), 0, st, w, (int32_t)rows, (int32_t)cols, ld_w, q,
+                           ld_q, qt, ld_qt, s, nbr, nbc);
+    return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = (n + 4 * kThreads - 1) / (4 * kThreads);
+    hipLaunchKernelGGL(k_e4m3_encode, dim3((unsigned)blocks), dim3(kThreads), 0, st, in, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -1,0 +1,225 @@
+"""Thin ctypes binding of libfp8bs.so (include/fp8bs.h).
+
+The functions carry the C names and only marshal arguments: tensor -> device
+pointer, sizes, strides, and the current torch stream as the HIP stream.
+Every step of the computation runs in the HIP library; if the library is not
+built or cannot be loaded, every call raises.  PyTorch provides device memory
+and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bs.so")
+_lock = threading.Lock()
+_lib = None
+
+STATUS = {0: "FP8BS_OK", 1: "FP8BS_ERR_NULL", 2: "FP8BS_ERR_SHAPE", 3: "FP8BS_ERR_STRIDE",
+          4: "FP8BS_ERR_ALIGN", 5: "FP8BS_ERR_UNSUPPORTED", 6: "FP8BS_ERR_DEVICE"}
+AXIS_ROW, AXIS_COL = 0, 1
+OUT_BF16, OUT_FP32 = 0, 1
+BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
+
+EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_blockscaled_gemm", "fp8_grouped_gemm",
+           "fp8_silu_mul_quant", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
+           "fp8bs_status_string", "fp8bs_last_error_detail"]
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(status, status), detail))
+        self.status = status
+        self.detail = detail
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libfp8bs.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libfp8bs.so is not built (%s); run `python -m fp8_block_scaled_x128_amd.build`"
+                               % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I32, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+        sig = {
+            "fp8_quant_rowblock": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P],
+            "fp8_quant_block2d": [P, I64, I64, I64, I64, P, I64, P, I64, P, P],
+            "fp8_blockscaled_gemm": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P, I64, INT, P],
+            "fp8_grouped_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64,
+                                 P, I64, INT, P],
+            "fp8_silu_mul_quant": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P, I64, P],
+            "mxfp8_quant": [P, I64, I64, I64, P, I64, P, I64, I64, P],
+            "mxfp8_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, INT, P],
+            "fp8bs_e4m3_encode": [P, P, I64, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.fp8bs_status_string.argtypes = [ctypes.c_int]
+        lib.fp8bs_status_string.restype = ctypes.c_char_p
+        lib.fp8bs_last_error_detail.argtypes = []
+        lib.fp8bs_last_error_detail.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(name, status, raise_on_error=True):
+    if status != 0 and raise_on_error:
+        detail = load().fp8bs_last_error_detail().decode()
+        raise Fp8bsError(name, status, detail)
+    return status
+
+
+# ---------------------------------------------------------------- raw C calls
+def fp8_quant_rowblock(x, rows, cols, ld_x, axis, q, ld_q, s, s_stride_row, s_stride_group, stream=None,
+                       raise_on_error=True):
+    st = load().fp8_quant_rowblock(_p(x), rows, cols, ld_x, axis, _p(q), ld_q, _p(s), s_stride_row,
+                                   s_stride_group, _stream(stream))
+    return _check("fp8_quant_rowblock", st, raise_on_error)
+
+
+def fp8_quant_block2d(w, batch, rows, cols, ld_w, q, ld_q, q_t, ld_qt, s, stream=None, raise_on_error=True):
+    st = load().fp8_quant_block2d(_p(w), batch, rows, cols, ld_w, _p(q), ld_q, _p(q_t), ld_qt, _p(s),
+                                  _stream(stream))
+    return _check("fp8_quant_block2d", st, raise_on_error)
+
+
+def fp8_blockscaled_gemm(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, sb, sb_stride_n, sb_stride_k,
+                         bscale, c, ldc, out, stream=None, raise_on_error=True):
+    st = load().fp8_blockscaled_gemm(M, N, K, _p(a), lda, _p(sa), sa_stride_m, sa_stride_k, _p(b), ldb, _p(sb),
+                                     sb_stride_n, sb_stride_k, bscale, _p(c), ldc, out, _stream(stream))
+    return _check("fp8_blockscaled_gemm", st, raise_on_error)
+
+
+def fp8_grouped_gemm(total_rows, N, K, G, offsets, a_rows, a_count, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb,
+                     b_stride_g, sb, sb_stride_g, sb_stride_n, sb_stride_k, c, ldc, out, stream=None,
+                     raise_on_error=True):
+    st = load().fp8_grouped_gemm(total_rows, N, K, G, _p(offsets), _p(a_rows), a_count, _p(a), lda, _p(sa),
+                                 sa_stride_m, sa_stride_k, _p(b), ldb, b_stride_g, _p(sb), sb_stride_g, sb_stride_n,
+                                 sb_stride_k, _p(c), ldc, out, _stream(stream))
+    return _check("fp8_grouped_gemm", st, raise_on_error)
+
+
+def fp8_silu_mul_quant(gate_up, rows, I, ld_in, mx, q, ld_q, s, s_stride_row, s_stride_group, h_out, ld_h,
+                       stream=None, raise_on_error=True):
+    st = load().fp8_silu_mul_quant(_p(gate_up), rows, I, ld_in, mx, _p(q), ld_q, _p(s), s_stride_row,
+                                   s_stride_group, _p(h_out), ld_h, _stream(stream))
+    return _check("fp8_silu_mul_quant", st, raise_on_error)
+
+
+def mxfp8_quant(x, rows, cols, ld_x, q, ld_q, s, s_stride_row, s_stride_group, stream=None, raise_on_error=True):
+    st = load().mxfp8_quant(_p(x), rows, cols, ld_x, _p(q), ld_q, _p(s), s_stride_row, s_stride_group,
+                            _stream(stream))
+    return _check("mxfp8_quant", st, raise_on_error)
+
+
+def mxfp8_gemm(rows, N, K, G, offsets, a_rows, a_count, a, lda, sa, lds_a, b, ldb, b_stride_g, sb, lds_b,
+               sb_stride_g, c, ldc, out, stream=None, raise_on_error=True):
+    st = load().mxfp8_gemm(rows, N, K, G, _p(offsets), _p(a_rows), a_count, _p(a), lda, _p(sa), lds_a, _p(b), ldb,
+                           b_stride_g, _p(sb), lds_b, sb_stride_g, _p(c), ldc, out, _stream(stream))
+    return _check("mxfp8_gemm", st, raise_on_error)
+
+
+def fp8bs_e4m3_encode(inp, out, n, stream=None, raise_on_error=True):
+    st = load().fp8bs_e4m3_encode(_p(inp), _p(out), n, _stream(stream))
+    return _check("fp8bs_e4m3_encode", st, raise_on_error)
+
+
+# ------------------------------------------------------- tensor conveniences
+def _u8(shape, device):
+    return torch.empty(shape, dtype=torch.uint8, device=device)
+
+
+def quant_rowblock(x: torch.Tensor, axis: int = AXIS_ROW, scale_layout: str = "m_major"):
+    """Quantize a bf16 [rows, cols] tensor.  Returns (q, s) with s logically
+    [rows, groups] (AXIS_ROW) or [cols, groups] (AXIS_COL).  scale_layout
+    'm_major' stores s as a [groups, rows] buffer (stride_row 1) and returns a
+    [rows, groups] view of it; 'row_major' stores [rows, groups]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if axis == AXIS_ROW:
+        q = _u8((rows, cols), x.device)
+        lead, ng = rows, (cols + 127) // 128
+        ld_q = cols
+    else:
+        q = _u8((cols, rows), x.device)
+        lead, ng = cols, (rows + 127) // 128
+        ld_q = rows
+    if scale_layout == "m_major":
+        sbuf = torch.empty((ng, lead), dtype=torch.float32, device=x.device)
+        s, ssr, ssg = sbuf.t(), 1, lead
+    else:
+        s = torch.empty((lead, ng), dtype=torch.float32, device=x.device)
+        ssr, ssg = ng, 1
+    fp8_quant_rowblock(x, rows, cols, x.stride(0), axis, q, ld_q, s, ssr, ssg)
+    return q, s
+
+
+def quant_block2d(w: torch.Tensor, transposed: bool = False):
+    """128x128 block quantization of a bf16 [rows, cols] or [batch, rows, cols]
+    tensor.  Returns (q, s, q_t or None)."""
+    assert w.dtype == torch.bfloat16 and w.is_contiguous()
+    batched = w.dim() == 3
+    ww = w if batched else w.unsqueeze(0)
+    batch, rows, cols = ww.shape
+    q = _u8(ww.shape, w.device)
+    qt = _u8((batch, cols, rows), w.device) if transposed else None
+    s = torch.empty((batch, (rows + 127) // 128, (cols + 127) // 128), dtype=torch.float32, device=w.device)
+    fp8_quant_block2d(ww, batch, rows, cols, cols, q, cols, qt, rows, s)
+    if not batched:
+        q, s = q[0], s[0]
+        qt = qt[0] if qt is not None else None
+    return q, s, qt
+
+
+def gemm(a, sa, b, sb, bscale=BSCALE_BLOCK128, out_dtype=torch.bfloat16):
+    """C = A B^T for codes a [M, K], b [N, K] and logical scale views
+    sa [M, K/128], sb [N/128 or N, K/128] (any strides)."""
+    M, K = a.shape
+    N = b.shape[0]
+    c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    fp8_blockscaled_gemm(M, N, K, a, a.stride(0), sa, sa.stride(0), sa.stride(1), b, b.stride(0), sb, sb.stride(0),
+                         sb.stride(1), bscale, c, c.stride(0), OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
+    return c
+
+
+def mx_quant(x: torch.Tensor):
+    """MXFP8 1x32 quantization of bf16 [rows, cols] -> (q, s [rows, cols/32] uint8)."""
+    rows, cols = x.shape
+    q = _u8((rows, cols), x.device)
+    s = _u8((rows, cols // 32), x.device)
+    mxfp8_quant(x, rows, cols, x.stride(0), q, cols, s, cols // 32, 1)
+    return q, s
+
+
+def e4m3_encode(v: torch.Tensor):
+    out = _u8(v.shape, v.device)
+    fp8bs_e4m3_encode(v.contiguous(), out, v.numel())
+    return out

@@ -1,0 +1,249 @@
+/*
+ * fp8bs: block-wise FP8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfp8bs.so.  The layer is the one the pages describe as shared by
+ * RL rollout and training ("Low Precision RL", miles.radixark.com, section
+ * "Unified training recipe" and section "2. Unified block-wise FP8
+ * (DeepSeek-style)"): quantize activations per token and weights per
+ * 128x128 block to E4M3 with FP32 scales, then run an FP8 GEMM that applies
+ * the two scales once per 128-wide slice of the contraction axis, with FP32
+ * accumulation.  The MXFP8 variant (1x32 blocks, UE8M0 scales) follows
+ * section "3. Unified MXFP8 (Blackwell)" of the same page.
+ *
+ * Quantizer definition ("Unified FP8: Beyond Mixed Precision...",
+ * winzheng.com, section "FP8 Quantization", Steps 1 and 2): per group,
+ *     S = max|x| / 448          (IEEE fp32 division; 448 = largest E4M3FN value)
+ *     q = E4M3(x / S)           (one IEEE fp32 division, then round to nearest
+ *                                even, saturating to +-448)
+ * An all-zero group has S = 0 and all codes 0x00.  FP8 codes are OCP E4M3FN
+ * bytes.  Inputs are expected to be finite; NaN/Inf inputs give unspecified
+ * codes.
+ *
+ * Conventions shared by every entry point
+ *  - Every buffer argument is a device pointer owned by the caller.  The
+ *    library never allocates, frees or synchronizes.
+ *  - Every call is asynchronous on the caller's HIP stream `stream`
+ *    (0 = the null stream) and returns once its kernels are enqueued.
+ *  - Arguments are validated on the host before anything is launched; on a
+ *    validation error nothing is launched and no output is touched.
+ *  - FP8BS_ERR_DEVICE reports a launch error or a current device that is not
+ *    gfx950; faults inside a kernel surface at the caller's next sync.
+ *  - bf16 tensors are passed as uint16_t bit patterns, FP8 as uint8_t codes.
+ *  - Strides and leading dimensions are in elements.  Matrices are row-major.
+ *  - Scale arrays are addressed through two strides so the caller chooses
+ *    their layout: the scale of (row r, group g) lives at
+ *    s[r * s_stride_row + g * s_stride_group].  The GEMMs read activation
+ *    scales fastest when s_stride_row == 1 ("M-major", [groups][rows]).
+ *  - Calls are thread-safe and keep no state between calls apart from the
+ *    per-device code-object load on first use.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8BS_OK = 0,
+    FP8BS_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    FP8BS_ERR_SHAPE = 2,       /* a size is negative, or K % 128 (K % 32 for MX) != 0, ... */
+    FP8BS_ERR_STRIDE = 3,      /* a leading dimension is smaller than the row length  */
+    FP8BS_ERR_ALIGN = 4,       /* a base pointer or leading dimension breaks 16-byte alignment */
+    FP8BS_ERR_UNSUPPORTED = 5, /* an enum value or a combination this build does not handle */
+    FP8BS_ERR_DEVICE = 6       /* current device is not gfx950, or a launch failed    */
+} fp8bs_status;
+
+typedef enum {
+    FP8BS_AXIS_ROW = 0,  /* 1x128 groups along the contiguous (column) axis: per-token activations */
+    FP8BS_AXIS_COL = 1   /* 128x1 groups along the row (token) axis; q is written transposed       */
+} fp8bs_axis;
+
+typedef enum { FP8BS_OUT_BF16 = 0, FP8BS_OUT_FP32 = 1 } fp8bs_out;
+
+typedef enum {
+    FP8BS_BSCALE_BLOCK128 = 0, /* B scale per 128x128 block: index (n / 128, k / 128)   */
+    FP8BS_BSCALE_ROW128 = 1    /* B scale per row and 128-wide K slice: index (n, k / 128) */
+} fp8bs_bscale;
+
+/* ------------------------------------------------------------------------
+ * fp8_quant_rowblock -- per-token (1x128) or token-axis (128x1) quantization.
+ *
+ * x      : bf16 [rows][ld_x] (row-major), cols <= ld_x.
+ * axis   : FP8BS_AXIS_ROW: groups are 1x128 runs of a row ("per-token"
+ *          activations and gradients, "Unified FP8...", section "FP8
+ *          Quantization", bullet list).  q is [rows][ld_q]; the scale of
+ *          (row r, group g = col / 128) is s[r * s_stride_row + g * s_stride_group],
+ *          g < ceil(cols / 128).
+ *          FP8BS_AXIS_COL: groups are 128x1 runs of a column (128 consecutive
+ *          tokens), for the operands of the weight-gradient GEMM whose
+ *          contraction runs over tokens.  q is written transposed, [cols][ld_q]
+ *          with the token axis contiguous; the scale of (column c, group
+ *          g = row / 128) is s[c * s_stride_row + g * s_stride_group].
+ *          This equals FP8BS_AXIS_ROW applied to the transpose of x.
+ * The last group of a row (column) covers only the elements present.
+ * Requirements: rows, cols >= 0; cols % 8 == 0, ld_x % 8 == 0 and x 16-byte
+ * aligned; AXIS_ROW: ld_q >= cols, ld_q % 8 == 0, q 8-byte aligned;
+ * AXIS_COL: rows % 16 == 0, ld_q >= rows, ld_q % 16 == 0, q 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_quant_rowblock(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                fp8bs_axis axis, uint8_t* q, int64_t ld_q,
+                                float* s, int64_t s_stride_row, int64_t s_stride_group,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_quant_block2d -- 128x128 block quantization of `batch` matrices
+ * (weights: "Low Precision RL", table "Choose a precision" and section
+ * "2. Unified block-wise FP8 (DeepSeek-style)").
+ *
+ * w   : bf16 [batch][rows][ld_w]; matrix b starts at w + b * rows * ld_w.
+ * q   : [batch][rows][ld_q] codes.
+ * q_t : nullable; if given, the transposed codes [batch][cols][ld_qt]
+ *       (the same codes, so a GEMM contracting over `rows` reads them with
+ *       the same block scales transposed).
+ * s   : [batch][ceil(rows/128)][ceil(cols/128)] fp32, contiguous; the scale of
+ *       block (i, j) of matrix b is s[(b * nbr + i) * nbc + j].
+ * Requirements: batch >= 1; rows, cols >= 0; cols % 8 == 0 and ld_w % 8 == 0;
+ * w 16-byte aligned; ld_q >= cols, ld_q % 8 == 0; if q_t: rows % 16 == 0,
+ * ld_qt >= rows, ld_qt % 16 == 0, q_t 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, int64_t cols, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt,
+                               float* s, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_blockscaled_gemm -- C = A B^T with block scales, FP32 accumulation.
+ *
+ *   C[m, n] = sum_kb (sa(m, kb) * sb(n, kb)) * sum_{k in kb} dec(a[m, k]) dec(b[n, k])
+ *
+ * over 128-wide K slices kb, the per-slice scale product applied to the FP32
+ * partial of each slice (the GEMM the rollout and the trainer forward share,
+ * "Low Precision RL", section "Unified training recipe").
+ *
+ * a  : [M][lda] E4M3 codes, K contiguous.      sa(m, kb) = sa[m * sa_stride_m + kb * sa_stride_k]
+ * b  : [N][ldb] E4M3 codes, K contiguous.      sb(n, kb) = sb[r * sb_stride_n + kb * sb_stride_k]
+ *      with r = n / 128 (FP8BS_BSCALE_BLOCK128) or r = n (FP8BS_BSCALE_ROW128).
+ *      The data-gradient GEMM dX = dY W reads W through the transposed copy
+ *      q_t of fp8_quant_block2d and W's scales with the two strides swapped.
+ * c  : [M][ldc] bf16 (round to nearest even) or fp32, per `out`.
+ * Requirements: M, N >= 0; K % 128 == 0; N % 128 == 0; lda >= K, ldb >= K,
+ * lda % 16 == 0, ldb % 16 == 0, a and b 16-byte aligned; ldc >= N.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* a, int64_t lda,
+                                  const float* sa, int64_t sa_stride_m, int64_t sa_stride_k,
+                                  const uint8_t* b, int64_t ldb,
+                                  const float* sb, int64_t sb_stride_n, int64_t sb_stride_k,
+                                  fp8bs_bscale bscale,
+                                  void* c, int64_t ldc, fp8bs_out out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_grouped_gemm -- the block-scaled GEMM over G expert groups of rows
+ * (the MoE layers the pages run the recipe on, Qwen3-30B-A3B, "Low
+ * Precision RL", table "Choose a precision").
+ *
+ * offsets : device int32 [G + 1]; rows offsets[g] .. offsets[g+1]-1 of the
+ *           output belong to expert g.  offsets[0] == 0, non-decreasing,
+ *           offsets[G] == total_rows; empty groups are allowed.  The offsets
+ *           stay on the device (no host synchronization); a violation of this
+ *           contract is not detected.
+ * a_rows  : nullable device int32 [total_rows]; if given, output row r reads
+ *           A row a_rows[r] (and its scales) -- the MoE dispatch gather fused
+ *           into the GEMM's operand load.  Every entry must be in [0, a_count).
+ * a, sa   : as in fp8_blockscaled_gemm, a has a_count rows (a_count = total_rows
+ *           when a_rows is NULL).
+ * b       : expert g's [N][ldb] codes start at b + g * b_stride_g.
+ * sb      : 128x128 block scales; expert g, block (n/128, kb) at
+ *           sb[g * sb_stride_g + (n/128) * sb_stride_n + kb * sb_stride_k].
+ * c       : [total_rows][ldc], bf16 or fp32.
+ * Requirements: as fp8_blockscaled_gemm; G >= 1; b_stride_g % 16 == 0.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t G,
+                              const int32_t* offsets, const int32_t* a_rows, int64_t a_count,
+                              const uint8_t* a, int64_t lda,
+                              const float* sa, int64_t sa_stride_m, int64_t sa_stride_k,
+                              const uint8_t* b, int64_t ldb, int64_t b_stride_g,
+                              const float* sb, int64_t sb_stride_g, int64_t sb_stride_n, int64_t sb_stride_k,
+                              void* c, int64_t ldc, fp8bs_out out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_silu_mul_quant -- the step between the MoE gate/up and down GEMMs:
+ * h = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)) in fp32, then
+ * quantization of h, 1x128 with FP32 scales (mx == 0) or 1x32 with UE8M0
+ * scales (mx == 1, see mxfp8_quant).
+ *
+ * gate_up : bf16 [rows][ld_in]; columns [0, I) hold the gate projection and
+ *           columns [I, 2I) the up projection.
+ * q       : [rows][ld_q] codes of h.   s : float* (mx == 0) or uint8_t* (mx == 1),
+ *           scale of (row r, group g) at s[r * s_stride_row + g * s_stride_group].
+ * h_out   : nullable bf16 [rows][ld_h]; receives h itself.
+ * Requirements: I % 128 == 0 (I % 32 == 0 when mx == 1); ld_in >= 2 I,
+ * ld_in % 8 == 0, gate_up 16-byte aligned; ld_q >= I, ld_q % 8 == 0;
+ * ld_h >= I if h_out.
+ * exp() is the device's expf; h agrees with an exactly rounded fp64
+ * evaluation to within one bf16 ulp.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_silu_mul_quant(const uint16_t* gate_up, int64_t rows, int64_t I, int64_t ld_in, int mx,
+                                uint8_t* q, int64_t ld_q, void* s, int64_t s_stride_row, int64_t s_stride_group,
+                                uint16_t* h_out, int64_t ld_h, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mxfp8_quant -- MXFP8 quantization: 32 consecutive values along a row share
+ * one UE8M0 scale ("Low Precision RL", section "3. Unified MXFP8
+ * (Blackwell)").  The block exponent is the smallest integer e with
+ * max|x| <= 448 * 2^e, clamped to [-127, 127] (-127 for an all-zero block);
+ * the scale byte is e + 127 and the codes are E4M3(x * 2^-e) (exact scaling,
+ * one rounding).  An all-zero block has all codes 0x00.
+ *
+ * x : bf16 [rows][ld_x]; q : [rows][ld_q]; s : uint8 scale of (row r, block
+ *     g = col / 32) at s[r * s_stride_row + g * s_stride_group].
+ * Requirements: cols % 32 == 0; ld_x % 8 == 0 and x 16-byte aligned;
+ * ld_q >= cols, ld_q % 8 == 0.
+ * ------------------------------------------------------------------------ */
+fp8bs_status mxfp8_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                         uint8_t* q, int64_t ld_q, uint8_t* s, int64_t s_stride_row, int64_t s_stride_group,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mxfp8_gemm -- C = A B^T on MXFP8 operands (dense when G == 0, grouped over
+ * experts when G >= 1), exact power-of-two block scaling inside gfx950's
+ * scaled FP8 matrix instructions, FP32 accumulation.
+ *
+ *   C[m, n] = sum_k 2^(sa(m, k/32) - 127) dec(a[m, k]) * 2^(sb(n, k/32) - 127) dec(b[n, k])
+ *
+ * a   : [rows][lda] codes (or a_count rows gathered through a_rows, as in
+ *       fp8_grouped_gemm);  sa : uint8 [.][lds_a], row m's scales at sa + m * lds_a.
+ * b   : [G or 1][N][ldb] codes, expert stride b_stride_g;
+ * sb  : uint8, expert g row n's scales at sb + g * sb_stride_g + n * lds_b.
+ * offsets : device int32 [G + 1] (ignored when G == 0), as in fp8_grouped_gemm.
+ * Requirements: K % 128 == 0; N % 128 == 0; lda, ldb % 16 == 0; lds_a >= K/32,
+ * lds_b >= K/32, lds_a % 4 == 0, lds_b % 4 == 0, sa and sb 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status mxfp8_gemm(int64_t rows, int64_t N, int64_t K, int32_t G,
+                        const int32_t* offsets, const int32_t* a_rows, int64_t a_count,
+                        const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t lds_a,
+                        const uint8_t* b, int64_t ldb, int64_t b_stride_g,
+                        const uint8_t* sb, int64_t lds_b, int64_t sb_stride_g,
+                        void* c, int64_t ldc, fp8bs_out out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8bs_e4m3_encode -- encode n fp32 values with the same device routine the
+ * quantizers use (round to nearest even, saturating to +-448).  For checking
+ * the device codec against a table; not on the layer's hot path.
+ * in : device float [n]; out : device uint8 [n].
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8bs_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* fp8bs_status_string(fp8bs_status s);
+/* Thread-local detail message of the last failing call on this thread ("" if none). */
+const char* fp8bs_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8BS_H */

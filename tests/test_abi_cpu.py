@@ -1,0 +1,88 @@
+"""The C-ABI library loads, exports every function include/fp8bs.h declares,
+and rejects invalid arguments on the host before touching a device.  No
+computation is launched here (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp8_block_scaled_x128_amd import ops
+    if not os.path.exists(ops.library_path()):
+        pytest.fail("libfp8bs.so is not built; run __graft_entry__.build()")
+    return ops.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_blockscaled_gemm", "fp8_grouped_gemm",
+              "fp8_silu_mul_quant", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
+              "fp8bs_status_string", "fp8bs_last_error_detail"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), "missing export %s" % n
+
+
+def test_status_strings(lib):
+    assert lib.fp8bs_status_string(0) == b"FP8BS_OK"
+    assert lib.fp8bs_status_string(2) == b"FP8BS_ERR_SHAPE"
+    assert lib.fp8bs_status_string(99) == b"FP8BS_UNKNOWN_STATUS"
+
+
+def test_host_validation_rejects_before_launch(lib):
+    from fp8_block_scaled_x128_amd import ops
+    fake = 1 << 20     # never dereferenced: validation fails first
+    # negative size
+    assert ops.fp8_quant_rowblock(fake, -1, 128, 128, 0, fake, 128, fake, 1, 1, stream=0,
+                                  raise_on_error=False) == 2
+    # cols not a multiple of 8
+    assert ops.fp8_quant_rowblock(fake, 4, 100, 104, 0, fake, 104, fake, 1, 1, stream=0,
+                                  raise_on_error=False) == 2
+    # ld_x < cols
+    assert ops.fp8_quant_rowblock(fake, 4, 128, 64, 0, fake, 128, fake, 1, 1, stream=0,
+                                  raise_on_error=False) == 3
+    # misaligned x
+    assert ops.fp8_quant_rowblock(fake + 2, 4, 128, 128, 0, fake, 128, fake, 1, 1, stream=0,
+                                  raise_on_error=False) == 4
+    # bad axis
+    assert ops.fp8_quant_rowblock(fake, 4, 128, 128, 7, fake, 128, fake, 1, 1, stream=0,
+                                  raise_on_error=False) == 5
+    # NULL input
+    assert ops.fp8_quant_rowblock(None, 4, 128, 128, 0, fake, 128, fake, 1, 1, stream=0,
+                                  raise_on_error=False) == 1
+    detail = lib.fp8bs_last_error_detail()
+    assert b"required" in detail
+    # GEMM: K % 128, N % 128, bad bscale, bad out
+    g = lambda M, N, K, bs=0, out=0: ops.fp8_blockscaled_gemm(M, N, K, fake, K, fake, 1, 1, fake, K, fake, 1, 1,
+                                                              bs, fake, N, out, stream=0, raise_on_error=False)
+    assert g(128, 128, 100) == 2
+    assert g(128, 100, 128) == 2
+    assert g(128, 128, 128, bs=3) == 5
+    assert g(128, 128, 128, out=9) == 5
+    # grouped: G < 1
+    assert ops.fp8_grouped_gemm(128, 128, 128, 0, fake, None, 0, fake, 128, fake, 1, 1, fake, 128, 0, fake, 0, 1, 1,
+                                fake, 128, 0, stream=0, raise_on_error=False) == 2
+    # MX: cols % 32
+    assert ops.mxfp8_quant(fake, 4, 48, 48, fake, 48, fake, 1, 1, stream=0, raise_on_error=False) == 2
+    # silu: I % 128 for the FP32-scale mode
+    assert ops.fp8_silu_mul_quant(fake, 4, 96, 192, 0, fake, 96, fake, 1, 1, None, 0, stream=0,
+                                  raise_on_error=False) == 2
+    # empty inputs are a successful no-op
+    assert ops.fp8_quant_rowblock(None, 0, 128, 128, 0, None, 128, None, 1, 1, stream=0,
+                                  raise_on_error=False) == 0

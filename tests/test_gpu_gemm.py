@@ -1,0 +1,267 @@
+"""GPU parity of the block-scaled FP8 GEMMs against the fp64 oracle.
+
+GEMM definition: C = sum over 128-wide K slices of the slice's scale product
+times the FP32 partial of the slice ("Low Precision RL", sections "Unified
+training recipe" and "2. Unified block-wise FP8 (DeepSeek-style)"), and the
+MXFP8 variant with 1x32 UE8M0 scales (section "3. Unified MXFP8
+(Blackwell)").  Tolerances: relative Frobenius error <= 1e-5 on FP32 outputs
+and elementwise |y - yref| <= 1e-4 * sum_k |a_k b_k| (+ half an output ulp);
+operands built from small integers and power-of-two scales are exact in any
+summation order and must match bit for bit.  Every call goes through the C ABI.
+
+gfx950's FP8 matrix instructions truncate, inside each aligned run of 8
+products, every product to 13 bits below the run's largest one (measured;
+see gpu_util.run_truncation).  Each result is therefore checked twice: against
+the oracle within the stated tolerance plus that truncation bound, and against
+the truncation model within the stated tolerance alone.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_x128_amd import inputs, ops
+from gpu_util import (check_vs_oracle_and_model, dev, dev_bf16, fp32_scale_fn, host, mx_scale_fn,
+                      run_truncation)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _bits(shape, seed, sigma=1.0, frac=0.0, mult=1.0):
+    return inputs.normal_bf16(np.random.default_rng(seed), shape, sigma, frac, mult)
+
+
+def _linear_operands(x, w):
+    """Quantize X (1x128, M-major scales) and W (128x128) on the GPU."""
+    qa, sa = ops.quant_rowblock(dev_bf16(x), ops.AXIS_ROW, "m_major")
+    qb, sb, _ = ops.quant_block2d(dev_bf16(w))
+    return qa, sa, qb, sb
+
+
+def verify(qa, sa, qb, sb, y32, y16=None, bscale_row=False, mi=None, ni=None, mx=False):
+    """Check GPU outputs (full matrices, or the entries (mi, ni)) against the
+    oracle and against the datapath truncation model."""
+    M, N = qa.shape[0], qb.shape[0]
+    if mi is None:
+        mi, ni = (g.reshape(-1) for g in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    if mx:
+        yref, babs = oracle.gemm_mx_sampled(qa, sa, qb, sb, mi, ni)
+        fn = mx_scale_fn(sa, sb)
+    else:
+        mode = oracle.BSCALE_ROW128 if bscale_row else oracle.BSCALE_BLOCK128
+        yref, babs = oracle.gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni, mode)
+        fn = fp32_scale_fn(sa, sb, bscale_row)
+    ymod, hb = run_truncation(qa, qb, fn, mi, ni)
+    if y32 is not None:
+        rel, relm = check_vs_oracle_and_model(y32[mi, ni], yref, babs, ymod, hb)
+        _say("rel. Frobenius error vs oracle %s, vs datapath model %s" % (rel, relm))
+    if y16 is not None:
+        check_vs_oracle_and_model(y16[mi, ni], yref, babs, ymod, hb, bf16_out=True)
+
+
+def _run_both(qa, sa, qb, sb, bscale=ops.BSCALE_BLOCK128):
+    y16 = ops.gemm(qa, sa, qb, sb, bscale, torch.bfloat16)
+    y32 = ops.gemm(qa, sa, qb, sb, bscale, torch.float32)
+    torch.cuda.synchronize()
+    return host(y16), host(y32)
+
+
+def test_tiny_linear_forward():
+    """256 tokens x 512 -> 512 with outliers: every output."""
+    d = inputs.tiny_linear(0)
+    qa, sa, qb, sb = _linear_operands(d["x"], d["w"])
+    y16, y32 = _run_both(qa, sa, qb, sb)
+    verify(host(qa), host(sa), host(qb), host(sb), y32, y16)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 1024), (1, 128, 128), (513, 640, 384), (64, 256, 2048)])
+def test_ragged_shapes(M, N, K):
+    _say("ragged", M, N, K)
+    x = _bits((M, K), 10 + M, 1.0, 0.01, 30.0)
+    w = _bits((N, K), 20 + N, 0.02)
+    qa, sa, qb, sb = _linear_operands(x, w)
+    y16, y32 = _run_both(qa, sa, qb, sb)
+    verify(host(qa), host(sa), host(qb), host(sb), y32, y16)
+
+
+def _exact_case(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    ia = rng.integers(-8, 9, size=(M, K))
+    ib = rng.integers(-8, 9, size=(N, K))
+    ja = rng.integers(-1, 2, size=(M, K // 128))
+    jb = rng.integers(-1, 2, size=(N // 128, K // 128))
+    qa = oracle.e4m3_encode(ia.astype(np.float32))
+    qb = oracle.e4m3_encode(ib.astype(np.float32))
+    return qa, np.exp2(ja).astype(np.float32), qb, np.exp2(jb).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 1024), (256, 512, 8192)])
+def test_exact_integer_case_bit_exact(M, N, K):
+    qa, sa, qb, sb = _exact_case(M, N, K, M + K)
+    yref, _ = oracle.gemm_blockscaled(qa, sa, qb, sb, with_abs=False)
+    y16, y32 = _run_both(dev(qa), dev(sa), dev(qb), dev(sb))
+    assert np.array_equal(y32.astype(np.float64), yref)
+    assert np.array_equal(y16, oracle.f64_to_bf16(yref))
+
+
+def test_dgrad_through_transposed_weight_copy():
+    """dX = dY W: dY [512, 1024] 1x128, W [1024 out, 384 in] 128x128; B is the
+    transposed code copy with W's block scales read transposed."""
+    dy = _bits((512, 1024), 30, 1e-3)
+    w = _bits((1024, 384), 31, 0.02)
+    qa, sa = ops.quant_rowblock(dev_bf16(dy), ops.AXIS_ROW, "m_major")
+    qw, sw, qwt = ops.quant_block2d(dev_bf16(w), transposed=True)
+    swt = sw.t()                                   # [in/128, out/128] view, strides swapped
+    y32 = ops.gemm(qa, sa, qwt, swt, ops.BSCALE_BLOCK128, torch.float32)
+    torch.cuda.synchronize()
+    verify(host(qa), host(sa), np.ascontiguousarray(host(qw).T), np.ascontiguousarray(host(sw).T), host(y32))
+
+
+def test_wgrad_row128():
+    """dW = dY^T X with both operands re-quantized 128x1 along tokens."""
+    T, O, I = 512, 256, 384
+    dy = _bits((T, O), 40, 1e-3)
+    x = _bits((T, I), 41, 1.0, 0.01, 30.0)
+    qa, sa = ops.quant_rowblock(dev_bf16(dy), ops.AXIS_COL, "m_major")
+    qb, sb = ops.quant_rowblock(dev_bf16(x), ops.AXIS_COL, "m_major")
+    y32 = ops.gemm(qa, sa, qb, sb, ops.BSCALE_ROW128, torch.float32)
+    torch.cuda.synchronize()
+    verify(host(qa), host(sa), host(qb), host(sb), host(y32), bscale_row=True)
+
+
+def _sample_indices(M, N, count, seed):
+    rng = np.random.default_rng(seed)
+    mi = rng.integers(0, M, count)
+    ni = rng.integers(0, N, count)
+    # corners of every 256 x 256 output tile and the matrix edges
+    tm = np.arange(0, M, 256)
+    tn = np.arange(0, N, 256)
+    cm, cn = np.meshgrid(np.concatenate([tm, np.minimum(tm + 255, M - 1)]),
+                         np.concatenate([tn, np.minimum(tn + 255, N - 1)]), indexing="ij")
+    return np.concatenate([mi, cm.reshape(-1)]), np.concatenate([ni, cn.reshape(-1)])
+
+
+@pytest.mark.parametrize("part", ["up", "down"])
+def test_qwen3_4b_mlp_full_size_sampled(part):
+    d = inputs.qwen3_4b_mlp(1, parts=(part,))
+    x, w = d["x_" + part], d["w_" + part]
+    _say("full size", part, x.shape, w.shape)
+    qa, sa, qb, sb = _linear_operands(x, w)
+    y16, y32 = _run_both(qa, sa, qb, sb)
+    M, N = y32.shape
+    mi, ni = _sample_indices(M, N, 3000, 7)
+    verify(host(qa), host(sa), host(qb), host(sb), y32, y16, mi=mi, ni=ni)
+
+
+# ---------------------------------------------------------------- grouped
+def _moe_operands(moe, part="gu"):
+    r = moe["routing"]
+    G = r.offsets.size - 1
+    qx, sx = ops.quant_rowblock(dev_bf16(moe["x"]), ops.AXIS_ROW, "m_major")
+    w = moe["w_gu"]
+    qw, sw, _ = ops.quant_block2d(dev_bf16(w))
+    return r, G, qx, sx, qw, sw
+
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_grouped_small_moe_with_empty_groups(gather):
+    moe = inputs.small_moe()
+    r, G, qx, sx, qw, sw = _moe_operands(moe)
+    assert np.any(np.diff(r.offsets) == 0)
+    rows = r.row_token.size
+    N, K = qw.shape[1], qw.shape[2]
+    offs = dev(r.offsets)
+    if gather:
+        a, sa, a_rows, a_count = qx, sx, dev(r.row_token), qx.shape[0]
+    else:
+        idx = torch.from_numpy(r.row_token.astype(np.int64)).cuda()
+        a, sa, a_rows, a_count = qx[idx].contiguous(), sx[idx].t().contiguous().t(), None, rows
+    for out_dtype in (torch.float32, torch.bfloat16):
+        c = torch.full((rows, N), float("nan"), dtype=out_dtype, device="cuda")
+        ops.fp8_grouped_gemm(rows, N, K, G, offs, a_rows, a_count, a, a.stride(0), sa, sa.stride(0), sa.stride(1),
+                             qw, qw.stride(1), qw.stride(0), sw, sw.stride(0), sw.stride(1), sw.stride(2), c,
+                             c.stride(0), ops.OUT_FP32 if out_dtype == torch.float32 else ops.OUT_BF16)
+        torch.cuda.synchronize()
+        qa_h = host(qx)[r.row_token]
+        sa_h = host(sx)[r.row_token]
+        ch = host(c)
+        for g in range(G):
+            r0, r1 = int(r.offsets[g]), int(r.offsets[g + 1])
+            if r1 > r0:
+                if out_dtype == torch.float32:
+                    verify(qa_h[r0:r1], sa_h[r0:r1], host(qw)[g], host(sw)[g], ch[r0:r1])
+                else:
+                    verify(qa_h[r0:r1], sa_h[r0:r1], host(qw)[g], host(sw)[g], None, ch[r0:r1])
+
+
+def test_grouped_exact_integer_case():
+    """Grouped GEMM on exact operands with ragged and empty groups: bit-exact."""
+    rng = np.random.default_rng(8)
+    counts = np.array([0, 300, 1, 0, 256, 513, 0, 40])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows, G, N, K = int(offsets[-1]), counts.size, 384, 512
+    qa, sa, _, _ = _exact_case(rows, 128, K, 9)
+    qbs, sbs = [], []
+    for g in range(G):
+        _, _, qb, sb = _exact_case(128, N, K, 100 + g)
+        qbs.append(qb)
+        sbs.append(sb)
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    yref, _ = oracle.grouped_gemm_blockscaled(qa, sa, offsets, qb, sb)
+    c = torch.zeros((rows, N), dtype=torch.float32, device="cuda")
+    dqb, dsb = dev(qb), dev(sb)
+    dsa = dev(sa)
+    ops.fp8_grouped_gemm(rows, N, K, G, dev(offsets), None, rows, dev(qa), K, dsa, dsa.stride(0), dsa.stride(1),
+                         dqb, K, N * K, dsb, dsb.stride(0), dsb.stride(1), dsb.stride(2), c, N, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c).astype(np.float64), yref)
+
+
+# ---------------------------------------------------------------------- MX
+def test_mx_dense_and_exact():
+    M, N, K = 300, 384, 1024
+    x = _bits((M, K), 50, 1.0, 0.02, 40.0)
+    w = _bits((N, K), 51, 0.02)
+    qa, sa = ops.mx_quant(dev_bf16(x))
+    qb, sb = ops.mx_quant(dev_bf16(w))
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.mxfp8_gemm(M, N, K, 0, None, None, M, qa, K, sa, K // 32, qb, K, 0, sb, K // 32, 0, c, N, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    verify(host(qa), host(sa), host(qb), host(sb), host(c), mx=True)
+    # exact: integer codes and UE8M0 codes 126..128
+    rng = np.random.default_rng(52)
+    ia = oracle.e4m3_encode(rng.integers(-8, 9, size=(M, K)).astype(np.float32))
+    ib = oracle.e4m3_encode(rng.integers(-8, 9, size=(N, K)).astype(np.float32))
+    ea = rng.integers(126, 129, size=(M, K // 32)).astype(np.uint8)
+    eb = rng.integers(126, 129, size=(N, K // 32)).astype(np.uint8)
+    yref, _ = oracle.gemm_mx(ia, ea, ib, eb)
+    ops.mxfp8_gemm(M, N, K, 0, None, None, M, dev(ia), K, dev(ea), K // 32, dev(ib), K, 0, dev(eb), K // 32, 0,
+                   c, N, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c).astype(np.float64), yref)
+
+
+def test_mx_grouped_small_moe():
+    moe = inputs.small_moe()
+    r = moe["routing"]
+    G = r.offsets.size - 1
+    rows = r.row_token.size
+    qx, sx = ops.mx_quant(dev_bf16(moe["x"]))
+    w = moe["w_gu"]
+    Gw, N, K = w.shape
+    qw, sw = ops.mx_quant(dev_bf16(w.reshape(Gw * N, K)))
+    c = torch.empty((rows, N), dtype=torch.float32, device="cuda")
+    ops.mxfp8_gemm(rows, N, K, G, dev(r.offsets), dev(r.row_token), qx.shape[0], qx, K, sx, K // 32, qw, K, N * K,
+                   sw, K // 32, N * (K // 32), c, N, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    qa_h, sa_h = host(qx)[r.row_token], host(sx)[r.row_token]
+    qw_h, sw_h = host(qw).reshape(Gw, N, K), host(sw).reshape(Gw, N, K // 32)
+    ch = host(c)
+    for g in range(G):
+        r0, r1 = int(r.offsets[g]), int(r.offsets[g + 1])
+        if r1 > r0:
+            verify(qa_h[r0:r1], sa_h[r0:r1], qw_h[g], sw_h[g], ch[r0:r1], mx=True)

@@ -1,0 +1,232 @@
+"""GPU parity of the quantizers against the CPU oracle: FP8 codes and scales
+must be bit-identical ("Unified FP8: Beyond Mixed Precision...", section "FP8
+Quantization"; groupings from "Low Precision RL", table "Choose a
+precision").  Every call goes through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_x128_amd import inputs, ops
+from gpu_util import dev, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _bits(shape, seed, sigma=1.0, frac=0.01, mult=50.0):
+    return inputs.normal_bf16(np.random.default_rng(seed), shape, sigma, frac, mult)
+
+
+def _assert_same_scales(s_gpu, s_ref):
+    a = np.ascontiguousarray(host(s_gpu)).view(np.uint32)
+    b = np.ascontiguousarray(s_ref).view(np.uint32)
+    assert a.shape == b.shape
+    bad = np.flatnonzero(a != b)
+    assert bad.size == 0, "scale mismatch at %s: gpu %s ref %s" % (bad[:5], a.reshape(-1)[bad[:5]], b.reshape(-1)[bad[:5]])
+
+
+def _assert_same_codes(q_gpu, q_ref):
+    a = host(q_gpu)
+    bad = np.flatnonzero(a != q_ref)
+    assert bad.size == 0, "%d code mismatches, first at %s: gpu %s ref %s" % (
+        bad.size, bad[:5], a.reshape(-1)[bad[:5]], q_ref.reshape(-1)[bad[:5]])
+
+
+# ------------------------------------------------------------------- codec
+def test_device_codec_table():
+    dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    vals = [d for d in dec if not np.isnan(d)]
+    grid = dec[:0x7F]
+    for c in range(0x7E):
+        mid = np.float32((grid[c] + grid[c + 1]) / 2)
+        for v in (mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(np.inf))):
+            vals += [v, -v]
+    vals += [448.5, 463.99997, 464.0, 465.0, 1e6, 3e38, np.inf, -np.inf, -1e6, 1e-40, -1e-40, 2 ** -10,
+             -2 ** -10, 2 ** -11, -2 ** -11, 0.0, -0.0]
+    rng = np.random.default_rng(0)
+    vals += list(rng.standard_normal(100_000) * np.exp2(rng.uniform(-14, 10, 100_000)))
+    v = np.array(vals, np.float32)
+    _say("codec probe", v.size)
+    out = ops.e4m3_encode(dev(v))
+    torch.cuda.synchronize()
+    _assert_same_codes(out, oracle.e4m3_encode(v))
+
+
+# ------------------------------------------------------------ 1x128 groups
+@pytest.mark.parametrize("shape,layout", [((256, 512), "m_major"), ((256, 512), "row_major"),
+                                          ((7, 264), "m_major"), ((1, 8), "row_major"),
+                                          ((300, 1000), "row_major")])
+def test_rowblock_small(shape, layout):
+    _say("rowblock", shape, layout)
+    x = _bits(shape, 1)
+    q, s = ops.quant_rowblock(dev_bf16(x), ops.AXIS_ROW, layout)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_1x128(x)
+    _assert_same_codes(q, qr)
+    _assert_same_scales(s, sr)
+
+
+def test_rowblock_special_groups():
+    x = _bits((6, 256), 2)
+    x[0, :128] = 0                                        # zero group
+    x[1, :128] = 0x8000                                   # -0 group
+    x[2, :128] = inputs.to_bf16_bits(np.linspace(-1e-38, 1e-38, 128).astype(np.float32))   # subnormal S
+    x[3, 128:] = inputs.to_bf16_bits(np.linspace(-3e38, 3e38, 128).astype(np.float32))     # huge values
+    x[4, :128] = inputs.to_bf16_bits(np.full(128, 448.0, np.float32))
+    x[5, 128:] = inputs.to_bf16_bits((np.arange(128) * 1e-20).astype(np.float32))          # S ~ 2^-70
+    q, s = ops.quant_rowblock(dev_bf16(x), ops.AXIS_ROW, "row_major")
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_1x128(x)
+    _assert_same_codes(q, qr)
+    _assert_same_scales(s, sr)
+
+
+def test_rowblock_division_coverage():
+    """Every bf16 significand of x against every bf16 significand of amax, at
+    several exponent gaps: the device division path must reproduce the IEEE
+    division of the oracle bit for bit."""
+    rows = []
+    rng = np.random.default_rng(3)
+    for gap in (1, 2, 5, 9, 20):
+        for ma in range(128):
+            amax = np.float32((1 + ma / 128) * 8.0)
+            xs = np.array([(1 + m / 128) * 8.0 * 2.0 ** -gap for m in range(128)], np.float32)
+            xs *= np.where(np.arange(128) % 2 == 0, 1, -1).astype(np.float32)
+            g0 = np.concatenate([[amax], xs[:127]])
+            g1 = np.concatenate([[-amax], xs[127:], rng.standard_normal(126).astype(np.float32)])
+            rows.append(np.concatenate([g0, g1]).astype(np.float32))
+    x = inputs.to_bf16_bits(np.stack(rows))
+    _say("division coverage", x.shape)
+    q, s = ops.quant_rowblock(dev_bf16(x), ops.AXIS_ROW, "row_major")
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_1x128(x)
+    _assert_same_codes(q, qr)
+    _assert_same_scales(s, sr)
+
+
+def test_rowblock_qwen3_4b_activation_full():
+    """Qwen3-4B MLP up-projection input, 4096 x 2560, every code and scale."""
+    x = inputs.qwen3_4b_mlp(1, parts=("up",))["x_up"]
+    _say("rowblock full", x.shape)
+    q, s = ops.quant_rowblock(dev_bf16(x), ops.AXIS_ROW, "m_major")
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_1x128(x)
+    _assert_same_codes(q, qr)
+    _assert_same_scales(s, sr)
+
+
+# ------------------------------------------------------------- 128x1 groups
+@pytest.mark.parametrize("shape", [(512, 384), (272, 72), (16, 8)])
+def test_colblock_small(shape):
+    _say("colblock", shape)
+    x = _bits(shape, 4)
+    qt, s = ops.quant_rowblock(dev_bf16(x), ops.AXIS_COL, "row_major")
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_128x1_t(x)
+    _assert_same_codes(qt, qr)
+    _assert_same_scales(s, sr)
+
+
+def test_colblock_qwen3_4b_gradient_full():
+    """dY of the Qwen3-4B MLP backward, 4096 tokens x 9728, 128x1 along tokens."""
+    dy = inputs.qwen3_4b_mlp_backward(2)["dy"]
+    _say("colblock full", dy.shape)
+    qt, s = ops.quant_rowblock(dev_bf16(dy), ops.AXIS_COL, "m_major")
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_128x1_t(dy)
+    _assert_same_codes(qt, qr)
+    _assert_same_scales(s, sr)
+
+
+# ----------------------------------------------------------- 128x128 blocks
+@pytest.mark.parametrize("shape", [(512, 512), (272, 200), (16, 8), (3, 384, 256)])
+def test_block2d_small(shape):
+    _say("block2d", shape)
+    w = _bits(shape, 5, 0.02, 0.0, 1.0)
+    trans = shape[-2] % 16 == 0
+    q, s, qt = ops.quant_block2d(dev_bf16(w), transposed=trans)
+    torch.cuda.synchronize()
+    ws = w if w.ndim == 3 else w[None]
+    qh, sh = host(q).reshape(ws.shape), host(s).reshape(ws.shape[0], -1)
+    for b in range(ws.shape[0]):
+        qr, sr = oracle.quant_128x128(ws[b])
+        assert np.array_equal(qh[b], qr)
+        assert np.array_equal(sh[b].view(np.uint32), sr.reshape(-1).view(np.uint32))
+        if trans:
+            qth = host(qt).reshape(ws.shape[0], ws.shape[2], ws.shape[1])
+            assert np.array_equal(qth[b], qr.T)
+
+
+def test_block2d_qwen3_4b_weight_full():
+    w = inputs.qwen3_4b_mlp(1, parts=("up",))["w_up"]
+    _say("block2d full", w.shape)
+    q, s, qt = ops.quant_block2d(dev_bf16(w), transposed=True)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant_128x128(w)
+    _assert_same_codes(q, qr)
+    _assert_same_scales(s, sr)
+    _assert_same_codes(qt, np.ascontiguousarray(qr.T))
+
+
+# ---------------------------------------------------------------------- MX
+@pytest.mark.parametrize("shape", [(64, 256), (5, 96), (300, 2048)])
+def test_mx_small(shape):
+    _say("mx", shape)
+    x = _bits(shape, 6, 1.0, 0.02, 40.0)
+    x[0, :32] = 0
+    if shape[0] > 2:
+        x[1, 32:64] = inputs.to_bf16_bits(np.full(32, 448.0, np.float32))
+        x[2, :32] = inputs.to_bf16_bits(np.linspace(-3e-39, 3e-39, 32).astype(np.float32))
+    q, s = ops.mx_quant(dev_bf16(x))
+    torch.cuda.synchronize()
+    qr, sr = oracle.mx_quant_1x32(x)
+    _assert_same_codes(q, qr)
+    assert np.array_equal(host(s), sr)
+
+
+def test_mx_moe_activation_full():
+    x = inputs.qwen3_30b_a3b_moe(3, weights=False)["x"]
+    _say("mx full", x.shape)
+    q, s = ops.mx_quant(dev_bf16(x))
+    torch.cuda.synchronize()
+    qr, sr = oracle.mx_quant_1x32(x)
+    _assert_same_codes(q, qr)
+    assert np.array_equal(host(s), sr)
+
+
+# ------------------------------------------------------------ SiLU * up
+@pytest.mark.parametrize("mx", [0, 1])
+def test_silu_mul_quant(mx):
+    rows, I = 1000, 768
+    gu = _bits((rows, 2 * I), 7, 2.0, 0.0, 1.0)
+    d = dev_bf16(gu)
+    q = torch.empty((rows, I), dtype=torch.uint8, device="cuda")
+    h = torch.empty((rows, I), dtype=torch.bfloat16, device="cuda")
+    if mx:
+        s = torch.empty((rows, I // 32), dtype=torch.uint8, device="cuda")
+        ops.fp8_silu_mul_quant(d, rows, I, 2 * I, 1, q, I, s, I // 32, 1, h, I)
+    else:
+        s = torch.empty((rows, I // 128), dtype=torch.float32, device="cuda")
+        ops.fp8_silu_mul_quant(d, rows, I, 2 * I, 0, q, I, s, I // 128, 1, h, I)
+    torch.cuda.synchronize()
+    hg = host(h)
+    hr = oracle.silu_mul(gu)
+    # h within one bf16 ulp of the exactly rounded value (device expf vs fp64 exp)
+    diff = np.abs(hg.astype(np.int32) - hr.astype(np.int32))
+    same_sign = (hg & 0x8000) == (hr & 0x8000)
+    ok = (diff <= 1) & same_sign | ((hg & 0x7FFF) == 0) & ((hr & 0x7FFF) <= 1)
+    assert np.all(ok), "h differs by more than one bf16 ulp at %s" % np.flatnonzero(~ok)[:5]
+    _say("silu h mismatch rate", float(np.mean(diff != 0)))
+    # the quantization of the device's own h is bit-exact
+    if mx:
+        qr, sr = oracle.mx_quant_1x32(hg)
+        _assert_same_codes(q, qr)
+        assert np.array_equal(host(s), sr)
+    else:
+        qr, sr = oracle.quant_1x128(hg)
+        _assert_same_codes(q, qr)
+        _assert_same_scales(s, sr)
