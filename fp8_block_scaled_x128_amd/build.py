@@ -17,6 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8bs.so")
 SOURCES = ["quant.hip", "gemm.hip", "capi.hip"]
+# The GEMM promotes MFMA results with VALU FMAs, so the results must land in
+# VGPRs (not AGPRs, which would need a v_accvgpr_read per value).
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -41,7 +44,8 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
     objs = [os.path.join(bdir, s.replace(".hip", ".o")) for s in SOURCES]
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        outs = list(ex.map(lambda so: _compile(os.path.join(CSRC, so[0]), so[1], extra), zip(SOURCES, objs)))
+        outs = list(ex.map(lambda so: _compile(os.path.join(CSRC, so[0]), so[1], extra + EXTRA.get(so[0], [])),
+                           zip(SOURCES, objs)))
     if verbose or resource_usage:
         for o in outs:
             if o.strip():

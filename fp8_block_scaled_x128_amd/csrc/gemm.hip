@@ -12,25 +12,25 @@
 // section "3. Unified MXFP8 (Blackwell)") hands its power-of-two block scales
 // to the scaled matrix instruction, which applies them exactly.
 //
-// Kernel structure (one workgroup per 256x256 output tile, 8 waves):
-//  - K advances in 128-byte slices.  Each slice of the 256-row A tile and of
-//    the 256-row B tile (32 KB each) is copied straight from global memory
-//    into LDS with global_load_lds_dwordx4 (no register staging), double
-//    buffered (2 x 64 KB).
+// Kernel structure: one workgroup of 4 waves (one per SIMD, so each wave has
+// the full 512-entry VGPR+AGPR budget) per output tile of 256 weight rows (n)
+// x 128 activation rows (m).
+//  - K advances in 128-byte slices.  Each slice of the weight tile (32 KB),
+//    the activation tile (16 KB) and the slice's scales is copied straight
+//    from global memory into LDS with global_load_lds (no register staging),
+//    three stages deep, so two slices are in flight while one is consumed.
 //  - LDS rows are 128 bytes; 16-byte chunk c of row r sits in slot
-//    c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), which makes the fragment
-//    reads conflict-free (16 consecutive rows reading the same logical chunk
-//    hit 16 distinct 16-byte bank groups).  The copy realizes the swizzle by
-//    choosing which global chunk each lane fetches.
-//  - Wave w owns n rows [128 * (w / 4), +128) and m rows [64 * (w % 4), +64):
-//    8 x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4 per slice.  The weight
-//    rows are the instruction's A operand and the activation rows its B
-//    operand, so each lane's 4 outputs share one activation row m and four
-//    consecutive n; the slice scale of a lane is then sa(m, kb) * sb(n/128, kb)
-//    with sb uniform over the wave.
-//  - FP32-scale modes: each MFMA produces a fresh FP32 partial for its
-//    slice (zero accumulator input, unit E8M0 scales), which is promoted with
-//    one FMA per output: acc = fma(partial, sa * sb, acc).
+//    c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): 16 consecutive rows reading
+//    the same logical chunk hit 16 distinct 16-byte bank groups.  The copy
+//    realizes the swizzle by choosing which global chunk each lane fetches.
+//  - Wave w owns n rows [128 * (w >> 1), +128) and m rows [64 * (w & 1), +64):
+//    8 x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4 per slice.  Weight rows
+//    are the instruction's A operand and activation rows its B operand, so a
+//    lane's 4 outputs share one activation row m and four consecutive n.
+//  - FP32-scale modes: each MFMA produces a fresh FP32 partial for its slice
+//    (zero accumulator input, unit E8M0 scales), promoted with one FMA per
+//    output, acc = fma(partial, sa * sb, acc), one n-tile behind the MFMAs so
+//    that the promotion overlaps the next n-tile's matrix work.
 //  - MX mode: the instruction accumulates in place with the per-lane UE8M0
 //    scale bytes of its row and 32-wide K block.
 #include "device_common.h"
@@ -42,28 +42,64 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kWaves = 8, kThreads = kWaves * 64;
-constexpr int kTileBytes = 256 * BK;          // one operand tile slice
-constexpr int kE8M0One = 127;                 // UE8M0 code of 1.0
+constexpr int BN = 256, BK = 128;              // weight rows per tile, K bytes per slice
+constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
+
+// Tile configurations.  Every wave computes 128 weight rows x 64 activation
+// rows; waves are arranged 2 (n) x WAVES/2 (m).
+//   WAVES = 4: 256 x 128 tile, one wave per SIMD (512 registers each), three
+//              LDS stages, promotion deferred by one n-tile within the wave.
+//   WAVES = 8: 256 x 256 tile, two waves per SIMD (256 registers each) whose
+//              matrix and vector work interleave, two LDS stages.
+template <int WAVES>
+struct Cfg {
+    static constexpr int kWaves = WAVES;
+    static constexpr int kThreads = WAVES * 64;
+    static constexpr int BM = 64 * (WAVES / 2);
+    static constexpr int kStages = WAVES == 4 ? 3 : 2;
+    static constexpr bool kDefer = WAVES == 4;
+    static constexpr int kOffB = 0;                       // weight tile: BN rows x 128 B
+    static constexpr int kOffA = BN * BK;                 // activation tile: BM rows x 128 B
+    static constexpr int kOffSA = kOffA + BM * BK;        // activation scales: BM x 4 B
+    static constexpr int kOffSB = kOffSA + BM * 4;        // weight scales: BN x 4 B
+    static constexpr int kStageBytes = kOffSB + BN * 4;
+    static constexpr int kDmaB = BN / 8 / WAVES;          // 16-byte copies per wave per slice
+    static constexpr int kDmaA = BM / 8 / WAVES;
+    static constexpr int kTileDma = kDmaB + kDmaA;
+};
 
 enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2 };
 
 struct KArgs {
     int32_t M, N, K;
     const uint8_t* a; int64_t lda;
-    const void* sa; int64_t sa_sm, sa_sk;      // MX: sa_sm = lds_a, sa_sk = 1 (bytes)
+    const uint8_t* sa; int64_t sa_sm, sa_sk;   // element strides (MX: bytes, sa_sk unused)
     const uint8_t* b; int64_t ldb; int64_t b_sg;
-    const void* sb; int64_t sb_sg, sb_sn, sb_sk;
+    const uint8_t* sb; int64_t sb_sg, sb_sn, sb_sk;
     void* c; int64_t ldc;
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// global -> LDS copies: lane l's bytes land at lds_wave_base + l * BYTES.
+// Issued as inline assembly on purpose: the compiler cannot tell which LDS
+// stage a copy writes, so for the builtin it would wait for every outstanding
+// copy (vmcnt(0)) before the first LDS read of the current stage, which
+// serializes the pipeline.  Ordering is explicit instead: s_waitcnt vmcnt(n)
+// on the issuing wave, then s_barrier, before any wave reads a stage.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(m0), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, const uint8_t* lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(m0), "v"(src) : "memory", "m0");
 }
 
 // Read the 32-byte MFMA fragment of tile row `row` for lane quarter q.  The
@@ -73,10 +109,9 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_wave_base
 // s < 2 and bytes 16-31 of quarters 2(s-2) and 2(s-2)+1 for s >= 2, and the
 // scale of slot s comes from the lanes of quarter s).  The lane's low 16 bytes
 // are therefore logical chunk q of the row's 128-byte K slice and its high 16
-// bytes chunk q + 4.
-// In this order the 32-wide K block s of the slice is exactly scale slot s,
-// which the MX mode relies on; the FP32-scale modes only need both operands
-// in the same order.
+// bytes chunk q + 4.  In this order the 32-wide K block s of the slice is
+// exactly scale slot s, which the MX mode relies on; the FP32-scale modes only
+// need both operands in the same order.
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int q) {
     const int f = swz(row);
     const uint8_t* base = tile + row * BK;
@@ -88,28 +123,37 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int q) {
     return r;
 }
 
-template <int MODE, bool GROUPED, bool OUTF32>
-__global__ void __launch_bounds__(kThreads, 1) k_gemm(KArgs p) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kTileBytes];   // [stage][0: B(n) 1: A(m)]
+__device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+}
+
+template <int MODE, bool GROUPED, bool OUTF32, int WAVES>
+__global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
+    using C = Cfg<WAVES>;
+    constexpr int BM = C::BM, kStages = C::kStages, kStageBytes = C::kStageBytes;
+    constexpr int kOffA = C::kOffA, kOffB = C::kOffB, kOffSA = C::kOffSA, kOffSB = C::kOffSB;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
     __shared__ int s_tile[2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wn = wave >> 2, wm = wave & 3;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int q = lane >> 4, r16 = lane & 15;
 
     // ---------------------------------------------------------------- tile
     int32_t m_begin, m_end, n0;
     const uint8_t* bptr = p.b;
-    const uint8_t* sbp = static_cast<const uint8_t*>(p.sb);
+    const uint8_t* sbp = p.sb;
     if (!GROUPED) {
         const int ntn = (p.N + BN - 1) / BN, ntm = (p.M + BM - 1) / BM;
         const int nblk = ntn * ntm;
-        int bid = blockIdx.x;
+        const int bid = blockIdx.x;
         // consecutive tile ids on one XCD (workgroups are dealt round-robin to the 8 XCDs)
         const int per = nblk / 8;
-        int tile = bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
-        // groups of 4 m-tiles sweep n, so co-resident tiles share A and B panels in L2
-        constexpr int GM = 4;
+        const int tile = bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
+        // groups of GM m-tiles sweep n, so co-resident tiles share operand panels in L2
+        constexpr int GM = 8;
         const int gsz = GM * ntn;
         const int grp = tile / gsz;
         const int fm = grp * GM;
@@ -120,7 +164,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm(KArgs p) {
         m_end = min(p.M, m_begin + BM);
         n0 = tn * BN;
     } else {
-        // Work item blockIdx.y is the blockIdx.y-th 256-row tile in the list of
+        // Work item blockIdx.y is the blockIdx.y-th BM-row tile in the list of
         // all groups' tiles; wave 0 scans the per-group tile counts.
         if (threadIdx.x == 0) s_tile[0] = -1;
         if (wave == 0) {
@@ -155,51 +199,66 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm(KArgs p) {
         bptr += (int64_t)g * p.b_sg;
         sbp += (int64_t)g * p.sb_sg * (MODE == MODE_MX ? 1 : 4);
     }
-
-    // ------------------------------------------------------- copy set-up
-    // Wave w copies rows [32 w, 32 w + 32) of each operand tile: 4 x 8 rows.
-    // Lane l fetches chunk (l % 8) ^ f(row) of row 8 j' + l / 8.
-    uint32_t offA[4], offB[4];     // byte offsets of the lane's rows (without the K slice)
-    const uint8_t* abase = p.a;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = wave * 32 + j * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz(row);
-        int nrow = min(n0 + row, p.N - 1);
-        offB[j] = (uint32_t)((int64_t)nrow * p.ldb + chunk * 16);
-        int mrow = min(m_begin + row, m_end - 1);
-        if (GROUPED && p.a_rows != nullptr) mrow = p.a_rows[mrow];
-        offA[j] = (uint32_t)((int64_t)mrow * p.lda + chunk * 16);
-    }
-    auto issue_copy = [&](int kb, int stage) {
-        const uint32_t ko = (uint32_t)kb * BK;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint8_t* dstB = &smem[stage][0][(wave * 32 + j * 8) * BK];
-            uint8_t* dstA = &smem[stage][1][(wave * 32 + j * 8) * BK];
-            dma16(bptr + offB[j] + ko, dstB);
-            dma16(abase + offA[j] + ko, dstA);
-        }
+    auto arow = [&](int m_local) {             // physical A row of tile row m_local (clamped)
+        int m = min(m_begin + m_local, m_end - 1);
+        if (GROUPED && p.a_rows != nullptr) m = p.a_rows[m];
+        return m;
     };
 
-    // ------------------------------------------------------- scales set-up
-    const int q = lane >> 4, r16 = lane & 15;
-    uint32_t sa_row[4];           // per m-tile: element offset of the lane's activation-row scales
+    // ------------------------------------------------------- copy set-up
+    // Wave w copies weight rows [8 kDmaB w, +8 kDmaB) and activation rows
+    // [8 kDmaA w, +8 kDmaA), one instruction per 8 rows x 128 bytes.  Lane l
+    // fetches logical chunk (l % 8) ^ f(row) of row 8 j + l / 8.
+    uint32_t offB[C::kDmaB], offA[C::kDmaA];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        int m = min(m_begin + wm * 64 + mt * 16 + r16, m_end - 1);
-        if (GROUPED && p.a_rows != nullptr) m = p.a_rows[m];
-        sa_row[mt] = (uint32_t)((int64_t)m * p.sa_sm);
+    for (int j = 0; j < C::kDmaB; ++j) {
+        const int row = (wave * C::kDmaB + j) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(row);
+        offB[j] = (uint32_t)((int64_t)min(n0 + row, p.N - 1) * p.ldb + chunk * 16);
     }
-    const int nw0 = n0 + wn * 128;                   // first n row of the wave (128-aligned)
-    const int nb_w = min(nw0, p.N - 1) / 128;
-    uint32_t sb_row[8];           // MX / ROW128: per n-tile
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        const int nrow = (MODE == MODE_MX) ? min(nw0 + nt * 16 + r16, p.N - 1)
-                                           : min(nw0 + nt * 16 + 4 * q, p.N - 4);
-        sb_row[nt] = (uint32_t)((int64_t)nrow * p.sb_sn);
+    for (int j = 0; j < C::kDmaA; ++j) {
+        const int row = (wave * C::kDmaA + j) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(row);
+        offA[j] = (uint32_t)((int64_t)arow(row) * p.lda + chunk * 16);
     }
+    // Scale copies (4-byte lanes).  Activation scales: waves [0, BM/64) copy
+    // rows [64 w, +64).  Weight scales: MODE_BLOCK128 -> wave BM/64 copies the
+    // two 128-row blocks of the tile; ROW128 / MX -> waves 0..3 copy rows [64 w, +64).
+    const bool has_sa = wave < BM / 64;
+    const bool has_sb = (MODE == MODE_BLOCK128) ? wave == BM / 64 : wave < 4;
+    int64_t sa_off = 0, sb_off = 0;             // byte offsets without the slice term
+    if (has_sa) {
+        const int m = arow(wave * 64 + lane);
+        sa_off = (MODE == MODE_MX) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4;
+    }
+    if (MODE == MODE_BLOCK128) {
+        const int nb = min(n0 / 128 + (lane & 1), (p.N - 1) / 128);
+        sb_off = (int64_t)nb * p.sb_sn * 4;
+    } else {
+        const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
+        sb_off = (MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4;
+    }
+    auto issue_copy = [&](int kb, int stage) {
+        uint8_t* st = smem + stage * kStageBytes;
+        if (MODE == MODE_MX) {
+            if (has_sa) dma4(p.sa + sa_off + kb * 4, st + kOffSA + wave * 64 * 4);
+            if (has_sb) dma4(sbp + sb_off + kb * 4, st + kOffSB + wave * 64 * 4);
+        } else {
+            if (has_sa) dma4(p.sa + sa_off + (int64_t)kb * p.sa_sk * 4, st + kOffSA + wave * 64 * 4);
+            if (has_sb) {
+                if (MODE == MODE_BLOCK128) dma4(sbp + sb_off + (int64_t)kb * p.sb_sk * 4, st + kOffSB);
+                else dma4(sbp + sb_off + (int64_t)kb * p.sb_sk * 4, st + kOffSB + wave * 64 * 4);
+            }
+        }
+        const uint32_t ko = (uint32_t)kb * BK;
+#pragma unroll
+        for (int j = 0; j < C::kDmaB; ++j)
+            dma16(bptr + offB[j] + ko, st + kOffB + (wave * C::kDmaB + j) * 8 * BK);
+#pragma unroll
+        for (int j = 0; j < C::kDmaA; ++j)
+            dma16(p.a + offA[j] + ko, st + kOffA + (wave * C::kDmaA + j) * 8 * BK);
+    };
 
     v4f acc[8][4];
 #pragma unroll
@@ -208,88 +267,97 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm(KArgs p) {
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int nk = p.K / BK;
-    issue_copy(0, 0);
-
-    // scale registers for the current slice
-    float sa_cur[4], sb_cur = 0.f;
-    uint32_t mxa_cur[4], mxb_cur[8];
-    auto load_scales = [&](int kb, float sa_v[4], float& sb_v, uint32_t mxa[4], uint32_t mxb[8]) {
-        if (MODE == MODE_MX) {
-            const uint8_t* sa8 = static_cast<const uint8_t*>(p.sa);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) mxa[mt] = sa8[sa_row[mt] + (uint32_t)(kb * 4 + q)];
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) mxb[nt] = sbp[sb_row[nt] + (uint32_t)(kb * 4 + q)];
-        } else {
-            const float* saf = static_cast<const float*>(p.sa);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) sa_v[mt] = saf[(int64_t)sa_row[mt] + (int64_t)kb * p.sa_sk];
-            if (MODE == MODE_BLOCK128)
-                sb_v = reinterpret_cast<const float*>(sbp)[(int64_t)nb_w * p.sb_sn + (int64_t)kb * p.sb_sk];
-        }
-    };
-    load_scales(0, sa_cur, sb_cur, mxa_cur, mxb_cur);
+    for (int s0 = 0; s0 < kStages - 1; ++s0)
+        if (s0 < nk) issue_copy(s0, s0);
 
     for (int kb = 0; kb < nk; ++kb) {
-        const int stage = kb & 1;
-        __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this wave's copies and scale loads landed
-        __syncthreads();                             // all waves' copies landed; stage^1 is free
-        float sa_nx[4], sb_nx = 0.f;
-        uint32_t mxa_nx[4], mxb_nx[8];
-        if (kb + 1 < nk) {
-            issue_copy(kb + 1, stage ^ 1);
-            load_scales(kb + 1, sa_nx, sb_nx, mxa_nx, mxb_nx);
-        }
-        const uint8_t* tB = smem[stage][0];
-        const uint8_t* tA = smem[stage][1];
+        const int stage = kb % kStages;
+        // This wave's copies for slice kb have landed once at most the
+        // kTileDma tile copies of slice kb+1 (issued last, three-stage
+        // pipeline) are outstanding; with two stages nothing newer is in flight.
+        if (kStages == 3 && kb + 1 < nk)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (C::kTileDma & 15) | ((C::kTileDma >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        // Every wave's copies landed and every wave finished reading the
+        // stage refilled next.  A plain s_barrier (with a compiler memory
+        // clobber) rather than __syncthreads(): the latter's release fence
+        // would also wait for copies still in flight.
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + kStages - 1 < nk) issue_copy(kb + kStages - 1, (kb + kStages - 1) % kStages);
+
+        const uint8_t* st = smem + stage * kStageBytes;
+        const uint8_t* tB = st + kOffB;
+        const uint8_t* tA = st + kOffA;
         v8i fa[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) fa[mt] = read_frag(tA, wm * 64 + mt * 16 + r16, q);
-        float sc[4];
-        if (MODE == MODE_BLOCK128) {
+
+        if (MODE == MODE_MX) {
+            const uint8_t* sa8 = st + kOffSA;
+            const uint8_t* sb8 = st + kOffSB;
+            int mxa[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) sc[mt] = sa_cur[mt] * sb_cur;
-        }
+            for (int mt = 0; mt < 4; ++mt) mxa[mt] = sa8[(wm * 64 + mt * 16 + r16) * 4 + q];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const v8i fb = read_frag(tB, wn * 128 + nt * 16 + r16, q);
-            float sbr[4];
-            if (MODE == MODE_ROW128) {
-                const float* sbf = reinterpret_cast<const float*>(sbp);
+            for (int nt = 0; nt < 8; ++nt) {
+                const int row = wn * 128 + nt * 16 + r16;
+                const v8i fb = read_frag(tB, row, q);
+                const int mxb = sb8[row * 4 + q];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sbr[r] = sbf[(int64_t)sb_row[nt] + (int64_t)r * p.sb_sn + (int64_t)kb * p.sb_sk];
+                for (int mt = 0; mt < 4; ++mt)
+                    acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[mt], acc[nt][mt], 0, 0, 0,
+                                                                                  mxb, 0, mxa[mt]);
             }
+        } else {
+            const float* saf = reinterpret_cast<const float*>(st + kOffSA);
+            const float* sbf = reinterpret_cast<const float*>(st + kOffSB);
+            float sam[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (MODE == MODE_MX) {
-                    acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        fb, fa[mt], acc[nt][mt], 0, 0, 0, (int)mxb_cur[nt], 0, (int)mxa_cur[mt]);
-                } else {
-                    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-                    const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        fb, fa[mt], zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+            for (int mt = 0; mt < 4; ++mt) sam[mt] = saf[wm * 64 + mt * 16 + r16];
+            float sc[4];
+            if (MODE == MODE_BLOCK128) {
+                const float sbv = sbf[wn];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) sc[mt] = sam[mt] * sbv;
+            }
+            v4f part[2][4];
+            float4 sbr[2];
+            auto promote = [&](int pt, int ps) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
                     if (MODE == MODE_BLOCK128) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[nt][mt][r] = __builtin_fmaf(part[r], sc[mt], acc[nt][mt][r]);
+                        for (int r = 0; r < 4; ++r)
+                            acc[pt][mt][r] = __builtin_fmaf(part[ps][mt][r], sc[mt], acc[pt][mt][r]);
                     } else {
+                        const float s4[4] = {sbr[ps].x, sbr[ps].y, sbr[ps].z, sbr[ps].w};
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            acc[nt][mt][r] = __builtin_fmaf(part[r], sa_cur[mt] * sbr[r], acc[nt][mt][r]);
+                            acc[pt][mt][r] = __builtin_fmaf(part[ps][mt][r], sam[mt] * s4[r], acc[pt][mt][r]);
                     }
                 }
+            };
+            v8i fb_next = read_frag(tB, wn * 128 + r16, q);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const int ps = C::kDefer ? (nt & 1) : 0;
+                const v8i fb = fb_next;
+                if (nt < 7) fb_next = read_frag(tB, wn * 128 + (nt + 1) * 16 + r16, q);
+                if (MODE == MODE_ROW128)
+                    sbr[ps] = *reinterpret_cast<const float4*>(sbf + wn * 128 + nt * 16 + 4 * q);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) part[ps][mt] = mfma_unit(fb, fa[mt]);
+                if (!C::kDefer) promote(nt, 0);
+                else if (nt > 0) promote(nt - 1, (nt - 1) & 1);
             }
-            __builtin_amdgcn_sched_barrier(0);   // keep the n-tile steps apart (register pressure)
-        }
-        if (kb + 1 < nk) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { sa_cur[i] = sa_nx[i]; mxa_cur[i] = mxa_nx[i]; }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) mxb_cur[i] = mxb_nx[i];
-            sb_cur = sb_nx;
+            if (C::kDefer) promote(7, 1);
         }
     }
 
     // ---------------------------------------------------------- epilogue
+    const int nw0 = n0 + wn * 128;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int m = m_begin + wm * 64 + mt * 16 + r16;
@@ -311,56 +379,75 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm(KArgs p) {
     }
 }
 
-template <int MODE, bool GROUPED>
+template <int MODE, bool GROUPED, int WAVES>
 hipError_t launch(const KArgs& p, bool out_f32, dim3 grid, hipStream_t st) {
+    constexpr int T = Cfg<WAVES>::kThreads;
     if (out_f32)
-        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true>), grid, dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES>), grid, dim3(T), 0, st, p);
     else
-        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false>), grid, dim3(kThreads), 0, st, p);
+        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false, WAVES>), grid, dim3(T), 0, st, p);
     return hipGetLastError();
+}
+
+template <int MODE, bool GROUPED, int WAVES>
+hipError_t launch_cfg(const KArgs& p, bool out_f32, hipStream_t st) {
+    constexpr int BM = Cfg<WAVES>::BM;
+    dim3 grid;
+    if (!GROUPED) {
+        grid = dim3((unsigned)(((int64_t)(p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN)));
+    } else {
+        // upper bound on the number of BM-row tiles over all groups
+        grid = dim3((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM + p.G));
+    }
+    return launch<MODE, GROUPED, WAVES>(p, out_f32, grid, st);
+}
+
+// Tile choice: 256 x 256 (8 waves) when it still gives every CU a tile,
+// else 256 x 128 (4 waves).
+int waves_for(int64_t rows, int64_t N) {
+    const int64_t big = ((rows + 255) / 256) * ((N + BN - 1) / BN);
+    return big >= 256 ? 8 : 4;
+}
+
+KArgs base_args(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const void* sa, const uint8_t* b,
+                int64_t ldb, const void* sb, void* c, int64_t ldc) {
+    KArgs p{};
+    p.M = (int32_t)M; p.N = (int32_t)N; p.K = (int32_t)K;
+    p.a = a; p.lda = lda; p.sa = static_cast<const uint8_t*>(sa);
+    p.b = b; p.ldb = ldb; p.sb = static_cast<const uint8_t*>(sb);
+    p.c = c; p.ldc = ldc;
+    return p;
 }
 
 }  // namespace
 
 hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
-    KArgs p{};
-    p.M = (int32_t)g.M; p.N = (int32_t)g.N; p.K = (int32_t)g.K;
-    p.a = g.a; p.lda = g.lda; p.sa = g.sa; p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk;
-    p.b = g.b; p.ldb = g.ldb; p.b_sg = 0; p.sb = g.sb; p.sb_sg = 0; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
-    p.c = g.c; p.ldc = g.ldc; p.G = 0; p.offsets = nullptr; p.a_rows = nullptr;
-    const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    dim3 grid((unsigned)tiles);
-    return g.bscale_row ? launch<MODE_ROW128, false>(p, g.out_f32, grid, st)
-                        : launch<MODE_BLOCK128, false>(p, g.out_f32, grid, st);
+    KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
+    p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
+    const int w = waves_for(g.M, g.N);
+    if (g.bscale_row)
+        return w == 8 ? launch_cfg<MODE_ROW128, false, 8>(p, g.out_f32, st) : launch_cfg<MODE_ROW128, false, 4>(p, g.out_f32, st);
+    return w == 8 ? launch_cfg<MODE_BLOCK128, false, 8>(p, g.out_f32, st) : launch_cfg<MODE_BLOCK128, false, 4>(p, g.out_f32, st);
 }
 
 hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
-    KArgs p{};
-    p.M = (int32_t)g.M; p.N = (int32_t)g.N; p.K = (int32_t)g.K;
-    p.a = g.a; p.lda = g.lda; p.sa = g.sa; p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk;
-    p.b = g.b; p.ldb = g.ldb; p.b_sg = g.b_sg; p.sb = g.sb; p.sb_sg = g.sb_sg; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
-    p.c = g.c; p.ldc = g.ldc; p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
-    // upper bound on the number of 256-row tiles over all groups
-    const int64_t mt = (g.M + BM - 1) / BM + g.G;
-    dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)mt);
-    return launch<MODE_BLOCK128, true>(p, g.out_f32, grid, st);
+    KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
+    p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
+    p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
+    return launch_cfg<MODE_BLOCK128, true, 4>(p, g.out_f32, st);
 }
 
 hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
-    KArgs p{};
-    p.M = (int32_t)g.M; p.N = (int32_t)g.N; p.K = (int32_t)g.K;
-    p.a = g.a; p.lda = g.lda; p.sa = g.sa; p.sa_sm = g.lds_a; p.sa_sk = 1;
-    p.b = g.b; p.ldb = g.ldb; p.b_sg = g.b_sg; p.sb = g.sb; p.sb_sg = g.sb_sg; p.sb_sn = g.lds_b; p.sb_sk = 1;
-    p.c = g.c; p.ldc = g.ldc; p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
-    if (g.G == 0) {
-        const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-        return launch<MODE_MX, false>(p, g.out_f32, dim3((unsigned)tiles), st);
-    }
-    const int64_t mt = (g.M + BM - 1) / BM + g.G;
-    return launch<MODE_MX, true>(p, g.out_f32, dim3((unsigned)((g.N + BN - 1) / BN), (unsigned)mt), st);
+    KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
+    p.sa_sm = g.lds_a; p.sa_sk = 1; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.lds_b; p.sb_sk = 1;
+    p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
+    if (g.G == 0)
+        return waves_for(g.M, g.N) == 8 ? launch_cfg<MODE_MX, false, 8>(p, g.out_f32, st)
+                                        : launch_cfg<MODE_MX, false, 4>(p, g.out_f32, st);
+    return launch_cfg<MODE_MX, true, 4>(p, g.out_f32, st);
 }
 
 }  // namespace fp8bs

@@ -108,6 +108,19 @@ def test_exact_integer_case_bit_exact(M, N, K):
     assert np.array_equal(y16, oracle.f64_to_bf16(yref))
 
 
+def test_exact_integer_case_256x256_tiles_ragged():
+    """Large enough for the 256 x 256 tile configuration, with M not a multiple
+    of the tile: sampled outputs (all of the last rows) bit-exact."""
+    M, N, K = 4100, 4096, 512
+    qa, sa, qb, sb = _exact_case(M, N, K, 77)
+    _, y32 = _run_both(dev(qa), dev(sa), dev(qb), dev(sb))
+    mi, ni = _sample_indices(M, N, 4000, 3)
+    mi = np.concatenate([mi, np.repeat(np.arange(M - 4, M), N)])
+    ni = np.concatenate([ni, np.tile(np.arange(N), 4)])
+    yref, _ = oracle.gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni)
+    assert np.array_equal(y32[mi, ni].astype(np.float64), yref)
+
+
 def test_dgrad_through_transposed_weight_copy():
     """dX = dY W: dY [512, 1024] 1x128, W [1024 out, 384 in] 128x128; B is the
     transposed code copy with W's block scales read transposed."""
