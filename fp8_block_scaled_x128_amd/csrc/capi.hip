@@ -126,6 +126,17 @@ fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, i
                     "fp8_quant_block2d");
 }
 
+// The kernels address a scale array with 32-bit byte offsets within one
+// group: the largest offset (rows - 1) * s_row + (slices - 1) * s_slice, in
+// elements of `bytes`, must stay below 4 GiB, and strides must not be negative.
+static fp8bs_status check_scale_extent(const char* name, int64_t rows, int64_t s_row, int64_t slices,
+                                       int64_t s_slice, int bytes) {
+    if (s_row < 0 || s_slice < 0) return fail(FP8BS_ERR_STRIDE, "%s: negative scale stride", name);
+    const double hi = ((double)(rows - 1) * (double)s_row + (double)(slices - 1) * (double)s_slice) * bytes;
+    if (hi >= 4294967296.0) return fail(FP8BS_ERR_SHAPE, "%s: scale array extent exceeds 4 GiB", name);
+    return FP8BS_OK;
+}
+
 static fp8bs_status check_gemm_common(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda, const void* b,
                                       int64_t ldb, const void* c, int64_t ldc, int out, int kmul) {
     if (M < 0 || N < 0 || K < 0) return fail(FP8BS_ERR_SHAPE, "negative size");
@@ -156,6 +167,10 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t
     if (!aligned(sa, 4) || !aligned(sb, 4)) return fail(FP8BS_ERR_ALIGN, "scales must be 4-byte aligned");
     if ((uint64_t)M * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
         return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
+    if ((v = check_scale_extent("sa", M, sa_stride_m, K / 128, sa_stride_k, 4)) != FP8BS_OK) return v;
+    if ((v = check_scale_extent("sb", bscale == FP8BS_BSCALE_ROW128 ? N : N / 128, sb_stride_n, K / 128,
+                                sb_stride_k, 4)) != FP8BS_OK)
+        return v;
     fp8bs_status d = check_device();
     if (d != FP8BS_OK) return d;
     GemmArgs g{};
@@ -182,6 +197,9 @@ fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t 
     if ((uint64_t)arows * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
         return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
     if ((total_rows + 255) / 256 + G > 65535) return fail(FP8BS_ERR_SHAPE, "too many row tiles");
+    if ((v = check_scale_extent("sa", arows, sa_stride_m, K / 128, sa_stride_k, 4)) != FP8BS_OK) return v;
+    if ((v = check_scale_extent("sb", N / 128, sb_stride_n, K / 128, sb_stride_k, 4)) != FP8BS_OK) return v;
+    if (sb_stride_g < 0 || b_stride_g < 0) return fail(FP8BS_ERR_STRIDE, "negative group stride");
     fp8bs_status d = check_device();
     if (d != FP8BS_OK) return d;
     GemmArgs g{};
@@ -249,6 +267,9 @@ fp8bs_status mxfp8_gemm(int64_t rows, int64_t N, int64_t K, int32_t G, const int
     if ((uint64_t)arows * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
         return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
     if ((rows + 255) / 256 + G > 65535) return fail(FP8BS_ERR_SHAPE, "too many row tiles");
+    if ((v = check_scale_extent("sa", arows, lds_a, 1, 0, 1)) != FP8BS_OK) return v;
+    if ((v = check_scale_extent("sb", N, lds_b, 1, 0, 1)) != FP8BS_OK) return v;
+    if (G > 0 && (sb_stride_g < 0 || b_stride_g < 0)) return fail(FP8BS_ERR_STRIDE, "negative group stride");
     fp8bs_status d = check_device();
     if (d != FP8BS_OK) return d;
     MxGemmArgs g{};

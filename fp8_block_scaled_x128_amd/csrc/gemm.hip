@@ -20,8 +20,9 @@
 //    from global memory into LDS with global_load_lds (no register staging),
 //    three stages deep, so two slices are in flight while one is consumed.
 //  - LDS rows are 128 bytes; 16-byte chunk c of row r sits in slot
-//    c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): 16 consecutive rows reading
-//    the same logical chunk hit 16 distinct 16-byte bank groups.  The copy
+//    c ^ (r & 7), which makes the fragment reads free of bank conflicts
+//    (measured with the LDS bank-conflict counter; the variant
+//    (r & 7) ^ ((r >> 3) & 1) costs 4 conflict cycles per read).  The copy
 //    realizes the swizzle by choosing which global chunk each lane fetches.
 //  - Wave w owns n rows [128 * (w >> 1), +128) and m rows [64 * (w & 1), +64):
 //    8 x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4 per slice.  Weight rows
@@ -33,6 +34,8 @@
 //    that the promotion overlaps the next n-tile's matrix work.
 //  - MX mode: the instruction accumulates in place with the per-lane UE8M0
 //    scale bytes of its row and 32-wide K block.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -47,25 +50,28 @@ constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
 
 // Tile configurations.  Every wave computes 128 weight rows x 64 activation
 // rows; waves are arranged 2 (n) x WAVES/2 (m).
-//   WAVES = 4: 256 x 128 tile, one wave per SIMD (512 registers each), three
-//              LDS stages, promotion deferred by one n-tile within the wave.
+//   WAVES = 4: 256 x 128 tile, one wave per SIMD (512 registers each),
+//              promotion deferred by one n-tile within the wave.
 //   WAVES = 8: 256 x 256 tile, two waves per SIMD (256 registers each) whose
-//              matrix and vector work interleave, two LDS stages.
+//              matrix and vector work interleave.
+// LDS: the weight tile of a slice is read during the whole slice, the
+// activation tile only at its start (each wave keeps its 4 activation
+// fragments in registers), so weight slices get kBStages = 3 buffers and
+// activation slices only kAStages (2 or 1), refilled as soon as every wave
+// has loaded its fragments.
 template <int WAVES>
 struct Cfg {
     static constexpr int kWaves = WAVES;
     static constexpr int kThreads = WAVES * 64;
     static constexpr int BM = 64 * (WAVES / 2);
-    static constexpr int kStages = WAVES == 4 ? 3 : 2;
-    static constexpr bool kDefer = WAVES == 4;
-    static constexpr int kOffB = 0;                       // weight tile: BN rows x 128 B
-    static constexpr int kOffA = BN * BK;                 // activation tile: BM rows x 128 B
-    static constexpr int kOffSA = kOffA + BM * BK;        // activation scales: BM x 4 B
-    static constexpr int kOffSB = kOffSA + BM * 4;        // weight scales: BN x 4 B
-    static constexpr int kStageBytes = kOffSB + BN * 4;
-    static constexpr int kDmaB = BN / 8 / WAVES;          // 16-byte copies per wave per slice
+    static constexpr bool kDefer = true;
+    static constexpr int kBStages = 3;
+    static constexpr int kAStages = WAVES == 4 ? 2 : 1;
+    static constexpr int kBStageBytes = BN * BK + BN * 4;   // weight tile + weight scales
+    static constexpr int kABufBytes = BM * BK + BM * 4;     // activation tile + activation scales
+    static constexpr int kLdsBytes = kBStages * kBStageBytes + kAStages * kABufBytes;
+    static constexpr int kDmaB = BN / 8 / WAVES;            // 16-byte copies per wave per slice
     static constexpr int kDmaA = BM / 8 / WAVES;
-    static constexpr int kTileDma = kDmaB + kDmaA;
 };
 
 enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2 };
@@ -80,47 +86,89 @@ struct KArgs {
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
 };
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
-// global -> LDS copies: lane l's bytes land at lds_wave_base + l * BYTES.
-// Issued as inline assembly on purpose: the compiler cannot tell which LDS
-// stage a copy writes, so for the builtin it would wait for every outstanding
-// copy (vmcnt(0)) before the first LDS read of the current stage, which
-// serializes the pipeline.  Ordering is explicit instead: s_waitcnt vmcnt(n)
-// on the issuing wave, then s_barrier, before any wave reads a stage.
+// LDS locations are handled as 32-bit LDS byte addresses (not generic
+// pointers, whose conversion back to LDS costs a null test per use).
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+    return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
-__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds_wave_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(m0), "v"(src) : "memory", "m0");
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((uintptr_t)addr);
 }
-__device__ __forceinline__ void dma4(const void* src, const uint8_t* lds_wave_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :: "s"(m0), "v"(src) : "memory", "m0");
+__device__ __forceinline__ float lds_readf(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)addr);
+}
+__device__ __forceinline__ f32x4 lds_readf4(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>((uintptr_t)addr);
+}
+__device__ __forceinline__ int lds_readu8(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint8_t*>((uintptr_t)addr);
 }
 
-// Read the 32-byte MFMA fragment of tile row `row` for lane quarter q.  The
-// 16x16x128 FP8 instruction takes K index 64 * (byte / 16) + 16 * q + byte % 16
-// from byte `byte` of a lane in quarter q (measured with one-hot probes of its
-// per-32-K scale slots: slot s covers bytes 0-15 of quarters 2s and 2s+1 for
-// s < 2 and bytes 16-31 of quarters 2(s-2) and 2(s-2)+1 for s >= 2, and the
-// scale of slot s comes from the lanes of quarter s).  The lane's low 16 bytes
-// are therefore logical chunk q of the row's 128-byte K slice and its high 16
+// global -> LDS copies: lane l's bytes land at LDS address lds_dst + l * BYTES
+// (lds_dst wave-uniform).  Issued as inline assembly on purpose: the compiler
+// cannot tell which LDS stage a copy writes, so for the builtin it would wait
+// for every outstanding copy (vmcnt(0)) before the first LDS read of the
+// current stage, which serializes the pipeline.  Ordering is explicit
+// instead: s_waitcnt vmcnt(n) on the issuing wave, then s_barrier, before any
+// wave reads a stage.  Copies use the scalar-base form: wave-uniform 64-bit
+// base in SGPRs plus a per-lane 32-bit byte offset (one VGPR per copy).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(m0), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// MFMA fragment of one 16-row tile for lane quarter q.  The 16x16x128 FP8
+// instruction takes K index 64 * (byte / 16) + 16 * q + byte % 16 from byte
+// `byte` of a lane in quarter q (measured with one-hot probes of its per-32-K
+// scale slots: slot s covers bytes 0-15 of quarters 2s and 2s+1 for s < 2 and
+// bytes 16-31 of quarters 2(s-2) and 2(s-2)+1 for s >= 2, and the scale of
+// slot s comes from the lanes of quarter s).  The lane's low 16 bytes are
+// therefore logical chunk q of its row's 128-byte K slice and its high 16
 // bytes chunk q + 4.  In this order the 32-wide K block s of the slice is
 // exactly scale slot s, which the MX mode relies on; the FP32-scale modes only
 // need both operands in the same order.
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int q) {
-    const int f = swz(row);
-    const uint8_t* base = tile + row * BK;
-    const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ f) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ f) << 4));
+//
+// Row r of a tile lives at r * 128 and its chunk c at slot c ^ (r & 7); tile
+// rows read together differ by multiples of 16, so the two per-lane chunk
+// offsets below serve every 16-row tile, which is then a constant offset.
+struct FragOff {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ FragOff frag_off(int r16, int q) {
+    const int f = swz(r16);
+    return FragOff{(uint32_t)(r16 * BK + ((q ^ f) << 4)), (uint32_t)(r16 * BK + (((q + 4) ^ f) << 4))};
+}
+// Per-lane LDS addresses of the fragments of the 16-row tile at `tile_row0`;
+// later tiles of the same buffer are then constant offsets (folded into the
+// ds_read offset field).  The empty asm keeps the compiler from hoisting the
+// sum out of the K loop and holding one address per tile in registers.
+__device__ __forceinline__ FragOff frag_base(uint32_t tile_row0, const FragOff& o) {
+    FragOff b{tile_row0 + o.lo, tile_row0 + o.hi};
+    asm volatile("" : "+v"(b.lo), "+v"(b.hi));
+    return b;
+}
+__device__ __forceinline__ v8i read_frag(const FragOff& b, uint32_t offset) {
+    const u32x4 lo = lds_read16(b.lo + offset);
+    const u32x4 hi = lds_read16(b.hi + offset);
     v8i r;
     r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
     r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
     return r;
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 __device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
@@ -131,15 +179,15 @@ __device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
 template <int MODE, bool GROUPED, bool OUTF32, int WAVES>
 __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
     using C = Cfg<WAVES>;
-    constexpr int BM = C::BM, kStages = C::kStages, kStageBytes = C::kStageBytes;
-    constexpr int kOffA = C::kOffA, kOffB = C::kOffB, kOffSA = C::kOffSA, kOffSB = C::kOffSB;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+    constexpr int BM = C::BM;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
     __shared__ int s_tile[2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave & 1, wm = wave >> 1;
     const int q = lane >> 4, r16 = lane & 15;
+    const FragOff fo = frag_off(r16, q);
 
     // ---------------------------------------------------------------- tile
     int32_t m_begin, m_end, n0;
@@ -227,37 +275,43 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
     // two 128-row blocks of the tile; ROW128 / MX -> waves 0..3 copy rows [64 w, +64).
     const bool has_sa = wave < BM / 64;
     const bool has_sb = (MODE == MODE_BLOCK128) ? wave == BM / 64 : wave < 4;
-    int64_t sa_off = 0, sb_off = 0;             // byte offsets without the slice term
+    uint32_t sa_off = 0, sb_off = 0;            // byte offsets without the slice term (< 4 GiB)
     if (has_sa) {
         const int m = arow(wave * 64 + lane);
-        sa_off = (MODE == MODE_MX) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4;
+        sa_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4);
     }
     if (MODE == MODE_BLOCK128) {
         const int nb = min(n0 / 128 + (lane & 1), (p.N - 1) / 128);
-        sb_off = (int64_t)nb * p.sb_sn * 4;
+        sb_off = (uint32_t)((int64_t)nb * p.sb_sn * 4);
     } else {
         const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
-        sb_off = (MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4;
+        sb_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4);
     }
-    auto issue_copy = [&](int kb, int stage) {
-        uint8_t* st = smem + stage * kStageBytes;
-        if (MODE == MODE_MX) {
-            if (has_sa) dma4(p.sa + sa_off + kb * 4, st + kOffSA + wave * 64 * 4);
-            if (has_sb) dma4(sbp + sb_off + kb * 4, st + kOffSB + wave * 64 * 4);
-        } else {
-            if (has_sa) dma4(p.sa + sa_off + (int64_t)kb * p.sa_sk * 4, st + kOffSA + wave * 64 * 4);
-            if (has_sb) {
-                if (MODE == MODE_BLOCK128) dma4(sbp + sb_off + (int64_t)kb * p.sb_sk * 4, st + kOffSB);
-                else dma4(sbp + sb_off + (int64_t)kb * p.sb_sk * 4, st + kOffSB + wave * 64 * 4);
-            }
+    const uint32_t lds0 = lds_addr(smem);
+    auto bstage = [&](int i) { return lds0 + (uint32_t)(i * C::kBStageBytes); };                      // weights + sb
+    auto abuf = [&](int i) { return lds0 + (uint32_t)(C::kBStages * C::kBStageBytes + i * C::kABufBytes); };  // acts + sa
+    // Copies of slice kb: the scale copies (wave-dependent, issued outside
+    // the n-tile loop), the activation tile with its scales, and weight-tile
+    // copy t of this wave.
+    auto copy_sb = [&](int kb, int stage) {
+        if (!has_sb) return;
+        const uint32_t st = bstage(stage) + BN * BK;
+        if (MODE == MODE_MX) dma4(sbp, sb_off + (uint32_t)(kb * 4), st + wave * 64 * 4);
+        else if (MODE == MODE_BLOCK128) dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st);
+        else dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st + wave * 64 * 4);
+    };
+    auto copy_a = [&](int kb, int buf) {
+        const uint32_t st = abuf(buf);
+        if (has_sa) {
+            if (MODE == MODE_MX) dma4(p.sa, sa_off + (uint32_t)(kb * 4), st + BM * BK + wave * 64 * 4);
+            else dma4(p.sa, sa_off + (uint32_t)(kb * p.sa_sk * 4), st + BM * BK + wave * 64 * 4);
         }
-        const uint32_t ko = (uint32_t)kb * BK;
 #pragma unroll
-        for (int j = 0; j < C::kDmaB; ++j)
-            dma16(bptr + offB[j] + ko, st + kOffB + (wave * C::kDmaB + j) * 8 * BK);
-#pragma unroll
-        for (int j = 0; j < C::kDmaA; ++j)
-            dma16(p.a + offA[j] + ko, st + kOffA + (wave * C::kDmaA + j) * 8 * BK);
+        for (int t = 0; t < C::kDmaA; ++t)
+            dma16(p.a, offA[t] + (uint32_t)kb * BK, st + (wave * C::kDmaA + t) * 8 * BK);
+    };
+    auto copy_b = [&](int kb, int stage, int t) {
+        dma16(bptr, offB[t] + (uint32_t)kb * BK, bstage(stage) + (wave * C::kDmaB + t) * 8 * BK);
     };
 
     v4f acc[8][4];
@@ -266,64 +320,102 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Issue order (the vmcnt waits rely on it): prologue sb(0) B(0),
+    // A(0..kAStages-1), sb(1) B(1); step kb then issues, after its second
+    // barrier, A(kb + kAStages) and sb(kb + 2), and spreads the weight-tile
+    // copies of slice kb + 2 over its n-tile loop.
     const int nk = p.K / BK;
+    copy_sb(0, 0);
 #pragma unroll
-    for (int s0 = 0; s0 < kStages - 1; ++s0)
-        if (s0 < nk) issue_copy(s0, s0);
+    for (int t = 0; t < C::kDmaB; ++t) copy_b(0, 0, t);
+#pragma unroll
+    for (int a0 = 0; a0 < C::kAStages; ++a0)
+        if (a0 < nk) copy_a(a0, a0);
+    if (nk > 1) {
+        copy_sb(1, 1);
+#pragma unroll
+        for (int t = 0; t < C::kDmaB; ++t) copy_b(1, 1, t);
+    }
 
-    for (int kb = 0; kb < nk; ++kb) {
-        const int stage = kb % kStages;
-        // This wave's copies for slice kb have landed once at most the
-        // kTileDma tile copies of slice kb+1 (issued last, three-stage
-        // pipeline) are outstanding; with two stages nothing newer is in flight.
-        if (kStages == 3 && kb + 1 < nk)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (C::kTileDma & 15) | ((C::kTileDma >> 4) << 14));
-        else
+    // One K slice.  COPY (compile time) = the weight tile of slice kb + 2 is
+    // copied during this step; it holds for every step but the last two, and
+    // keeping it a constant leaves each n-tile step a single basic block, so
+    // the sched_barrier below really bounds the scheduler (with a branch per
+    // copy the compiler sank every matrix instruction below all fragment reads).
+    auto step = [&](int kb, auto copy_tag) {
+        constexpr bool COPY = decltype(copy_tag)::value;
+        // Slice kb's copies have landed once at most the tile copies issued
+        // during step kb-1 (B(kb+1), and A(kb+1) with two activation buffers)
+        // are outstanding; scale copies were issued before them, so counting
+        // tile copies only is conservative.
+        if (kb + 1 < nk) {
+            constexpr int n_after = C::kDmaB + (C::kAStages == 2 ? C::kDmaA : 0);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (n_after & 15) | ((n_after >> 4) << 14));
+        } else {
             __builtin_amdgcn_s_waitcnt(0x0F70);
-        // Every wave's copies landed and every wave finished reading the
-        // stage refilled next.  A plain s_barrier (with a compiler memory
+        }
+        // Every wave's copies landed and every wave finished step kb-1, so
+        // B stage (kb+2)%3 is free.  A plain s_barrier (with a compiler memory
         // clobber) rather than __syncthreads(): the latter's release fence
         // would also wait for copies still in flight.
         asm volatile("s_barrier" ::: "memory");
-        if (kb + kStages - 1 < nk) issue_copy(kb + kStages - 1, (kb + kStages - 1) % kStages);
+        const int cst = (kb + 2) % C::kBStages;
+        const uint32_t tB = bstage(kb % C::kBStages);
+        const uint32_t tA = abuf(kb % C::kAStages);
 
-        const uint8_t* st = smem + stage * kStageBytes;
-        const uint8_t* tB = st + kOffB;
-        const uint8_t* tA = st + kOffA;
         v8i fa[4];
+        const FragOff ab = frag_base(tA + wm * 64 * BK, fo);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) fa[mt] = read_frag(tA, wm * 64 + mt * 16 + r16, q);
+        for (int mt = 0; mt < 4; ++mt) fa[mt] = read_frag(ab, mt * 16 * BK);
+        // activation-side scales of the wave's 4 m-tiles (bytes in MX mode)
+        const uint32_t sa_lds = opaque(tA + BM * BK + (wm * 64 + r16) * 4);
+        int mxa[4];
+        float sam[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
+            else sam[mt] = lds_readf(sa_lds + mt * 64);
+        }
+        // Every wave has its activation fragments and scales in registers:
+        // the activation buffer can be refilled.
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        if (kb + C::kAStages < nk) copy_a(kb + C::kAStages, kb % C::kAStages);
+        if (COPY) copy_sb(kb + 2, cst);
+        // weight-tile copies of slice kb + 2, spread over the n-tile steps
+        auto copy_step = [&](int nt) {
+            if (!COPY) return;
+#pragma unroll
+            for (int t = 0; t < C::kDmaB; ++t)
+                if (t * 8 / C::kDmaB == nt) copy_b(kb + 2, cst, t);
+        };
 
         if (MODE == MODE_MX) {
-            const uint8_t* sa8 = st + kOffSA;
-            const uint8_t* sb8 = st + kOffSB;
-            int mxa[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) mxa[mt] = sa8[(wm * 64 + mt * 16 + r16) * 4 + q];
+            const uint32_t sb8 = opaque(tB + BN * BK + (wn * 128 + r16) * 4 + q);
+            const FragOff bb = frag_base(tB + wn * 128 * BK, fo);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
-                const int row = wn * 128 + nt * 16 + r16;
-                const v8i fb = read_frag(tB, row, q);
-                const int mxb = sb8[row * 4 + q];
+                const v8i fb = read_frag(bb, nt * 16 * BK);
+                const int mxb = lds_readu8(sb8 + nt * 64);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
                     acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[mt], acc[nt][mt], 0, 0, 0,
                                                                                   mxb, 0, mxa[mt]);
+                copy_step(nt);
+                // keep the scheduler from hoisting every n-tile's fragment
+                // reads to the top of the slice (8 fragments = 64 registers)
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            const float* saf = reinterpret_cast<const float*>(st + kOffSA);
-            const float* sbf = reinterpret_cast<const float*>(st + kOffSB);
-            float sam[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) sam[mt] = saf[wm * 64 + mt * 16 + r16];
+            const uint32_t sbf = tB + BN * BK;
             float sc[4];
             if (MODE == MODE_BLOCK128) {
-                const float sbv = sbf[wn];
+                const float sbv = lds_readf(sbf + wn * 4);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) sc[mt] = sam[mt] * sbv;
             }
             v4f part[2][4];
-            float4 sbr[2];
+            f32x4 sbr[2];
             auto promote = [&](int pt, int ps) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
@@ -332,29 +424,35 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
                         for (int r = 0; r < 4; ++r)
                             acc[pt][mt][r] = __builtin_fmaf(part[ps][mt][r], sc[mt], acc[pt][mt][r]);
                     } else {
-                        const float s4[4] = {sbr[ps].x, sbr[ps].y, sbr[ps].z, sbr[ps].w};
+                        const float s4[4] = {sbr[ps][0], sbr[ps][1], sbr[ps][2], sbr[ps][3]};
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             acc[pt][mt][r] = __builtin_fmaf(part[ps][mt][r], sam[mt] * s4[r], acc[pt][mt][r]);
                     }
                 }
             };
-            v8i fb_next = read_frag(tB, wn * 128 + r16, q);
+            const FragOff bb = frag_base(tB + wn * 128 * BK, fo);
+            const uint32_t sbr_lds = opaque(sbf + (wn * 128 + 4 * q) * 4);
+            v8i fb_next = read_frag(bb, 0);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 const int ps = C::kDefer ? (nt & 1) : 0;
                 const v8i fb = fb_next;
-                if (nt < 7) fb_next = read_frag(tB, wn * 128 + (nt + 1) * 16 + r16, q);
-                if (MODE == MODE_ROW128)
-                    sbr[ps] = *reinterpret_cast<const float4*>(sbf + wn * 128 + nt * 16 + 4 * q);
+                if (nt < 7) fb_next = read_frag(bb, (nt + 1) * 16 * BK);
+                if (MODE == MODE_ROW128) sbr[ps] = lds_readf4(sbr_lds + nt * 64);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) part[ps][mt] = mfma_unit(fb, fa[mt]);
+                copy_step(nt);
                 if (!C::kDefer) promote(nt, 0);
                 else if (nt > 0) promote(nt - 1, (nt - 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (C::kDefer) promote(7, 1);
         }
-    }
+    };
+    int kb = 0;
+    for (; kb + 2 < nk; ++kb) step(kb, std::true_type{});
+    for (; kb < nk; ++kb) step(kb, std::false_type{});
 
     // ---------------------------------------------------------- epilogue
     const int nw0 = n0 + wn * 128;
