@@ -54,24 +54,48 @@ constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
 //              promotion deferred by one n-tile within the wave.
 //   WAVES = 8: 256 x 256 tile, two waves per SIMD (256 registers each) whose
 //              matrix and vector work interleave.
-// LDS: the weight tile of a slice is read during the whole slice, the
-// activation tile only at its start (each wave keeps its 4 activation
-// fragments in registers), so weight slices get kBStages = 3 buffers and
-// activation slices only kAStages (2 or 1), refilled as soon as every wave
-// has loaded its fragments.
+// LDS pipeline.  The weight tile of a slice is read during the whole slice,
+// the activation tile only at its start (each wave keeps its 4 activation
+// fragments in registers).  Weight slices get kBStages buffers; activation
+// slices kAStages, and with kABarrier a second barrier right after the
+// fragment reads lets the current activation buffer be refilled at once.
+// A slice's copies are issued kLeadA / kLeadB steps before it is consumed.
 template <int WAVES>
 struct Cfg {
     static constexpr int kWaves = WAVES;
     static constexpr int kThreads = WAVES * 64;
     static constexpr int BM = 64 * (WAVES / 2);
     static constexpr bool kDefer = true;
+    // Measured on the MLP shapes (M 4096; N 9728, K 2560 and N 2560, K 9728):
+    // 256x256 tile: 3 weight stages + 1 activation buffer with the second
+    // barrier beats 2 + 2 without it (equal on the first shape, 9% faster on
+    // the second); 256x128 tile: 3 + 2 without the second barrier is 2-3%
+    // faster than with it.
     static constexpr int kBStages = 3;
     static constexpr int kAStages = WAVES == 4 ? 2 : 1;
+    static constexpr bool kABarrier = WAVES == 8;
     static constexpr int kBStageBytes = BN * BK + BN * 4;   // weight tile + weight scales
     static constexpr int kABufBytes = BM * BK + BM * 4;     // activation tile + activation scales
     static constexpr int kLdsBytes = kBStages * kBStageBytes + kAStages * kABufBytes;
     static constexpr int kDmaB = BN / 8 / WAVES;            // 16-byte copies per wave per slice
     static constexpr int kDmaA = BM / 8 / WAVES;
+    static constexpr int kLeadA = kABarrier ? kAStages : kAStages - 1;
+    static constexpr int kLeadB = kBStages - 1;
+    static constexpr int kLeadMax = kLeadA > kLeadB ? kLeadA : kLeadB;
+    // Within a step the activation copies are issued before the weight
+    // copies.  At the top of step kb, slice kb's copies have landed once at
+    // most kNAfter tile copies (those issued after its last one) remain.
+    static constexpr int kNAfter = kLeadA < kLeadB ? kDmaB + (kLeadA - 1) * (kDmaA + kDmaB)
+                                                   : (kLeadB - 1) * (kDmaA + kDmaB);
+    // That count assumes the steps in between issued full copies, which holds
+    // for leads of 1 or 2 (a step short of copies is then the last one).
+    static_assert(kLeadA >= 1 && kLeadB >= 1 && kLeadMax <= 2, "pipeline leads must be 1 or 2");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    // tile copy slots: activation copy t in n-tile step t; weight copies
+    // after the activation copies when they must follow them, else in step t
+    // (lead 1: as early as possible) or spread over the slice (lead 2)
+    static constexpr int kBFirst = kLeadA < kLeadB ? kDmaA : 0;
+    static constexpr int b_slot(int t) { return kLeadB == 1 ? t : kBFirst + t * (8 - kBFirst) / kDmaB; }
 };
 
 enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2 };
@@ -300,15 +324,14 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
         else if (MODE == MODE_BLOCK128) dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st);
         else dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st + wave * 64 * 4);
     };
-    auto copy_a = [&](int kb, int buf) {
-        const uint32_t st = abuf(buf);
-        if (has_sa) {
-            if (MODE == MODE_MX) dma4(p.sa, sa_off + (uint32_t)(kb * 4), st + BM * BK + wave * 64 * 4);
-            else dma4(p.sa, sa_off + (uint32_t)(kb * p.sa_sk * 4), st + BM * BK + wave * 64 * 4);
-        }
-#pragma unroll
-        for (int t = 0; t < C::kDmaA; ++t)
-            dma16(p.a, offA[t] + (uint32_t)kb * BK, st + (wave * C::kDmaA + t) * 8 * BK);
+    auto copy_sa = [&](int kb, int buf) {
+        if (!has_sa) return;
+        const uint32_t st = abuf(buf) + BM * BK + wave * 64 * 4;
+        if (MODE == MODE_MX) dma4(p.sa, sa_off + (uint32_t)(kb * 4), st);
+        else dma4(p.sa, sa_off + (uint32_t)(kb * p.sa_sk * 4), st);
+    };
+    auto copy_a = [&](int kb, int buf, int t) {
+        dma16(p.a, offA[t] + (uint32_t)kb * BK, abuf(buf) + (wave * C::kDmaA + t) * 8 * BK);
     };
     auto copy_b = [&](int kb, int stage, int t) {
         dma16(bptr, offB[t] + (uint32_t)kb * BK, bstage(stage) + (wave * C::kDmaB + t) * 8 * BK);
@@ -320,46 +343,50 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Issue order (the vmcnt waits rely on it): prologue sb(0) B(0),
-    // A(0..kAStages-1), sb(1) B(1); step kb then issues, after its second
-    // barrier, A(kb + kAStages) and sb(kb + 2), and spreads the weight-tile
-    // copies of slice kb + 2 over its n-tile loop.
+    // Issue order (the waits rely on it): step kb issues the copies of
+    // activation slice kb + kLeadA (scales right after the barriers, tile in
+    // the first n-tile steps) and then those of weight slice kb + kLeadB; the
+    // prologue issues the same sequence for the steps -kLeadMax..-1.
     const int nk = p.K / BK;
-    copy_sb(0, 0);
 #pragma unroll
-    for (int t = 0; t < C::kDmaB; ++t) copy_b(0, 0, t);
+    for (int j = -C::kLeadMax; j < 0; ++j) {
+        const int sa_kb = j + C::kLeadA, sb_kb = j + C::kLeadB;
+        if (sa_kb >= 0 && sa_kb < nk) {
+            copy_sa(sa_kb, sa_kb % C::kAStages);
 #pragma unroll
-    for (int a0 = 0; a0 < C::kAStages; ++a0)
-        if (a0 < nk) copy_a(a0, a0);
-    if (nk > 1) {
-        copy_sb(1, 1);
+            for (int t = 0; t < C::kDmaA; ++t) copy_a(sa_kb, sa_kb % C::kAStages, t);
+        }
+        if (sb_kb >= 0 && sb_kb < nk) {
+            copy_sb(sb_kb, sb_kb % C::kBStages);
 #pragma unroll
-        for (int t = 0; t < C::kDmaB; ++t) copy_b(1, 1, t);
+            for (int t = 0; t < C::kDmaB; ++t) copy_b(sb_kb, sb_kb % C::kBStages, t);
+        }
     }
 
-    // One K slice.  COPY (compile time) = the weight tile of slice kb + 2 is
-    // copied during this step; it holds for every step but the last two, and
-    // keeping it a constant leaves each n-tile step a single basic block, so
-    // the sched_barrier below really bounds the scheduler (with a branch per
-    // copy the compiler sank every matrix instruction below all fragment reads).
-    auto step = [&](int kb, auto copy_tag) {
-        constexpr bool COPY = decltype(copy_tag)::value;
-        // Slice kb's copies have landed once at most the tile copies issued
-        // during step kb-1 (B(kb+1), and A(kb+1) with two activation buffers)
-        // are outstanding; scale copies were issued before them, so counting
-        // tile copies only is conservative.
+    // One K slice.  CA / CB (compile time): this step copies activation slice
+    // kb + kLeadA / weight slice kb + kLeadB.  Both hold in every step but the
+    // last one or two; keeping them constants leaves each n-tile step a single basic
+    // block, so the sched_barrier below really bounds the scheduler (with a
+    // branch per copy the compiler sank every matrix instruction below all
+    // fragment reads).
+    auto step = [&](int kb, auto ca_tag, auto cb_tag) {
+        constexpr bool CA = decltype(ca_tag)::value, CB = decltype(cb_tag)::value;
+        // Wait for this wave's copies of slice kb (scale copies were issued
+        // before the tile copies of their step, so counting tile copies only
+        // is conservative).
         if (kb + 1 < nk) {
-            constexpr int n_after = C::kDmaB + (C::kAStages == 2 ? C::kDmaA : 0);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (n_after & 15) | ((n_after >> 4) << 14));
+            constexpr int n = C::kNAfter;
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
         } else {
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         // Every wave's copies landed and every wave finished step kb-1, so
-        // B stage (kb+2)%3 is free.  A plain s_barrier (with a compiler memory
+        // the buffers of slice kb-1 are free.  A plain s_barrier (with a compiler memory
         // clobber) rather than __syncthreads(): the latter's release fence
         // would also wait for copies still in flight.
         asm volatile("s_barrier" ::: "memory");
-        const int cst = (kb + 2) % C::kBStages;
+        const int a_kb = kb + C::kLeadA, b_kb = kb + C::kLeadB;
+        const int a_buf = a_kb % C::kAStages, cst = b_kb % C::kBStages;
         const uint32_t tB = bstage(kb % C::kBStages);
         const uint32_t tA = abuf(kb % C::kAStages);
 
@@ -376,18 +403,22 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
             if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
             else sam[mt] = lds_readf(sa_lds + mt * 64);
         }
-        // Every wave has its activation fragments and scales in registers:
-        // the activation buffer can be refilled.
-        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
-        asm volatile("s_barrier" ::: "memory");
-        if (kb + C::kAStages < nk) copy_a(kb + C::kAStages, kb % C::kAStages);
-        if (COPY) copy_sb(kb + 2, cst);
-        // weight-tile copies of slice kb + 2, spread over the n-tile steps
+        if (C::kABarrier) {
+            // Every wave has its activation fragments and scales in
+            // registers: the current activation buffer can be refilled.
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+            asm volatile("s_barrier" ::: "memory");
+        }
+        if (CA) copy_sa(a_kb, a_buf);
+        if (CB) copy_sb(b_kb, cst);
+        // tile copies, placed in the n-tile steps given by Cfg
         auto copy_step = [&](int nt) {
-            if (!COPY) return;
+#pragma unroll
+            for (int t = 0; t < C::kDmaA; ++t)
+                if (CA && t == nt) copy_a(a_kb, a_buf, t);
 #pragma unroll
             for (int t = 0; t < C::kDmaB; ++t)
-                if (t * 8 / C::kDmaB == nt) copy_b(kb + 2, cst, t);
+                if (CB && C::b_slot(t) == nt) copy_b(b_kb, cst, t);
         };
 
         if (MODE == MODE_MX) {
@@ -451,8 +482,18 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
         }
     };
     int kb = 0;
-    for (; kb + 2 < nk; ++kb) step(kb, std::true_type{});
-    for (; kb < nk; ++kb) step(kb, std::false_type{});
+    for (; kb + C::kLeadMax < nk; ++kb) step(kb, std::true_type{}, std::true_type{});
+    // At most kLeadMax (<= 2) steps remain.  With unequal leads the next to
+    // last step still copies the side with the longer lead; the last step
+    // copies nothing.
+    if constexpr (C::kLeadA != C::kLeadB) {
+        if (kb + 2 == nk) {
+            step(kb, std::integral_constant<bool, (C::kLeadA < C::kLeadB)>{},
+                 std::integral_constant<bool, (C::kLeadB < C::kLeadA)>{});
+            ++kb;
+        }
+    }
+    for (; kb < nk; ++kb) step(kb, std::false_type{}, std::false_type{});
 
     // ---------------------------------------------------------- epilogue
     const int nw0 = n0 + wn * 128;
@@ -469,8 +510,8 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
                 *reinterpret_cast<float4*>(dst) = make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
             } else {
                 uint16_t* dst = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
-                const uint32_t lo = f32_to_bf16_rne(acc[nt][mt][0]) | (f32_to_bf16_rne(acc[nt][mt][1]) << 16);
-                const uint32_t hi = f32_to_bf16_rne(acc[nt][mt][2]) | (f32_to_bf16_rne(acc[nt][mt][3]) << 16);
+                const uint32_t lo = pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]);
+                const uint32_t hi = pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]);
                 *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
             }
         }
@@ -500,11 +541,15 @@ hipError_t launch_cfg(const KArgs& p, bool out_f32, hipStream_t st) {
     return launch<MODE, GROUPED, WAVES>(p, out_f32, grid, st);
 }
 
-// Tile choice: 256 x 256 (8 waves) when it still gives every CU a tile,
-// else 256 x 128 (4 waves).
-int waves_for(int64_t rows, int64_t N) {
-    const int64_t big = ((rows + 255) / 256) * ((N + BN - 1) / BN);
-    return big >= 256 ? 8 : 4;
+// Tile choice by rounds of tiles over the 256 CUs: a 256 x 256 tile (8 waves)
+// does twice the work of a 256 x 128 tile (4 waves) in about 4/3 of its time,
+// so it wins unless it saves no round (small problems, where the smaller tile
+// finishes first).  `extra_tiles` counts partial tiles of grouped problems.
+int waves_for(int64_t rows, int64_t N, int64_t extra_tiles = 0) {
+    const int64_t ntn = (N + BN - 1) / BN;
+    const int64_t r8 = (((rows + 255) / 256 + extra_tiles) * ntn + 255) / 256;
+    const int64_t r4 = (((rows + 127) / 128 + extra_tiles) * ntn + 255) / 256;
+    return 4 * r8 <= 3 * r4 ? 8 : 4;
 }
 
 KArgs base_args(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const void* sa, const uint8_t* b,
@@ -534,7 +579,8 @@ hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st) {
     KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
     p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
     p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
-    return launch_cfg<MODE_BLOCK128, true, 4>(p, g.out_f32, st);
+    return waves_for(g.M, g.N, g.G / 2) == 8 ? launch_cfg<MODE_BLOCK128, true, 8>(p, g.out_f32, st)
+                                              : launch_cfg<MODE_BLOCK128, true, 4>(p, g.out_f32, st);
 }
 
 hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st) {
@@ -545,7 +591,8 @@ hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st) {
     if (g.G == 0)
         return waves_for(g.M, g.N) == 8 ? launch_cfg<MODE_MX, false, 8>(p, g.out_f32, st)
                                         : launch_cfg<MODE_MX, false, 4>(p, g.out_f32, st);
-    return launch_cfg<MODE_MX, true, 4>(p, g.out_f32, st);
+    return waves_for(g.M, g.N, g.G / 2) == 8 ? launch_cfg<MODE_MX, true, 8>(p, g.out_f32, st)
+                                              : launch_cfg<MODE_MX, true, 4>(p, g.out_f32, st);
 }
 
 }  // namespace fp8bs

@@ -2,6 +2,8 @@
 import numpy as np
 import torch
 
+import oracle
+
 
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
     """numpy uint16 bf16 bit patterns -> cuda bf16 tensor."""
@@ -145,3 +147,36 @@ def check_vs_oracle_and_model(y_gpu, yref, babs, y_model, hbound, bf16_out=False
         assert rel <= allowed, "relative Frobenius error vs oracle %.3g > %.3g" % (rel, allowed)
         return rel, rel_model
     return None, None
+
+
+def sample_indices(M, N, count, seed):
+    rng = np.random.default_rng(seed)
+    mi = rng.integers(0, M, count)
+    ni = rng.integers(0, N, count)
+    # corners of every 256 x 256 output tile and the matrix edges
+    tm = np.arange(0, M, 256)
+    tn = np.arange(0, N, 256)
+    cm, cn = np.meshgrid(np.concatenate([tm, np.minimum(tm + 255, M - 1)]),
+                         np.concatenate([tn, np.minimum(tn + 255, N - 1)]), indexing="ij")
+    return np.concatenate([mi, cm.reshape(-1)]), np.concatenate([ni, cn.reshape(-1)])
+
+
+def verify(qa, sa, qb, sb, y32, y16=None, bscale_row=False, mi=None, ni=None, mx=False):
+    """Check GPU outputs (full matrices, or the entries (mi, ni)) against the
+    oracle and against the datapath truncation model."""
+    M, N = qa.shape[0], qb.shape[0]
+    if mi is None:
+        mi, ni = (g.reshape(-1) for g in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+    if mx:
+        yref, babs = oracle.gemm_mx_sampled(qa, sa, qb, sb, mi, ni)
+        fn = mx_scale_fn(sa, sb)
+    else:
+        mode = oracle.BSCALE_ROW128 if bscale_row else oracle.BSCALE_BLOCK128
+        yref, babs = oracle.gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni, mode)
+        fn = fp32_scale_fn(sa, sb, bscale_row)
+    ymod, hb = run_truncation(qa, qb, fn, mi, ni)
+    if y32 is not None:
+        rel, relm = check_vs_oracle_and_model(y32[mi, ni], yref, babs, ymod, hb)
+        print("rel. Frobenius error vs oracle %s, vs datapath model %s" % (rel, relm), flush=True)
+    if y16 is not None:
+        check_vs_oracle_and_model(y16[mi, ni], yref, babs, ymod, hb, bf16_out=True)

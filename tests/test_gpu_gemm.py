@@ -21,8 +21,7 @@ import torch
 
 import oracle
 from fp8_block_scaled_x128_amd import inputs, ops
-from gpu_util import (check_vs_oracle_and_model, dev, dev_bf16, fp32_scale_fn, host, mx_scale_fn,
-                      run_truncation)
+from gpu_util import dev, dev_bf16, host, sample_indices, verify
 
 pytestmark = pytest.mark.gpu
 
@@ -40,27 +39,6 @@ def _linear_operands(x, w):
     qa, sa = ops.quant_rowblock(dev_bf16(x), ops.AXIS_ROW, "m_major")
     qb, sb, _ = ops.quant_block2d(dev_bf16(w))
     return qa, sa, qb, sb
-
-
-def verify(qa, sa, qb, sb, y32, y16=None, bscale_row=False, mi=None, ni=None, mx=False):
-    """Check GPU outputs (full matrices, or the entries (mi, ni)) against the
-    oracle and against the datapath truncation model."""
-    M, N = qa.shape[0], qb.shape[0]
-    if mi is None:
-        mi, ni = (g.reshape(-1) for g in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
-    if mx:
-        yref, babs = oracle.gemm_mx_sampled(qa, sa, qb, sb, mi, ni)
-        fn = mx_scale_fn(sa, sb)
-    else:
-        mode = oracle.BSCALE_ROW128 if bscale_row else oracle.BSCALE_BLOCK128
-        yref, babs = oracle.gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni, mode)
-        fn = fp32_scale_fn(sa, sb, bscale_row)
-    ymod, hb = run_truncation(qa, qb, fn, mi, ni)
-    if y32 is not None:
-        rel, relm = check_vs_oracle_and_model(y32[mi, ni], yref, babs, ymod, hb)
-        _say("rel. Frobenius error vs oracle %s, vs datapath model %s" % (rel, relm))
-    if y16 is not None:
-        check_vs_oracle_and_model(y16[mi, ni], yref, babs, ymod, hb, bf16_out=True)
 
 
 def _run_both(qa, sa, qb, sb, bscale=ops.BSCALE_BLOCK128):
@@ -114,7 +92,7 @@ def test_exact_integer_case_256x256_tiles_ragged():
     M, N, K = 4100, 4096, 512
     qa, sa, qb, sb = _exact_case(M, N, K, 77)
     _, y32 = _run_both(dev(qa), dev(sa), dev(qb), dev(sb))
-    mi, ni = _sample_indices(M, N, 4000, 3)
+    mi, ni = sample_indices(M, N, 4000, 3)
     mi = np.concatenate([mi, np.repeat(np.arange(M - 4, M), N)])
     ni = np.concatenate([ni, np.tile(np.arange(N), 4)])
     yref, _ = oracle.gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni)
@@ -146,18 +124,6 @@ def test_wgrad_row128():
     verify(host(qa), host(sa), host(qb), host(sb), host(y32), bscale_row=True)
 
 
-def _sample_indices(M, N, count, seed):
-    rng = np.random.default_rng(seed)
-    mi = rng.integers(0, M, count)
-    ni = rng.integers(0, N, count)
-    # corners of every 256 x 256 output tile and the matrix edges
-    tm = np.arange(0, M, 256)
-    tn = np.arange(0, N, 256)
-    cm, cn = np.meshgrid(np.concatenate([tm, np.minimum(tm + 255, M - 1)]),
-                         np.concatenate([tn, np.minimum(tn + 255, N - 1)]), indexing="ij")
-    return np.concatenate([mi, cm.reshape(-1)]), np.concatenate([ni, cn.reshape(-1)])
-
-
 @pytest.mark.parametrize("part", ["up", "down"])
 def test_qwen3_4b_mlp_full_size_sampled(part):
     d = inputs.qwen3_4b_mlp(1, parts=(part,))
@@ -166,8 +132,33 @@ def test_qwen3_4b_mlp_full_size_sampled(part):
     qa, sa, qb, sb = _linear_operands(x, w)
     y16, y32 = _run_both(qa, sa, qb, sb)
     M, N = y32.shape
-    mi, ni = _sample_indices(M, N, 3000, 7)
+    mi, ni = sample_indices(M, N, 3000, 7)
     verify(host(qa), host(sa), host(qb), host(sb), y32, y16, mi=mi, ni=ni)
+
+
+def test_qwen3_4b_backward_full_size_sampled():
+    """Backward GEMMs of the MLP up-projection at full size, FP32 outputs:
+    dgrad dX = dY W (dY 1x128, W's transposed codes with its 128x128 block
+    scales read transposed, no requantization) and wgrad dW = dY^T X (both
+    requantized 128x1 along tokens from the bf16 originals)."""
+    d = inputs.qwen3_4b_mlp_backward(2)
+    dy, x, w = d["dy"], d["x"], d["w"]
+    qdy, sdy = ops.quant_rowblock(dev_bf16(dy), ops.AXIS_ROW, "m_major")
+    qw, sw, qwt = ops.quant_block2d(dev_bf16(w), transposed=True)
+    dx = ops.gemm(qdy, sdy, qwt, sw.t(), ops.BSCALE_BLOCK128, torch.float32)
+    torch.cuda.synchronize()
+    _say("dgrad", tuple(dx.shape))
+    mi, ni = sample_indices(dx.shape[0], dx.shape[1], 3000, 21)
+    verify(host(qdy), host(sdy), np.ascontiguousarray(host(qw).T), np.ascontiguousarray(host(sw).T), host(dx),
+           mi=mi, ni=ni)
+    del dx
+    qa, sa = ops.quant_rowblock(dev_bf16(dy), ops.AXIS_COL, "m_major")
+    qb, sb = ops.quant_rowblock(dev_bf16(x), ops.AXIS_COL, "m_major")
+    dw = ops.gemm(qa, sa, qb, sb, ops.BSCALE_ROW128, torch.float32)
+    torch.cuda.synchronize()
+    _say("wgrad", tuple(dw.shape))
+    mi, ni = sample_indices(dw.shape[0], dw.shape[1], 3000, 22)
+    verify(host(qa), host(sa), host(qb), host(sb), host(dw), bscale_row=True, mi=mi, ni=ni)
 
 
 # ---------------------------------------------------------------- grouped
@@ -232,6 +223,67 @@ def test_grouped_exact_integer_case():
                          dqb, K, N * K, dsb, dsb.stride(0), dsb.stride(1), dsb.stride(2), c, N, ops.OUT_FP32)
     torch.cuda.synchronize()
     assert np.array_equal(host(c).astype(np.float64), yref)
+
+
+def _group_samples(offsets, N, seed, per_group=20):
+    """Per non-empty group: its first and last 3 rows and `per_group` random
+    rows, every column; returns {g: (local rows, local cols)}."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for g in range(offsets.size - 1):
+        n = int(offsets[g + 1] - offsets[g])
+        if n == 0:
+            continue
+        rows = np.unique(np.concatenate([np.arange(min(3, n)), np.arange(max(0, n - 3), n),
+                                         rng.integers(0, n, per_group)]))
+        mi = np.repeat(rows, N)
+        ni = np.tile(np.arange(N), rows.size)
+        out[g] = (mi, ni)
+    return out
+
+
+GROUP_COUNTS_LARGE = np.array([0, 1500, 1, 0, 2300, 1777, 0, 2501])   # 256 x 256 tiles
+
+
+def test_grouped_exact_integer_case_256x256_tiles():
+    """Grouped GEMM large enough for the 256 x 256 tile configuration, ragged
+    and empty groups, exact operands: sampled outputs bit-exact."""
+    offsets = np.concatenate([[0], np.cumsum(GROUP_COUNTS_LARGE)]).astype(np.int32)
+    rows, G, N, K = int(offsets[-1]), GROUP_COUNTS_LARGE.size, 1024, 256
+    qa, sa, _, _ = _exact_case(rows, 128, K, 11)
+    qbs, sbs = zip(*[_exact_case(128, N, K, 200 + g)[2:] for g in range(G)])
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    c = torch.full((rows, N), float("nan"), dtype=torch.float32, device="cuda")
+    dsa, dqb, dsb = dev(sa), dev(qb), dev(sb)
+    ops.fp8_grouped_gemm(rows, N, K, G, dev(offsets), None, rows, dev(qa), K, dsa, dsa.stride(0), dsa.stride(1),
+                         dqb, K, N * K, dsb, dsb.stride(0), dsb.stride(1), dsb.stride(2), c, N, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    ch = host(c)
+    for g, (mi, ni) in _group_samples(offsets, N, 12).items():
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        yref, _ = oracle.gemm_blockscaled_sampled(qa[r0:r1], sa[r0:r1], qb[g], sb[g], mi, ni)
+        assert np.array_equal(ch[r0:r1][mi, ni].astype(np.float64), yref), "group %d" % g
+
+
+def test_mx_grouped_exact_integer_case_256x256_tiles():
+    """The same for the MX grouped GEMM: integer codes, UE8M0 scale codes
+    126..128, sampled outputs bit-exact."""
+    offsets = np.concatenate([[0], np.cumsum(GROUP_COUNTS_LARGE)]).astype(np.int32)
+    rows, G, N, K = int(offsets[-1]), GROUP_COUNTS_LARGE.size, 1024, 256
+    rng = np.random.default_rng(13)
+    qa = oracle.e4m3_encode(rng.integers(-8, 9, size=(rows, K)).astype(np.float32))
+    ea = rng.integers(126, 129, size=(rows, K // 32)).astype(np.uint8)
+    qb = oracle.e4m3_encode(rng.integers(-8, 9, size=(G, N, K)).astype(np.float32))
+    eb = rng.integers(126, 129, size=(G, N, K // 32)).astype(np.uint8)
+    c = torch.full((rows, N), float("nan"), dtype=torch.float32, device="cuda")
+    ops.mxfp8_gemm(rows, N, K, G, dev(offsets), None, rows, dev(qa), K, dev(ea), K // 32, dev(qb), K, N * K,
+                   dev(eb), K // 32, N * (K // 32), c, N, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    ch = host(c)
+    for g, (mi, ni) in _group_samples(offsets, N, 14).items():
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        yref, _ = oracle.gemm_mx_sampled(qa[r0:r1], ea[r0:r1], qb[g], eb[g], mi, ni)
+        assert np.array_equal(ch[r0:r1][mi, ni].astype(np.float64), yref), "group %d" % g
 
 
 # ---------------------------------------------------------------------- MX

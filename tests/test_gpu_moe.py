@@ -1,0 +1,249 @@
+"""GPU parity of the full-size MoE chains against the oracle (Qwen3-30B-A3B
+shapes: 16384 tokens, hidden 2048, 128 experts, intermediate 768, top-8).
+
+Block-wise FP8 chain ("Low Precision RL", section "2. Unified block-wise FP8
+(DeepSeek-style)"): X 1x128 -> gather by expert -> grouped gate_up GEMM with
+128x128-block weights -> h = bf16(silu(gate) * up) -> 1x128 requantization
+-> grouped down GEMM.  MXFP8 chain (section "3. Unified MXFP8 (Blackwell)"):
+the same with 1x32 UE8M0 scales on both operands.
+
+Every stage is checked on the device's own inputs to that stage (stage-wise
+parity): quantizer codes and scales bit-exact on sampled rows and experts,
+SiLU within one bf16 ulp, and each GEMM on sampled outputs of sampled groups
+against the fp64 oracle and the datapath truncation model.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_x128_amd import inputs, ops
+from gpu_util import dev, dev_bf16, host, verify
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+HID, INTER, E = 2048, 768, 128
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    _say("generating the MoE layer inputs (seed 3)")
+    d = inputs.qwen3_30b_a3b_moe(3)
+    d["routing_skewed"] = inputs.qwen3_30b_a3b_moe(3, skewed=True, weights=False)["routing"]
+    _say("done")
+    return d
+
+
+def _sample_groups(offsets, seed, n_groups=8):
+    """Sampled non-empty groups (always the first and last non-empty ones and
+    the largest) with sampled local rows and columns of each."""
+    rng = np.random.default_rng(seed)
+    sizes = np.diff(offsets)
+    ne = np.flatnonzero(sizes > 0)
+    pick = set([int(ne[0]), int(ne[-1]), int(ne[np.argmax(sizes[ne])])])
+    pick |= set(int(g) for g in rng.choice(ne, size=min(n_groups, ne.size), replace=False))
+    return sorted(pick)
+
+
+def _sample_rc(n_rows, n_cols, rng):
+    rows = np.unique(np.concatenate([[0, 1], [n_rows - 2, n_rows - 1], rng.integers(0, n_rows, 8)]))
+    rows = rows[(rows >= 0) & (rows < n_rows)]
+    cols = np.unique(np.concatenate([np.arange(0, n_cols, 256), np.arange(255, n_cols, 256),
+                                     rng.integers(0, n_cols, 64)]))
+    mi = np.repeat(rows, cols.size)
+    ni = np.tile(cols, rows.size)
+    return rows, cols, mi, ni
+
+
+def _check_grouped(offsets, groups, seed, c16, c32, operands, mx=False):
+    """Verify sampled outputs of the grouped GEMM.  operands(g, r0, r1) gives
+    the host (qa, sa, qb, sb) of group g's rows [r0, r1)."""
+    rng = np.random.default_rng(seed)
+    for g in groups:
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        N = c32.shape[1]
+        rows, cols, mi, ni = _sample_rc(r1 - r0, N, rng)
+        qa, sa, qb, sb = operands(g, r0, r1)
+        y32 = np.zeros((r1 - r0, N), np.float32)
+        y16 = np.zeros((r1 - r0, N), np.uint16)
+        y32[rows] = host(c32[r0 + torch.from_numpy(rows).cuda()])
+        y16[rows] = host(c16[r0 + torch.from_numpy(rows).cuda()])
+        _say("group %d: %d rows" % (g, r1 - r0))
+        verify(qa, sa, qb, sb, y32, y16, mi=mi, ni=ni, mx=mx)
+
+
+def _check_rows_quant_1x128(x_bits, q, s, rows):
+    qr, sr = oracle.quant_1x128(x_bits[rows])
+    idx = torch.from_numpy(rows).cuda()
+    assert np.array_equal(host(q[idx]), qr)
+    assert np.array_equal(host(s[idx].contiguous()).view(np.uint32), sr.view(np.uint32))
+
+
+def _check_rows_mx(x_bits, q, s, rows):
+    qr, sr = oracle.mx_quant_1x32(x_bits[rows])
+    idx = torch.from_numpy(rows).cuda()
+    assert np.array_equal(host(q[idx]), qr)
+    assert np.array_equal(host(s[idx]), sr)
+
+
+def _check_h(gate_up, h, qh, sh, rows, mx):
+    """SiLU(g) * u within one bf16 ulp of the oracle; the requantization of
+    the device's own h bit-exact."""
+    idx = torch.from_numpy(rows).cuda()
+    gu = host(gate_up[idx])
+    hg = host(h[idx])
+    hr = oracle.silu_mul(gu)
+    diff = np.abs(hg.astype(np.int32) - hr.astype(np.int32))
+    same_sign = (hg & 0x8000) == (hr & 0x8000)
+    ok = (diff <= 1) & same_sign | ((hg & 0x7FFF) == 0) & ((hr & 0x7FFF) <= 1)
+    assert np.all(ok)
+    _say("silu h mismatch rate %.4g" % float(np.mean(diff != 0)))
+    if mx:
+        qr, sr = oracle.mx_quant_1x32(hg)
+        assert np.array_equal(host(qh[idx]), qr)
+        assert np.array_equal(host(sh[idx]), sr)
+    else:
+        qr, sr = oracle.quant_1x128(hg)
+        assert np.array_equal(host(qh[idx]), qr)
+        assert np.array_equal(host(sh[idx].contiguous()).view(np.uint32), sr.view(np.uint32))
+
+
+def _grouped(rows, N, K, G, offs, a_rows, a_count, a, sa, b, sb, out_dtype):
+    c = torch.empty((rows, N), dtype=out_dtype, device="cuda")
+    ops.fp8_grouped_gemm(rows, N, K, G, offs, a_rows, a_count, a, a.stride(0), sa, sa.stride(0), sa.stride(1),
+                         b, b.stride(1), b.stride(0), sb, sb.stride(0), sb.stride(1), sb.stride(2), c, c.stride(0),
+                         ops.OUT_FP32 if out_dtype == torch.float32 else ops.OUT_BF16)
+    return c
+
+
+def _blockwise_weights(d):
+    wgu = dev_bf16(d["w_gu"])
+    qgu, sgu, _ = ops.quant_block2d(wgu)
+    del wgu
+    wd = dev_bf16(d["w_d"])
+    qd, sd, qdt = ops.quant_block2d(wd, transposed=True)
+    del wd
+    torch.cuda.synchronize()
+    for e in (0, 77, E - 1):
+        qr, sr = oracle.quant_128x128(d["w_gu"][e])
+        assert np.array_equal(host(qgu[e]), qr) and np.array_equal(host(sgu[e]), sr), "W_gu expert %d" % e
+        qr, sr = oracle.quant_128x128(d["w_d"][e])
+        assert np.array_equal(host(qd[e]), qr) and np.array_equal(host(sd[e]), sr), "W_d expert %d" % e
+        assert np.array_equal(host(qdt[e]), qr.T), "W_d transposed copy, expert %d" % e
+    # down GEMM operand: B[n = hidden, k = inter] = W_d[e]^T codes, scales read transposed
+    return qgu, sgu, qdt, sd.transpose(1, 2)
+
+
+def _blockwise_chain(d, routing, seed, check_down=True, weights=None):
+    r = routing
+    rows, G = r.row_token.size, r.offsets.size - 1
+    offs = dev(r.offsets)
+    x = dev_bf16(d["x"])
+    qx, sx = ops.quant_rowblock(x, ops.AXIS_ROW, "m_major")
+    torch.cuda.synchronize()
+    _check_rows_quant_1x128(d["x"], qx, sx, np.random.default_rng(seed).integers(0, x.shape[0], 64))
+    qgu, sgu, qdt, sdt = weights
+    a_rows = dev(r.row_token)
+    _say("gate_up: %d rows, G=%d" % (rows, G))
+    gu16 = _grouped(rows, 2 * INTER, HID, G, offs, a_rows, x.shape[0], qx, sx, qgu, sgu, torch.bfloat16)
+    gu32 = _grouped(rows, 2 * INTER, HID, G, offs, a_rows, x.shape[0], qx, sx, qgu, sgu, torch.float32)
+    torch.cuda.synchronize()
+    groups = _sample_groups(r.offsets, seed)
+    qx_h, sx_h = host(qx), host(sx)
+    _check_grouped(r.offsets, groups, seed + 1, gu16, gu32,
+                   lambda g, r0, r1: (qx_h[r.row_token[r0:r1]], sx_h[r.row_token[r0:r1]], host(qgu[g]), host(sgu[g])))
+    del gu32
+    if not check_down:
+        return
+    qh = torch.empty((rows, INTER), dtype=torch.uint8, device="cuda")
+    shb = torch.empty((INTER // 128, rows), dtype=torch.float32, device="cuda")
+    sh = shb.t()
+    h = torch.empty((rows, INTER), dtype=torch.bfloat16, device="cuda")
+    ops.fp8_silu_mul_quant(gu16, rows, INTER, 2 * INTER, 0, qh, INTER, sh, 1, rows, h, INTER)
+    torch.cuda.synchronize()
+    _check_h(gu16, h, qh, sh, np.random.default_rng(seed + 2).integers(0, rows, 256), mx=False)
+    _say("down")
+    dn16 = _grouped(rows, HID, INTER, G, offs, None, rows, qh, sh, qdt, sdt, torch.bfloat16)
+    dn32 = _grouped(rows, HID, INTER, G, offs, None, rows, qh, sh, qdt, sdt, torch.float32)
+    torch.cuda.synchronize()
+    qh_h, sh_h = host(qh), host(sh)
+    _check_grouped(r.offsets, groups, seed + 3, dn16, dn32,
+                   lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g]), host(sdt[g])))
+
+
+@pytest.fixture(scope="module")
+def blockwise_weights(moe):
+    return _blockwise_weights(moe)
+
+
+def test_moe_blockwise_chain_full_size(moe, blockwise_weights):
+    r = moe["routing"]
+    assert r.row_token.size == 16384 * 8
+    _blockwise_chain(moe, r, 30, weights=blockwise_weights)
+
+
+def test_moe_blockwise_chain_skewed_routing(moe, blockwise_weights):
+    """The parity-only skewed routing: 8 empty experts and group sizes from
+    tens to thousands, not multiples of 128."""
+    r = moe["routing_skewed"]
+    sizes = np.diff(r.offsets)
+    assert np.sum(sizes == 0) == 8 and np.any(sizes % 128 != 0)
+    _blockwise_chain(moe, r, 40, check_down=True, weights=blockwise_weights)
+
+
+def test_moe_mxfp8_chain_full_size(moe):
+    d, r = moe, moe["routing"]
+    rows, G = r.row_token.size, r.offsets.size - 1
+    offs = dev(r.offsets)
+    x = dev_bf16(d["x"])
+    qx, sx = ops.mx_quant(x)
+    torch.cuda.synchronize()
+    _check_rows_mx(d["x"], qx, sx, np.random.default_rng(50).integers(0, x.shape[0], 64))
+    wgu = dev_bf16(d["w_gu"])
+    qgu, sgu = ops.mx_quant(wgu.view(E * 2 * INTER, HID))
+    del wgu
+    wdt = dev_bf16(d["w_d"]).transpose(1, 2).contiguous()          # [E, hidden, inter]
+    qdt, sdt = ops.mx_quant(wdt.view(E * HID, INTER))
+    torch.cuda.synchronize()
+    for e in (0, E - 1):
+        _check_rows_mx(d["w_gu"].reshape(E * 2 * INTER, HID), qgu, sgu, np.arange(e * 2 * INTER, (e + 1) * 2 * INTER))
+        _check_rows_mx(np.ascontiguousarray(d["w_d"][e].T), qdt[e * HID:(e + 1) * HID], sdt[e * HID:(e + 1) * HID],
+                       np.arange(HID))
+    del wdt
+
+    def mx_grouped(N, K, a_rows, a_count, a, sa, b, sb, out_dtype):
+        c = torch.empty((rows, N), dtype=out_dtype, device="cuda")
+        ops.mxfp8_gemm(rows, N, K, G, offs, a_rows, a_count, a, K, sa, K // 32, b, K, N * K, sb, K // 32,
+                       N * (K // 32), c, N, ops.OUT_FP32 if out_dtype == torch.float32 else ops.OUT_BF16)
+        return c
+
+    a_rows = dev(r.row_token)
+    gu16 = mx_grouped(2 * INTER, HID, a_rows, x.shape[0], qx, sx, qgu, sgu, torch.bfloat16)
+    gu32 = mx_grouped(2 * INTER, HID, a_rows, x.shape[0], qx, sx, qgu, sgu, torch.float32)
+    torch.cuda.synchronize()
+    groups = _sample_groups(r.offsets, 51)
+    qx_h, sx_h = host(qx), host(sx)
+    n_gu = 2 * INTER
+    _check_grouped(r.offsets, groups, 52, gu16, gu32,
+                   lambda g, r0, r1: (qx_h[r.row_token[r0:r1]], sx_h[r.row_token[r0:r1]],
+                                      host(qgu[g * n_gu:(g + 1) * n_gu]), host(sgu[g * n_gu:(g + 1) * n_gu])),
+                   mx=True)
+    del gu32
+    qh = torch.empty((rows, INTER), dtype=torch.uint8, device="cuda")
+    sh = torch.empty((rows, INTER // 32), dtype=torch.uint8, device="cuda")
+    h = torch.empty((rows, INTER), dtype=torch.bfloat16, device="cuda")
+    ops.fp8_silu_mul_quant(gu16, rows, INTER, 2 * INTER, 1, qh, INTER, sh, INTER // 32, 1, h, INTER)
+    torch.cuda.synchronize()
+    _check_h(gu16, h, qh, sh, np.random.default_rng(53).integers(0, rows, 256), mx=True)
+    dn16 = mx_grouped(HID, INTER, None, rows, qh, sh, qdt, sdt, torch.bfloat16)
+    dn32 = mx_grouped(HID, INTER, None, rows, qh, sh, qdt, sdt, torch.float32)
+    torch.cuda.synchronize()
+    qh_h, sh_h = host(qh), host(sh)
+    _check_grouped(r.offsets, groups, 54, dn16, dn32,
+                   lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g * HID:(g + 1) * HID]),
+                                      host(sdt[g * HID:(g + 1) * HID])),
+                   mx=True)
