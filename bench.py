@@ -1,17 +1,28 @@
 """Benchmark of the block-wise FP8 linear layer on one MI355X.
 
-One step is the Qwen3-4B MLP forward with the block-wise FP8 recipe, every
-part on the GPU through the C ABI:
+Headline step: the Qwen3-4B MLP forward with the block-wise FP8 recipe,
+every part on the GPU through the C ABI:
     quantize X_up [4096 x 2560] per token (1x128), quantize W_up [9728 x 2560]
     in 128x128 blocks, GEMM up (bf16 out), quantize X_down [4096 x 9728],
     quantize W_down [2560 x 9728], GEMM down (bf16 out).
 Inputs are seeded synthetic tensors (see fp8_block_scaled_x128_amd.inputs),
-resident in HBM before timing; the step rotates over several copies so that
-the 256 MB last-level cache cannot serve them.
+resident in HBM before timing; activations rotate over several copies so
+that the 256 MB last-level cache cannot serve them.
 
-Prints ONE JSON line: value = GEMM FLOPs of the step / step time (TFLOP/s),
-with per-kernel times, TFLOP/s or GB/s against MI355X's peaks, a roofline
-object for the dominant kernel (the block-scaled GEMM) and a CPU-oracle
+The other workloads of the path are timed after it (median of --reps
+repetitions, each kernel bracketed by HIP events on the launch stream):
+    tiny_linear      X [256 x 512], W [512 x 512] (quantizers, GEMM bf16/fp32)
+    mlp_backward     dY [4096 x 9728]: 1x128 and 128x1 quantization, X 128x1,
+                     W 128x128 with its transposed code copy, dgrad and wgrad
+                     GEMMs (fp32 out)
+    moe_blockwise    Qwen3-30B-A3B MoE layer (16384 tokens, 128 experts, top 8):
+                     X 1x128, W_gu / W_d 128x128, grouped gate_up GEMM, SiLU*mul
+                     + 1x128 requantization, grouped down GEMM
+    moe_mxfp8        the same layer with 1x32 UE8M0 scales (MXFP8)
+
+Prints ONE JSON line: value = GEMM FLOPs of the headline step / step time
+(TFLOP/s); per-kernel times with TFLOP/s or GB/s against MI355X's peaks; a
+roofline object for the dominant kernel (the block-scaled GEMM); a CPU-oracle
 baseline on a bounded sample.
 """
 from __future__ import annotations
@@ -30,6 +41,8 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5030.0     # 256 CUs x 2.4 GHz x 8192 dense FP8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 M_TOK, HID, INTER = 4096, 2560, 9728
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
+WORKLOADS = ("tiny_linear", "mlp_backward", "moe_blockwise", "moe_mxfp8")
 
 
 def parse():
@@ -37,22 +50,204 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--copies", type=int, default=4, help="input copies rotated across steps")
+    ap.add_argument("--copies", type=int, default=4, help="activation copies rotated across steps")
+    ap.add_argument("--reps", type=int, default=10, help="repetitions per kernel of the other workloads")
+    ap.add_argument("--workloads", default=",".join(WORKLOADS),
+                    help="other workloads to time after the headline step (comma list, or 'none')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=288, help="token rows in the CPU-oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB 3 times (counter calibration)")
     return ap.parse_args()
 
 
-def quant_bytes_1x128(rows, cols):
-    return rows * cols * 3 + rows * ((cols + 127) // 128) * 4
+def qbytes_row(rows, cols, group=128, scale_bytes=4):
+    """Quantizer algorithmic bytes: bf16 in, one code byte out, one scale per group."""
+    return rows * cols * 3 + rows * ((cols + group - 1) // group) * scale_bytes
 
 
-def quant_bytes_128x128(rows, cols):
-    return rows * cols * 3 + ((rows + 127) // 128) * ((cols + 127) // 128) * 4
+def qbytes_block2d(batch, rows, cols, transposed=False):
+    return batch * (rows * cols * (4 if transposed else 3) + ((rows + 127) // 128) * ((cols + 127) // 128) * 4)
 
 
+def rate(unit, amount, ms):
+    if unit == "TFLOP/s":
+        r = amount / (ms * 1e-3) / 1e12
+        return r, r / PEAK_FP8_TFLOPS
+    r = amount / (ms * 1e-3) / 1e9
+    return r, r / PEAK_HBM_GBS
+
+
+def kernel_entry(unit, amount, ms):
+    r, f = rate(unit, amount, ms)
+    return {"ms": round(ms, 5), unit: round(r, 2), "frac_of_peak": round(f, 4)}
+
+
+def time_sequence(torch, stream, launches, reps, warmup):
+    """Run the list of launches `warmup` + `reps` times, each launch bracketed
+    by events; returns the per-launch median ms."""
+    for i in range(warmup):
+        for fn in launches:
+            fn(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        for k, fn in enumerate(launches):
+            ev[i][k].record(stream)
+            fn(i)
+        ev[i][len(launches)].record(stream)
+    torch.cuda.synchronize()
+    return [float(np.median([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(reps)])) for k in range(len(launches))]
+
+
+# ------------------------------------------------------------- workloads
+def wl_tiny_linear(torch, ops, inputs, to_dev, R):
+    d = inputs.tiny_linear(0)
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    xs = [to_dev(d["x"]) for _ in range(R)]
+    w = to_dev(d["w"])
+    qx = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sx = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+    qw = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    gemm = lambda c, out: ops.fp8_blockscaled_gemm(M, N, K, qx, K, sx, 1, M, qw, K, sw, K // 128, 1,
+                                                   ops.BSCALE_BLOCK128, c, N, out)
+    return [
+        ("quant_x_1x128", lambda i: ops.fp8_quant_rowblock(xs[i % R], M, K, K, ops.AXIS_ROW, qx, K, sx, 1, M),
+         ("GB/s", qbytes_row(M, K))),
+        ("quant_w_128x128", lambda i: ops.fp8_quant_block2d(w, 1, N, K, K, qw, K, None, 0, sw),
+         ("GB/s", qbytes_block2d(1, N, K))),
+        ("gemm_bf16", lambda i: gemm(y16, ops.OUT_BF16), ("TFLOP/s", 2.0 * M * N * K)),
+        ("gemm_fp32", lambda i: gemm(y32, ops.OUT_FP32), ("TFLOP/s", 2.0 * M * N * K)),
+    ], {"workload": "tiny_linear", "tokens": M, "in": K, "out": N, "seed": 0}
+
+
+def wl_mlp_backward(torch, ops, inputs, to_dev, R):
+    d = inputs.qwen3_4b_mlp_backward(2)
+    T, O = d["dy"].shape
+    I = d["x"].shape[1]
+    dys = [to_dev(d["dy"]) for _ in range(R)]
+    xs = [to_dev(d["x"]) for _ in range(R)]
+    w = to_dev(d["w"])
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+    qdy, sdy = u8(T, O), f32(O // 128, T)                  # 1x128, M-major scales
+    qdyt, sdyt = u8(O, T), f32(T // 128, O)                # 128x1 along tokens, transposed codes
+    qxt, sxt = u8(I, T), f32(T // 128, I)
+    qw, qwt, sw = u8(O, I), u8(I, O), f32(O // 128, I // 128)
+    dx = torch.empty((T, I), dtype=torch.float32, device="cuda")
+    dw = torch.empty((O, I), dtype=torch.float32, device="cuda")
+    return [
+        ("quant_dy_1x128", lambda i: ops.fp8_quant_rowblock(dys[i % R], T, O, O, ops.AXIS_ROW, qdy, O, sdy, 1, T),
+         ("GB/s", qbytes_row(T, O))),
+        ("quant_dy_128x1", lambda i: ops.fp8_quant_rowblock(dys[i % R], T, O, O, ops.AXIS_COL, qdyt, T, sdyt, 1, O),
+         ("GB/s", qbytes_row(O, T))),
+        ("quant_x_128x1", lambda i: ops.fp8_quant_rowblock(xs[i % R], T, I, I, ops.AXIS_COL, qxt, T, sxt, 1, I),
+         ("GB/s", qbytes_row(I, T))),
+        ("quant_w_128x128_with_transpose", lambda i: ops.fp8_quant_block2d(w, 1, O, I, I, qw, I, qwt, O, sw),
+         ("GB/s", qbytes_block2d(1, O, I, transposed=True))),
+        # dX [T, I] = dY [T, O] W [O, I]: B = W^T codes [I, O], scales sw read transposed
+        ("gemm_dgrad_fp32", lambda i: ops.fp8_blockscaled_gemm(T, I, O, qdy, O, sdy, 1, T, qwt, O, sw, 1, I // 128,
+                                                              ops.BSCALE_BLOCK128, dx, I, ops.OUT_FP32),
+         ("TFLOP/s", 2.0 * T * I * O)),
+        # dW [O, I] = dY^T [O, T] X [T, I]: both 128x1 along tokens, per-row B scales
+        ("gemm_wgrad_fp32", lambda i: ops.fp8_blockscaled_gemm(O, I, T, qdyt, T, sdyt, 1, O, qxt, T, sxt, 1, I,
+                                                              ops.BSCALE_ROW128, dw, I, ops.OUT_FP32),
+         ("TFLOP/s", 2.0 * O * I * T)),
+    ], {"workload": "mlp_backward", "tokens": T, "hidden": I, "intermediate": O, "seeds": [1, 2]}
+
+
+def _moe_inputs(inputs, cache={}):
+    if "d" not in cache:
+        cache["d"] = inputs.qwen3_30b_a3b_moe(3)
+    return cache["d"]
+
+
+def wl_moe_blockwise(torch, ops, inputs, to_dev, R):
+    d = _moe_inputs(inputs)
+    r = d["routing"]
+    T, H = d["x"].shape
+    E, N2, _ = d["w_gu"].shape
+    I = N2 // 2
+    rows, G = r.row_token.size, r.offsets.size - 1
+    xs = [to_dev(d["x"]) for _ in range(R)]
+    wgu, wd = to_dev(d["w_gu"]), to_dev(d["w_d"])
+    offs = torch.from_numpy(r.offsets).cuda()
+    a_rows = torch.from_numpy(r.row_token).cuda()
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+    qx, sx = u8(T, H), f32(H // 128, T)
+    qgu, sgu = u8(E, N2, H), f32(E, N2 // 128, H // 128)
+    qd, qdt, sd = u8(E, I, H), u8(E, H, I), f32(E, I // 128, H // 128)
+    gu = torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
+    qh, sh = u8(rows, I), f32(I // 128, rows)
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    n_gu = 2.0 * rows * N2 * H
+    n_dn = 2.0 * rows * H * I
+    return [
+        ("quant_x_1x128", lambda i: ops.fp8_quant_rowblock(xs[i % R], T, H, H, ops.AXIS_ROW, qx, H, sx, 1, T),
+         ("GB/s", qbytes_row(T, H))),
+        ("quant_w_gate_up_128x128", lambda i: ops.fp8_quant_block2d(wgu, E, N2, H, H, qgu, H, None, 0, sgu),
+         ("GB/s", qbytes_block2d(E, N2, H))),
+        ("quant_w_down_128x128_with_transpose", lambda i: ops.fp8_quant_block2d(wd, E, I, H, H, qd, H, qdt, I, sd),
+         ("GB/s", qbytes_block2d(E, I, H, transposed=True))),
+        ("grouped_gemm_gate_up", lambda i: ops.fp8_grouped_gemm(
+            rows, N2, H, G, offs, a_rows, T, qx, H, sx, 1, T, qgu, H, N2 * H, sgu, (N2 // 128) * (H // 128),
+            H // 128, 1, gu, N2, ops.OUT_BF16), ("TFLOP/s", n_gu)),
+        ("silu_mul_quant_1x128", lambda i: ops.fp8_silu_mul_quant(gu, rows, I, N2, 0, qh, I, sh, 1, rows, None, 0),
+         ("GB/s", rows * N2 * 2 + rows * I + rows * (I // 128) * 4)),
+        # B[n = hidden, k = inter] = W_d[e]^T codes; scales sd[e][k/128][n/128] read transposed
+        ("grouped_gemm_down", lambda i: ops.fp8_grouped_gemm(
+            rows, H, I, G, offs, None, rows, qh, I, sh, 1, rows, qdt, I, H * I, sd, (I // 128) * (H // 128),
+            1, H // 128, y, H, ops.OUT_BF16), ("TFLOP/s", n_dn)),
+    ], {"workload": "moe_blockwise", "tokens": T, "hidden": H, "experts": E, "intermediate": I, "top_k": 8,
+        "grouped_rows": rows, "seed": 3}
+
+
+def wl_moe_mxfp8(torch, ops, inputs, to_dev, R):
+    d = _moe_inputs(inputs)
+    r = d["routing"]
+    T, H = d["x"].shape
+    E, N2, _ = d["w_gu"].shape
+    I = N2 // 2
+    rows, G = r.row_token.size, r.offsets.size - 1
+    xs = [to_dev(d["x"]) for _ in range(R)]
+    wgu = to_dev(d["w_gu"]).view(E * N2, H)
+    wdt = to_dev(d["w_d"]).transpose(1, 2).contiguous().view(E * H, I)   # contraction axis (inter) contiguous
+    offs = torch.from_numpy(r.offsets).cuda()
+    a_rows = torch.from_numpy(r.row_token).cuda()
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    qx, sx = u8(T, H), u8(T, H // 32)
+    qgu, sgu = u8(E * N2, H), u8(E * N2, H // 32)
+    qdt, sdt = u8(E * H, I), u8(E * H, I // 32)
+    gu = torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
+    qh, sh = u8(rows, I), u8(rows, I // 32)
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    return [
+        ("mx_quant_x", lambda i: ops.mxfp8_quant(xs[i % R], T, H, H, qx, H, sx, H // 32, 1),
+         ("GB/s", qbytes_row(T, H, 32, 1))),
+        ("mx_quant_w_gate_up", lambda i: ops.mxfp8_quant(wgu, E * N2, H, H, qgu, H, sgu, H // 32, 1),
+         ("GB/s", qbytes_row(E * N2, H, 32, 1))),
+        ("mx_quant_w_down_t", lambda i: ops.mxfp8_quant(wdt, E * H, I, I, qdt, I, sdt, I // 32, 1),
+         ("GB/s", qbytes_row(E * H, I, 32, 1))),
+        ("mx_grouped_gemm_gate_up", lambda i: ops.mxfp8_gemm(
+            rows, N2, H, G, offs, a_rows, T, qx, H, sx, H // 32, qgu, H, N2 * H, sgu, H // 32, N2 * (H // 32),
+            gu, N2, ops.OUT_BF16), ("TFLOP/s", 2.0 * rows * N2 * H)),
+        ("silu_mul_quant_mx", lambda i: ops.fp8_silu_mul_quant(gu, rows, I, N2, 1, qh, I, sh, I // 32, 1, None, 0),
+         ("GB/s", rows * N2 * 2 + rows * I + rows * (I // 32))),
+        ("mx_grouped_gemm_down", lambda i: ops.mxfp8_gemm(
+            rows, H, I, G, offs, None, rows, qh, I, sh, I // 32, qdt, I, H * I, sdt, I // 32, H * (I // 32),
+            y, H, ops.OUT_BF16), ("TFLOP/s", 2.0 * rows * H * I)),
+    ], {"workload": "moe_mxfp8", "tokens": T, "hidden": H, "experts": E, "intermediate": I, "top_k": 8,
+        "grouped_rows": rows, "seed": 3}
+
+
+# ---------------------------------------------------------- CPU baseline
 def cpu_baseline(d, rows):
-    """Time the CPU oracle on a bounded sample of the same step: the first
+    """Time the CPU oracle on a bounded sample of the headline step: the first
     `rows` tokens of both activations (1x128), both full weights (128x128) and
     both GEMMs for those tokens.  Reported in the metric's unit (TFLOP/s of
     GEMM work per second of oracle time)."""
@@ -76,6 +271,20 @@ def cpu_baseline(d, rows):
                       % (rows, dt)}
 
 
+def traffic_record():
+    """HBM bytes per GEMM launch from the committed counter runs, or None if
+    the GEMM sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    from fp8_block_scaled_x128_amd.profiling import gemm_sources_hash
+    if rec.get("gemm_sources_sha256") != gemm_sources_hash():
+        return None
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -88,16 +297,16 @@ def main():
     ops.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
     d = inputs.qwen3_4b_mlp(1)
 
     def to_dev(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     R = max(1, args.copies)
     xs_up = [to_dev(d["x_up"]) for _ in range(R)]
-    ws_up = [to_dev(d["w_up"]) for _ in range(R)]
     xs_dn = [to_dev(d["x_down"]) for _ in range(R)]
-    ws_dn = [to_dev(d["w_down"]) for _ in range(R)]
+    w_up, w_dn = to_dev(d["w_up"]), to_dev(d["w_down"])
 
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
     f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
@@ -111,23 +320,22 @@ def main():
     names = ["quant_x_up", "quant_w_up", "gemm_up", "quant_x_down", "quant_w_down", "gemm_down"]
     launches = [
         lambda i: ops.fp8_quant_rowblock(xs_up[i], M_TOK, HID, HID, ops.AXIS_ROW, qx_up, HID, sx_up, 1, M_TOK),
-        lambda i: ops.fp8_quant_block2d(ws_up[i], 1, INTER, HID, HID, qw_up, HID, None, 0, sw_up),
+        lambda i: ops.fp8_quant_block2d(w_up, 1, INTER, HID, HID, qw_up, HID, None, 0, sw_up),
         lambda i: ops.fp8_blockscaled_gemm(M_TOK, INTER, HID, qx_up, HID, sx_up, 1, M_TOK, qw_up, HID, sw_up,
                                            HID // 128, 1, ops.BSCALE_BLOCK128, y_up, INTER, ops.OUT_BF16),
         lambda i: ops.fp8_quant_rowblock(xs_dn[i], M_TOK, INTER, INTER, ops.AXIS_ROW, qx_dn, INTER, sx_dn, 1, M_TOK),
-        lambda i: ops.fp8_quant_block2d(ws_dn[i], 1, HID, INTER, INTER, qw_dn, INTER, None, 0, sw_dn),
+        lambda i: ops.fp8_quant_block2d(w_dn, 1, HID, INTER, INTER, qw_dn, INTER, None, 0, sw_dn),
         lambda i: ops.fp8_blockscaled_gemm(M_TOK, HID, INTER, qx_dn, INTER, sx_dn, 1, M_TOK, qw_dn, INTER, sw_dn,
                                            INTER // 128, 1, ops.BSCALE_BLOCK128, y_dn, HID, ops.OUT_BF16),
     ]
     gemm_flops = 2.0 * M_TOK * INTER * HID
-    work = {"quant_x_up": ("GB/s", quant_bytes_1x128(M_TOK, HID)),
-            "quant_w_up": ("GB/s", quant_bytes_128x128(INTER, HID)),
+    work = {"quant_x_up": ("GB/s", qbytes_row(M_TOK, HID)),
+            "quant_w_up": ("GB/s", qbytes_block2d(1, INTER, HID)),
             "gemm_up": ("TFLOP/s", gemm_flops),
-            "quant_x_down": ("GB/s", quant_bytes_1x128(M_TOK, INTER)),
-            "quant_w_down": ("GB/s", quant_bytes_128x128(HID, INTER)),
+            "quant_x_down": ("GB/s", qbytes_row(M_TOK, INTER)),
+            "quant_w_down": ("GB/s", qbytes_block2d(1, HID, INTER)),
             "gemm_down": ("TFLOP/s", gemm_flops)}
 
-    stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
 
     def step(i, events=None):
@@ -154,19 +362,13 @@ def main():
     kernels = {}
     for k, n in enumerate(names):
         ms = float(np.mean([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)]))
-        unit, amount = work[n]
-        if unit == "TFLOP/s":
-            rate = amount / (ms * 1e-3) / 1e12
-            frac = rate / PEAK_FP8_TFLOPS
-        else:
-            rate = amount / (ms * 1e-3) / 1e9
-            frac = rate / PEAK_HBM_GBS
-        kernels[n] = {"ms": round(ms, 5), unit: round(rate, 2), "frac_of_peak": round(frac, 4)}
+        kernels[n] = kernel_entry(*work[n], ms)
 
     gemm_ms = (kernels["gemm_up"]["ms"] + kernels["gemm_down"]["ms"]) / 2
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     value = 2 * gemm_flops / (ms_step * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(dev)
+    trec = traffic_record()
     res = {
         "metric": "block-scaled FP8 GEMM TFLOPS + quant GB/s, % of MI355X FP8/HBM peak",
         "value": round(value, 2),
@@ -184,13 +386,47 @@ def main():
                    "intermediate": INTER, "act_groups": "1x128", "weight_blocks": "128x128",
                    "scales": "fp32", "out": "bf16", "seed": 1, "input_copies": R},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
-                     "kernel": "fp8bs k_gemm (block-scaled FP8 GEMM)",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": (round(trec["hbm_bytes_per_launch"]) if trec else None),
+                     "kernel": "k_gemm, block-scaled FP8 GEMM (gemm_up and gemm_down of the step)",
                      "per_launch": "2*M*N*K = %.4g FLOP" % gemm_flops},
         "kernels": kernels,
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
+    if trec:
+        res["roofline"]["traffic_detail"] = {k: trec[k] for k in ("fetch_bytes_per_launch", "write_bytes_per_launch",
+                                                                  "algorithmic_min_bytes_per_launch", "source")}
+    del xs_up, xs_dn
+
+    # ------------------------------------------------- the other workloads
+    wanted = [w for w in args.workloads.split(",") if w and w != "none"]
+    table = {"tiny_linear": wl_tiny_linear, "mlp_backward": wl_mlp_backward,
+             "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8}
+    others = {}
+    for wname in wanted:
+        if wname not in table:
+            print("unknown workload %s" % wname, file=sys.stderr)
+            sys.exit(2)
+        print("timing %s" % wname, file=sys.stderr, flush=True)
+        seq, cfg = table[wname](torch, ops, inputs, to_dev, R)
+        ms = time_sequence(torch, stream, [fn for _, fn, _ in seq], args.reps, 3)
+        ks = {n: kernel_entry(*wk, t) for (n, _, wk), t in zip(seq, ms)}
+        others[wname] = {"config": cfg, "ms_per_pass": round(float(sum(ms)), 5), "kernels": ks}
+        del seq
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if others:
+        res["workloads"] = others
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_probe"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, args.cpu_rows)
     print(json.dumps(res), flush=True)

@@ -12,19 +12,18 @@
 // section "3. Unified MXFP8 (Blackwell)") hands its power-of-two block scales
 // to the scaled matrix instruction, which applies them exactly.
 //
-// Kernel structure: one workgroup of 4 waves (one per SIMD, so each wave has
-// the full 512-entry VGPR+AGPR budget) per output tile of 256 weight rows (n)
-// x 128 activation rows (m).
-//  - K advances in 128-byte slices.  Each slice of the weight tile (32 KB),
-//    the activation tile (16 KB) and the slice's scales is copied straight
-//    from global memory into LDS with global_load_lds (no register staging),
-//    three stages deep, so two slices are in flight while one is consumed.
+// Kernel structure: one workgroup per output tile of 256 weight rows (n) x
+// 128 (4 waves, one per SIMD) or 256 (8 waves, two per SIMD) activation rows.
+//  - K advances in 128-byte slices.  The slice of the weight tile (32 KB), of
+//    the activation tile (16 or 32 KB) and the slice's scales are copied
+//    straight from global memory into LDS with global_load_lds (no register
+//    staging), through the multi-buffer pipeline described at Cfg.
 //  - LDS rows are 128 bytes; 16-byte chunk c of row r sits in slot
 //    c ^ (r & 7), which makes the fragment reads free of bank conflicts
 //    (measured with the LDS bank-conflict counter; the variant
 //    (r & 7) ^ ((r >> 3) & 1) costs 4 conflict cycles per read).  The copy
 //    realizes the swizzle by choosing which global chunk each lane fetches.
-//  - Wave w owns n rows [128 * (w >> 1), +128) and m rows [64 * (w & 1), +64):
+//  - Wave w owns n rows [128 * (w & 1), +128) and m rows [64 * (w >> 1), +64):
 //    8 x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4 per slice.  Weight rows
 //    are the instruction's A operand and activation rows its B operand, so a
 //    lane's 4 outputs share one activation row m and four consecutive n.
