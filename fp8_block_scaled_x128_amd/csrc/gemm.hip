@@ -495,24 +495,27 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
     for (; kb < nk; ++kb) step(kb, std::false_type{}, std::false_type{});
 
     // ---------------------------------------------------------- epilogue
+    // N % 128 == 0 and each wave covers 128 aligned n, so a wave's columns are
+    // all inside the matrix or all outside; rows are checked per lane.  One
+    // base address per m-tile, the n-tiles at constant offsets from it.
     const int nw0 = n0 + wn * 128;
+    if (nw0 >= p.N) return;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int m = m_begin + wm * 64 + mt * 16 + r16;
         if (m >= m_end) continue;
+        if (OUTF32) {
+            float* dst = static_cast<float*>(p.c) + (int64_t)m * p.ldc + nw0 + 4 * q;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const int n = nw0 + nt * 16 + 4 * q;
-            if (n >= p.N) continue;
-            if (OUTF32) {
-                float* dst = static_cast<float*>(p.c) + (int64_t)m * p.ldc + n;
-                *reinterpret_cast<float4*>(dst) = make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
-            } else {
-                uint16_t* dst = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + n;
-                const uint32_t lo = pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]);
-                const uint32_t hi = pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]);
-                *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-            }
+            for (int nt = 0; nt < 8; ++nt)
+                *reinterpret_cast<float4*>(dst + nt * 16) =
+                    make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
+        } else {
+            uint16_t* dst = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + nw0 + 4 * q;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                *reinterpret_cast<uint2*>(dst + nt * 16) = make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
+                                                                      pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
         }
     }
 }
