@@ -52,9 +52,31 @@ __device__ __forceinline__ float absmax8(const float v[8]) {
 }
 
 // silu(g) * u rounded to bf16 and widened back (the value the next GEMM consumes).
+// silu(g) = g * sigmoid(g), with sigmoid(g) = 1 / (1 + t) for g >= 0 and
+// t / (1 + t) for g < 0, t = exp(-|g|) in (0, 1]: no overflow, and 1 + t in
+// [1, 2] for the hardware reciprocal.  t = 2^a with a = -|g| log2(e) split
+// into a rounded part for the hardware exp2 and its exact residual applied to
+// first order, so t is good to about one fp32 ulp.  Where t would be an fp32
+// denormal (a < -64, that is |g| above about 44.4) it is formed scaled by 2^64
+// and the scale is removed from the final product.  The accurate expf and IEEE
+// division cost about 25 more instructions per element, enough to make this
+// kernel VALU bound.  The product is rounded once to bf16: the result stays
+// within one bf16 ulp of the exactly rounded value, and differs from it only
+// where the exact value lies a few fp32 ulp from a bf16 rounding midpoint.
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
-    float sg = g / (1.0f + expf(-g));
-    return f32_to_bf16_rne(sg * u);
+    constexpr float kLog2e = 1.4426950216293335f;       // log2(e) rounded to fp32
+    constexpr float kLog2eLo = 1.925963033500011e-08f;  // log2(e) - kLog2e
+    constexpr float kLn2 = 0.6931471824645996f;
+    const float ng = -fabsf(g);
+    const float a_hi = ng * kLog2e;
+    const float a_lo = __builtin_fmaf(ng, kLog2e, -a_hi) + ng * kLog2eLo;
+    const bool tiny = a_hi < -64.0f;
+    const float t = __builtin_amdgcn_exp2f(tiny ? a_hi + 64.0f : a_hi) * __builtin_fmaf(a_lo, kLn2, 1.0f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + (tiny ? 0.0f : t));
+    const float sig = g >= 0.0f ? r : t * r;
+    float h = (g * sig) * u;
+    if (tiny && g < 0.0f) h *= 0x1p-64f;
+    return f32_to_bf16_rne(h);
 }
 
 // ---------------------------------------------------------------------------
@@ -96,8 +118,8 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
             raw_u[u] = make_uint4(0, 0, 0, 0);
             if (run < p.total_runs && c < p.cols) {
                 const uint16_t* src = p.x + (int64_t)r * p.ld_x + c;
-                raw[u] = *reinterpret_cast<const uint4*>(src);
-                if (SILU) raw_u[u] = *reinterpret_cast<const uint4*>(src + p.up_off);
+                raw[u] = load_nt16(src);
+                if (SILU) raw_u[u] = load_nt16(src + p.up_off);
             }
         }
 #pragma unroll
@@ -120,7 +142,7 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
                 if (p.h != nullptr && valid) {
                     uint4 hw = make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
                                           hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16));
-                    *reinterpret_cast<uint4*>(p.h + (int64_t)r * p.ld_h + c) = hw;
+                    store_nt16(p.h + (int64_t)r * p.ld_h + c, hw);
                 }
             }
             uint32_t w0, w1;
@@ -144,7 +166,7 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
                     static_cast<uint8_t*>(p.s)[(int64_t)r * p.ssr + (int64_t)(g * 4 + (sub >> 2)) * p.ssg] =
                         (uint8_t)(e + 127);
             }
-            if (valid) *reinterpret_cast<uint2*>(p.q + (int64_t)r * p.ld_q + c) = make_uint2(w0, w1);
+            if (valid) store_nt8(p.q + (int64_t)r * p.ld_q + c, w0, w1);
         }
     }
 }
@@ -281,7 +303,7 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
         encode8(v, sc, w0, w1);
         const int rl = (t >> 4) + 16 * i;
         const int32_t r = r0 + rl, c = c0 + cc * 8;
-        if (r < rows && c < cols) *reinterpret_cast<uint2*>(q + (int64_t)r * ld_q + c) = make_uint2(w0, w1);
+        if (r < rows && c < cols) store_nt8(q + (int64_t)r * ld_q + c, w0, w1);
         if (TRANS) { ctile[rl][2 * cc] = w0; ctile[rl][2 * cc + 1] = w1; }
     }
     if (t == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = sc;

@@ -184,8 +184,8 @@ fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t 
  * Requirements: I % 128 == 0 (I % 32 == 0 when mx == 1); ld_in >= 2 I,
  * ld_in % 8 == 0, gate_up 16-byte aligned; ld_q >= I, ld_q % 8 == 0;
  * ld_h >= I if h_out.
- * exp() is the device's expf; h agrees with an exactly rounded fp64
- * evaluation to within one bf16 ulp.
+ * silu is evaluated with the hardware exp2 and reciprocal (a few fp32 ulp);
+ * h agrees with an exactly rounded fp64 evaluation to within one bf16 ulp.
  * ------------------------------------------------------------------------ */
 fp8bs_status fp8_silu_mul_quant(const uint16_t* gate_up, int64_t rows, int64_t I, int64_t ld_in, int mx,
                                 uint8_t* q, int64_t ld_q, void* s, int64_t s_stride_row, int64_t s_stride_group,

@@ -198,6 +198,48 @@ def test_mx_moe_activation_full():
     assert np.array_equal(host(s), sr)
 
 
+def test_silu_mul_every_bf16_gate_value():
+    """h = bf16(silu(g) * u) for every finite bf16 g with |g| <= 120 and a few
+    u: within one bf16 ulp of the exactly rounded value, and off it only where
+    the exact product lies within the fp32 evaluation error of a bf16 rounding
+    midpoint (bf16 inputs make exact midpoints common: for |g| below 2^-24,
+    sigmoid(g) is 0.5 in fp32 and g * u / 2 may be a midpoint that only the
+    dropped g^2 term moves off)."""
+    g = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    gv = (g.astype(np.uint32) << 16).view(np.float32)
+    g = g[np.isfinite(gv) & (np.abs(gv) <= 120.0)]
+    us = np.array([1.0, -3.5, 0.0078125, 1000.0, -2.0 ** -20], np.float32)
+    I = 128
+    n = g.size * us.size
+    rows = (n + I - 1) // I
+    gate = np.zeros(rows * I, np.uint16)
+    up = np.zeros(rows * I, np.uint16)
+    gate[:n] = np.tile(g, us.size)
+    up[:n] = np.repeat(oracle.f64_to_bf16(us.astype(np.float64)), g.size)
+    gu = np.concatenate([gate.reshape(rows, I), up.reshape(rows, I)], axis=1)
+    q = torch.empty((rows, I), dtype=torch.uint8, device="cuda")
+    s_ = torch.empty((rows, 1), dtype=torch.float32, device="cuda")
+    h = torch.empty((rows, I), dtype=torch.bfloat16, device="cuda")
+    ops.fp8_silu_mul_quant(dev_bf16(gu), rows, I, 2 * I, 0, q, I, s_, 1, 1, h, I)
+    torch.cuda.synchronize()
+    hg = host(h).reshape(-1)[:n]
+    hr = oracle.silu_mul(gu).reshape(-1)[:n]
+    diff = np.abs(hg.astype(np.int32) - hr.astype(np.int32))
+    same_sign = (hg & 0x8000) == (hr & 0x8000)
+    ok = (diff <= 1) & same_sign | ((hg & 0x7FFF) == 0) & ((hr & 0x7FFF) <= 1)
+    assert np.all(ok), "h differs by more than one bf16 ulp at %s" % np.flatnonzero(~ok)[:5]
+    bad = np.flatnonzero(diff != 0)
+    _say("silu h, %d gate values x %d up values: mismatch rate %.3g" % (g.size, us.size, bad.size / n))
+    # every mismatch sits at a near-midpoint: |exact - midpoint| within 2^-20 relative
+    # (the fp32 evaluation: exp2 and reciprocal of about 1 ulp each, three products)
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    gb, ub = f(gate[:n][bad]), f(up[:n][bad])
+    exact = gb / (1.0 + np.exp(-gb)) * ub
+    mid = 0.5 * (f(hg[bad]) + f(hr[bad]))
+    far = np.abs(exact - mid) > 2.0 ** -20 * np.abs(exact) + 2.0 ** -149
+    assert not far.any(), "mismatch away from a rounding midpoint at g=%s u=%s" % (gb[far][:5], ub[far][:5])
+
+
 # ------------------------------------------------------------ SiLU * up
 @pytest.mark.parametrize("mx", [0, 1])
 def test_silu_mul_quant(mx):
