@@ -180,6 +180,14 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t
     return launched(launch_gemm_blockscaled(g, stream), "fp8_blockscaled_gemm");
 }
 
+fp8bs_status fp8_blockscaled_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t* plan) {
+    if (!plan) return fail(FP8BS_ERR_NULL, "plan is required");
+    if (M < 0 || N < 0 || K < 0 || K % 128 || N % 128) return fail(FP8BS_ERR_SHAPE, "M %lld N %lld K %lld",
+                                                                   (long long)M, (long long)N, (long long)K);
+    plan_gemm_blockscaled(M, N, K, plan);
+    return ok();
+}
+
 fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t G, const int32_t* offsets,
                               const int32_t* a_rows, int64_t a_count, const uint8_t* a, int64_t lda, const float* sa,
                               int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b, int64_t ldb,

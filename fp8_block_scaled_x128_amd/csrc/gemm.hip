@@ -44,25 +44,32 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 256, BK = 128;              // weight rows per tile, K bytes per slice
+constexpr int BK = 128;                         // K bytes per slice
 constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
 
-// Tile configurations.  Every wave computes 128 weight rows x 64 activation
-// rows; waves are arranged 2 (n) x WAVES/2 (m).
-//   WAVES = 4: 256 x 128 tile, one wave per SIMD (512 registers each),
-//              promotion deferred by one n-tile within the wave.
-//   WAVES = 8: 256 x 256 tile, two waves per SIMD (256 registers each) whose
-//              matrix and vector work interleave.
+// Tile configurations.  Every wave computes NF 16-row weight tiles (16 NF
+// weight rows) x 64 activation rows; waves are arranged 2 (n) x WAVES/2 (m),
+// so a tile is 32 NF weight rows x 32 WAVES activation rows.
+//   WAVES = 4: one wave per SIMD (512 registers each), promotion deferred by
+//              one n-tile within the wave.
+//   WAVES = 8: two waves per SIMD (256 registers each) whose matrix and
+//              vector work interleave.
+//   NF = 8 (256 weight rows) is the general tile; NF = 5 and 6 (160 and 192
+//   rows) exist so that problems whose 256-row tiles leave a round of the 256
+//   compute units mostly idle can be tiled into whole rounds.
 // LDS pipeline.  The weight tile of a slice is read during the whole slice,
 // the activation tile only at its start (each wave keeps its 4 activation
 // fragments in registers).  Weight slices get kBStages buffers; activation
-// slices kAStages, and with kABarrier a second barrier right after the
-// fragment reads lets the current activation buffer be refilled at once.
-// A slice's copies are issued kLeadA / kLeadB steps before it is consumed.
-template <int WAVES>
+// slices two where they fit in LDS, else one with kABarrier: a second barrier
+// right after the fragment reads lets the current activation buffer be
+// refilled at once.  A slice's copies are issued kLeadA / kLeadB steps before
+// it is consumed.
+template <int WAVES, int NF>
 struct Cfg {
     static constexpr int kWaves = WAVES;
+    static constexpr int kNF = NF;
     static constexpr int kThreads = WAVES * 64;
+    static constexpr int BN = 32 * NF;
     static constexpr int BM = 64 * (WAVES / 2);
     static constexpr bool kDefer = true;
     // Measured on the MLP shapes (M 4096; N 9728, K 2560 and N 2560, K 9728):
@@ -71,12 +78,16 @@ struct Cfg {
     // the second); 256x128 tile: 3 + 2 without the second barrier is 2-3%
     // faster than with it.
     static constexpr int kBStages = 3;
-    static constexpr int kAStages = WAVES == 4 ? 2 : 1;
-    static constexpr bool kABarrier = WAVES == 8;
     static constexpr int kBStageBytes = BN * BK + BN * 4;   // weight tile + weight scales
     static constexpr int kABufBytes = BM * BK + BM * 4;     // activation tile + activation scales
+    static constexpr int kAStages = kBStages * kBStageBytes + 2 * kABufBytes <= 160 * 1024 ? 2 : 1;
+    static constexpr bool kABarrier = kAStages == 1;
     static constexpr int kLdsBytes = kBStages * kBStageBytes + kAStages * kABufBytes;
-    static constexpr int kDmaB = BN / 8 / WAVES;            // 16-byte copies per wave per slice
+    // 16-byte copies per wave per slice: a wave copy moves 8 rows.  When the
+    // 4 NF weight-row copies do not divide among the waves, the surplus copy
+    // slots repeat copies of wave 0 (same bytes to the same LDS location).
+    static constexpr int kCopiesB = BN / 8;
+    static constexpr int kDmaB = (kCopiesB + WAVES - 1) / WAVES;
     static constexpr int kDmaA = BM / 8 / WAVES;
     static constexpr int kLeadA = kABarrier ? kAStages : kAStages - 1;
     static constexpr int kLeadB = kBStages - 1;
@@ -90,11 +101,13 @@ struct Cfg {
     // for leads of 1 or 2 (a step short of copies is then the last one).
     static_assert(kLeadA >= 1 && kLeadB >= 1 && kLeadMax <= 2, "pipeline leads must be 1 or 2");
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    static_assert(kDmaA <= NF, "one activation copy per n-tile step");
     // tile copy slots: activation copy t in n-tile step t; weight copies
     // after the activation copies when they must follow them, else in step t
     // (lead 1: as early as possible) or spread over the slice (lead 2)
     static constexpr int kBFirst = kLeadA < kLeadB ? kDmaA : 0;
-    static constexpr int b_slot(int t) { return kLeadB == 1 ? t : kBFirst + t * (8 - kBFirst) / kDmaB; }
+    static constexpr int b_slot(int t) { return kLeadB == 1 ? t : kBFirst + t * (NF - kBFirst) / kDmaB; }
+    static_assert(kLeadB != 1 || kDmaB <= NF, "one weight copy per n-tile step");
 };
 
 enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2 };
@@ -199,10 +212,12 @@ __device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
 }
 
-template <int MODE, bool GROUPED, bool OUTF32, int WAVES>
-__global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
-    using C = Cfg<WAVES>;
-    constexpr int BM = C::BM;
+template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF>
+__global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p) {
+    using C = Cfg<WAVES, NF>;
+    constexpr int BM = C::BM, BN = C::BN;
+    // per-row weight scales are copied by waves 0..3 in 64-row pieces
+    static_assert(MODE == MODE_BLOCK128 || NF == 8, "ROW128 and MX modes use 256-row weight tiles");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
     __shared__ int s_tile[2];
 
@@ -279,11 +294,13 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
     // ------------------------------------------------------- copy set-up
     // Wave w copies weight rows [8 kDmaB w, +8 kDmaB) and activation rows
     // [8 kDmaA w, +8 kDmaA), one instruction per 8 rows x 128 bytes.  Lane l
-    // fetches logical chunk (l % 8) ^ f(row) of row 8 j + l / 8.
+    // fetches logical chunk (l % 8) ^ f(row) of row 8 j + l / 8.  Copy slots
+    // past the tile's kCopiesB weight copies repeat the first ones.
     uint32_t offB[C::kDmaB], offA[C::kDmaA];
+    auto bcopy = [&](int t) { const int j = wave * C::kDmaB + t; return j < C::kCopiesB ? j : j - C::kCopiesB; };
 #pragma unroll
     for (int j = 0; j < C::kDmaB; ++j) {
-        const int row = (wave * C::kDmaB + j) * 8 + (lane >> 3);
+        const int row = bcopy(j) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz(row);
         offB[j] = (uint32_t)((int64_t)min(n0 + row, p.N - 1) * p.ldb + chunk * 16);
     }
@@ -310,6 +327,12 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
         const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
         sb_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4);
     }
+    // BLOCK128 weight scales: the wave's n-tiles before nb_w lie in the
+    // tile's first 128-row block, the rest in the next one.  Tiles span at
+    // most two blocks: 256 rows start at multiples of 256, 160 rows at
+    // multiples of 160 (block offsets 0..96) and 192 rows at multiples of
+    // 192 (offsets 0 or 64).
+    const int nb_w = NF == 8 ? NF : min(max(((n0 / 128 + 1) * 128 - (n0 + wn * 16 * NF)) / 16, 0), NF);
     const uint32_t lds0 = lds_addr(smem);
     auto bstage = [&](int i) { return lds0 + (uint32_t)(i * C::kBStageBytes); };                      // weights + sb
     auto abuf = [&](int i) { return lds0 + (uint32_t)(C::kBStages * C::kBStageBytes + i * C::kABufBytes); };  // acts + sa
@@ -333,12 +356,12 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
         dma16(p.a, offA[t] + (uint32_t)kb * BK, abuf(buf) + (wave * C::kDmaA + t) * 8 * BK);
     };
     auto copy_b = [&](int kb, int stage, int t) {
-        dma16(bptr, offB[t] + (uint32_t)kb * BK, bstage(stage) + (wave * C::kDmaB + t) * 8 * BK);
+        dma16(bptr, offB[t] + (uint32_t)kb * BK, bstage(stage) + bcopy(t) * 8 * BK);
     };
 
-    v4f acc[8][4];
+    v4f acc[NF][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -421,10 +444,10 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
         };
 
         if (MODE == MODE_MX) {
-            const uint32_t sb8 = opaque(tB + BN * BK + (wn * 128 + r16) * 4 + q);
-            const FragOff bb = frag_base(tB + wn * 128 * BK, fo);
+            const uint32_t sb8 = opaque(tB + BN * BK + (wn * 16 * NF + r16) * 4 + q);
+            const FragOff bb = frag_base(tB + wn * 16 * NF * BK, fo);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int nt = 0; nt < NF; ++nt) {
                 const v8i fb = read_frag(bb, nt * 16 * BK);
                 const int mxb = lds_readu8(sb8 + nt * 64);
 #pragma unroll
@@ -438,11 +461,19 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
             }
         } else {
             const uint32_t sbf = tB + BN * BK;
-            float sc[4];
+            // BLOCK128: a 256-row tile is two aligned 128-row blocks, one per
+            // wave column; other tiles hold the tile's first block for the
+            // wave's n-tiles before nb_w and the next block after it.
+            float sc[4], sc1[4];
             if (MODE == MODE_BLOCK128) {
-                const float sbv = lds_readf(sbf + wn * 4);
+                const float sbv = lds_readf(sbf + (NF == 8 ? wn * 4 : 0));
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) sc[mt] = sam[mt] * sbv;
+                if (NF != 8) {
+                    const float sbv1 = lds_readf(sbf + 4);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) sc1[mt] = sam[mt] * sbv1;
+                }
             }
             v4f part[2][4];
             f32x4 sbr[2];
@@ -450,9 +481,10 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     if (MODE == MODE_BLOCK128) {
+                        const float s = (NF == 8 || pt < nb_w) ? sc[mt] : sc1[mt];
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            acc[pt][mt][r] = __builtin_fmaf(part[ps][mt][r], sc[mt], acc[pt][mt][r]);
+                            acc[pt][mt][r] = __builtin_fmaf(part[ps][mt][r], s, acc[pt][mt][r]);
                     } else {
                         const float s4[4] = {sbr[ps][0], sbr[ps][1], sbr[ps][2], sbr[ps][3]};
 #pragma unroll
@@ -461,14 +493,14 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
                     }
                 }
             };
-            const FragOff bb = frag_base(tB + wn * 128 * BK, fo);
-            const uint32_t sbr_lds = opaque(sbf + (wn * 128 + 4 * q) * 4);
+            const FragOff bb = frag_base(tB + wn * 16 * NF * BK, fo);
+            const uint32_t sbr_lds = opaque(sbf + (wn * 16 * NF + 4 * q) * 4);
             v8i fb_next = read_frag(bb, 0);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int nt = 0; nt < NF; ++nt) {
                 const int ps = C::kDefer ? (nt & 1) : 0;
                 const v8i fb = fb_next;
-                if (nt < 7) fb_next = read_frag(bb, (nt + 1) * 16 * BK);
+                if (nt < NF - 1) fb_next = read_frag(bb, (nt + 1) * 16 * BK);
                 if (MODE == MODE_ROW128) sbr[ps] = lds_readf4(sbr_lds + nt * 64);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) part[ps][mt] = mfma_unit(fb, fa[mt]);
@@ -477,7 +509,7 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
                 else if (nt > 0) promote(nt - 1, (nt - 1) & 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (C::kDefer) promote(7, 1);
+            if (C::kDefer) promote(NF - 1, (NF - 1) & 1);
         }
     };
     int kb = 0;
@@ -495,10 +527,11 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
     for (; kb < nk; ++kb) step(kb, std::false_type{}, std::false_type{});
 
     // ---------------------------------------------------------- epilogue
-    // N % 128 == 0 and each wave covers 128 aligned n, so a wave's columns are
-    // all inside the matrix or all outside; rows are checked per lane.  One
-    // base address per m-tile, the n-tiles at constant offsets from it.
-    const int nw0 = n0 + wn * 128;
+    // N % 128 == 0: with 256-row tiles each wave covers 128 aligned n, so a
+    // wave's columns are all inside the matrix or all outside; other tiles
+    // check each 16-column n-tile (wave-uniform).  Rows are checked per lane.
+    // One base address per m-tile, the n-tiles at constant offsets from it.
+    const int nw0 = n0 + wn * 16 * NF;
     if (nw0 >= p.N) return;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -507,40 +540,36 @@ __global__ void __launch_bounds__(Cfg<WAVES>::kThreads, 1) k_gemm(KArgs p) {
         if (OUTF32) {
             float* dst = static_cast<float*>(p.c) + (int64_t)m * p.ldc + nw0 + 4 * q;
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                *reinterpret_cast<float4*>(dst + nt * 16) =
+            for (int nt = 0; nt < NF; ++nt)
+                if (NF == 8 || nw0 + nt * 16 < p.N)
+                    *reinterpret_cast<float4*>(dst + nt * 16) =
                     make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
         } else {
             uint16_t* dst = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + nw0 + 4 * q;
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                *reinterpret_cast<uint2*>(dst + nt * 16) = make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
-                                                                      pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
+            for (int nt = 0; nt < NF; ++nt)
+                if (NF == 8 || nw0 + nt * 16 < p.N)
+                    *reinterpret_cast<uint2*>(dst + nt * 16) =
+                        make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]), pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
         }
     }
 }
 
-template <int MODE, bool GROUPED, int WAVES>
-hipError_t launch(const KArgs& p, bool out_f32, dim3 grid, hipStream_t st) {
-    constexpr int T = Cfg<WAVES>::kThreads;
-    if (out_f32)
-        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES>), grid, dim3(T), 0, st, p);
-    else
-        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false, WAVES>), grid, dim3(T), 0, st, p);
-    return hipGetLastError();
-}
-
-template <int MODE, bool GROUPED, int WAVES>
-hipError_t launch_cfg(const KArgs& p, bool out_f32, hipStream_t st) {
-    constexpr int BM = Cfg<WAVES>::BM;
+template <int MODE, bool GROUPED, int WAVES, int NF>
+hipError_t launch(const KArgs& p, bool out_f32, hipStream_t st) {
+    using C = Cfg<WAVES, NF>;
     dim3 grid;
     if (!GROUPED) {
-        grid = dim3((unsigned)(((int64_t)(p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN)));
+        grid = dim3((unsigned)(((int64_t)(p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN)));
     } else {
         // upper bound on the number of BM-row tiles over all groups
-        grid = dim3((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM + p.G));
+        grid = dim3((unsigned)((p.N + C::BN - 1) / C::BN), (unsigned)((p.M + C::BM - 1) / C::BM + p.G));
     }
-    return launch<MODE, GROUPED, WAVES>(p, out_f32, grid, st);
+    if (out_f32)
+        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES, NF>), grid, dim3(C::kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false, WAVES, NF>), grid, dim3(C::kThreads), 0, st, p);
+    return hipGetLastError();
 }
 
 // Tile choice by rounds of tiles over the 256 CUs: a 256 x 256 tile (8 waves)
@@ -548,10 +577,73 @@ hipError_t launch_cfg(const KArgs& p, bool out_f32, hipStream_t st) {
 // so it wins unless it saves no round (small problems, where the smaller tile
 // finishes first).  `extra_tiles` counts partial tiles of grouped problems.
 int waves_for(int64_t rows, int64_t N, int64_t extra_tiles = 0) {
-    const int64_t ntn = (N + BN - 1) / BN;
+    const int64_t ntn = (N + 255) / 256;
     const int64_t r8 = (((rows + 255) / 256 + extra_tiles) * ntn + 255) / 256;
     const int64_t r4 = (((rows + 127) / 128 + extra_tiles) * ntn + 255) / 256;
     return 4 * r8 <= 3 * r4 ? 8 : 4;
+}
+
+// Dense BLOCK128 plans.  The output columns (weight rows) are cut into at
+// most two regions, each tiled with one configuration, so that the tiles
+// fill whole rounds over the compute units where the 256-row tile would
+// leave most of a round idle (N 2560 at M 4096: 160 tiles of 256 x 256 for
+// 256 CUs, against 256 tiles of 160 x 256).  The estimate per region is
+// rounds x (K slices x cycles per slice + cycles per tile), with the cycle
+// figures measured per configuration on the MLP shapes.
+constexpr int kCUs = 256;
+struct TileCfg {
+    int waves, nf;
+    double slice_cycles, tile_cycles;
+};
+constexpr TileCfg kDenseCfgs[] = {
+    {8, 8, 3440, 14000},   // 256 x 256
+    {4, 8, 2530, 10000},   // 256 x 128
+    {8, 5, 2520, 10000},   // 160 x 256
+    {4, 6, 2110, 8000},    // 192 x 128
+};
+constexpr double kLaunchCycles = 5000;       // a second launch on the stream
+
+double region_cycles(const TileCfg& c, int64_t M, int64_t N, int64_t nk) {
+    const int64_t bm = 32 * c.waves, bn = 32 * c.nf;
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    return (double)((tiles + kCUs - 1) / kCUs) * ((double)nk * c.slice_cycles + c.tile_cycles);
+}
+
+struct DensePlan {
+    int c1, c2;          // indices into kDenseCfgs; c2 < 0: one region
+    int64_t split;       // first column of the second region (multiple of 128)
+};
+
+DensePlan plan_dense(int64_t M, int64_t N, int64_t K) {
+    const int64_t nk = K / BK;
+    DensePlan best{0, -1, N};
+    double best_t = region_cycles(kDenseCfgs[0], M, N, nk);
+    const int nc = (int)(sizeof(kDenseCfgs) / sizeof(kDenseCfgs[0]));
+    for (int i = 0; i < nc; ++i) {
+        const double t = region_cycles(kDenseCfgs[i], M, N, nk);
+        if (t < best_t) { best_t = t; best = DensePlan{i, -1, N}; }
+        // region 1 in whole tiles of configuration i, on a 128-column boundary
+        const int64_t bn = 32 * kDenseCfgs[i].nf;
+        for (int64_t split = bn; split < N; split += bn) {
+            if (split % 128) continue;
+            const double t1 = region_cycles(kDenseCfgs[i], M, split, nk);
+            for (int j = 0; j < nc; ++j) {
+                if (j == i) continue;
+                const double tt = t1 + region_cycles(kDenseCfgs[j], M, N - split, nk) + kLaunchCycles;
+                if (tt < best_t) { best_t = tt; best = DensePlan{i, j, split}; }
+            }
+        }
+    }
+    return best;
+}
+
+hipError_t launch_dense(int ci, const KArgs& p, bool out_f32, hipStream_t st) {
+    switch (ci) {
+        case 0: return launch<MODE_BLOCK128, false, 8, 8>(p, out_f32, st);
+        case 1: return launch<MODE_BLOCK128, false, 4, 8>(p, out_f32, st);
+        case 2: return launch<MODE_BLOCK128, false, 8, 5>(p, out_f32, st);
+        default: return launch<MODE_BLOCK128, false, 4, 6>(p, out_f32, st);
+    }
 }
 
 KArgs base_args(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const void* sa, const uint8_t* b,
@@ -570,10 +662,29 @@ hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
     KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
     p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
-    const int w = waves_for(g.M, g.N);
     if (g.bscale_row)
-        return w == 8 ? launch_cfg<MODE_ROW128, false, 8>(p, g.out_f32, st) : launch_cfg<MODE_ROW128, false, 4>(p, g.out_f32, st);
-    return w == 8 ? launch_cfg<MODE_BLOCK128, false, 8>(p, g.out_f32, st) : launch_cfg<MODE_BLOCK128, false, 4>(p, g.out_f32, st);
+        return waves_for(g.M, g.N) == 8 ? launch<MODE_ROW128, false, 8, 8>(p, g.out_f32, st)
+                                        : launch<MODE_ROW128, false, 4, 8>(p, g.out_f32, st);
+    const DensePlan plan = plan_dense(g.M, g.N, g.K);
+    if (plan.c2 < 0) return launch_dense(plan.c1, p, g.out_f32, st);
+    KArgs p1 = p, p2 = p;
+    p1.N = (int32_t)plan.split;
+    p2.N = (int32_t)(g.N - plan.split);
+    p2.b = p.b + plan.split * p.ldb;
+    p2.sb = p.sb + (plan.split / 128) * p.sb_sn * 4;
+    p2.c = static_cast<uint8_t*>(p.c) + plan.split * (g.out_f32 ? 4 : 2);
+    const hipError_t e = launch_dense(plan.c1, p1, g.out_f32, st);
+    if (e != hipSuccess) return e;
+    return launch_dense(plan.c2, p2, g.out_f32, st);
+}
+
+void plan_gemm_blockscaled(int64_t M, int64_t N, int64_t K, int32_t out[5]) {
+    const DensePlan plan = plan_dense(M, N, K);
+    out[0] = kDenseCfgs[plan.c1].waves;
+    out[1] = 32 * kDenseCfgs[plan.c1].nf;
+    out[2] = plan.c2 < 0 ? 0 : kDenseCfgs[plan.c2].waves;
+    out[3] = plan.c2 < 0 ? 0 : 32 * kDenseCfgs[plan.c2].nf;
+    out[4] = (int32_t)plan.split;
 }
 
 hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st) {
@@ -581,8 +692,8 @@ hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st) {
     KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
     p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
     p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
-    return waves_for(g.M, g.N, g.G / 2) == 8 ? launch_cfg<MODE_BLOCK128, true, 8>(p, g.out_f32, st)
-                                              : launch_cfg<MODE_BLOCK128, true, 4>(p, g.out_f32, st);
+    return waves_for(g.M, g.N, g.G / 2) == 8 ? launch<MODE_BLOCK128, true, 8, 8>(p, g.out_f32, st)
+                                              : launch<MODE_BLOCK128, true, 4, 8>(p, g.out_f32, st);
 }
 
 hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st) {
@@ -591,10 +702,10 @@ hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st) {
     p.sa_sm = g.lds_a; p.sa_sk = 1; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.lds_b; p.sb_sk = 1;
     p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
     if (g.G == 0)
-        return waves_for(g.M, g.N) == 8 ? launch_cfg<MODE_MX, false, 8>(p, g.out_f32, st)
-                                        : launch_cfg<MODE_MX, false, 4>(p, g.out_f32, st);
-    return waves_for(g.M, g.N, g.G / 2) == 8 ? launch_cfg<MODE_MX, true, 8>(p, g.out_f32, st)
-                                              : launch_cfg<MODE_MX, true, 4>(p, g.out_f32, st);
+        return waves_for(g.M, g.N) == 8 ? launch<MODE_MX, false, 8, 8>(p, g.out_f32, st)
+                                        : launch<MODE_MX, false, 4, 8>(p, g.out_f32, st);
+    return waves_for(g.M, g.N, g.G / 2) == 8 ? launch<MODE_MX, true, 8, 8>(p, g.out_f32, st)
+                                              : launch<MODE_MX, true, 4, 8>(p, g.out_f32, st);
 }
 
 }  // namespace fp8bs

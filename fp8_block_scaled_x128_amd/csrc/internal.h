@@ -32,6 +32,9 @@ struct GemmArgs {
     int32_t G; const int32_t* offsets; const int32_t* a_rows;   // grouped only
 };
 hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st);
+// Tiling of a dense BLOCK128 problem: waves and weight rows per tile of the
+// two column regions, and the first column of the second (N if one region).
+void plan_gemm_blockscaled(int64_t M, int64_t N, int64_t K, int32_t out[5]);
 hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st);
 
 struct MxGemmArgs {

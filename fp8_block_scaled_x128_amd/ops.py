@@ -24,7 +24,8 @@ AXIS_ROW, AXIS_COL = 0, 1
 OUT_BF16, OUT_FP32 = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
-EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_blockscaled_gemm", "fp8_grouped_gemm",
+EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
+           "fp8_grouped_gemm",
            "fp8_silu_mul_quant", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
 
@@ -55,6 +56,7 @@ def load():
             "fp8_quant_rowblock": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P],
             "fp8_quant_block2d": [P, I64, I64, I64, I64, P, I64, P, I64, P, P],
             "fp8_blockscaled_gemm": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P, I64, INT, P],
+            "fp8_blockscaled_gemm_plan": [I64, I64, I64, P],
             "fp8_grouped_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64,
                                  P, I64, INT, P],
             "fp8_silu_mul_quant": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P, I64, P],
@@ -116,6 +118,14 @@ def fp8_blockscaled_gemm(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, 
     st = load().fp8_blockscaled_gemm(M, N, K, _p(a), lda, _p(sa), sa_stride_m, sa_stride_k, _p(b), ldb, _p(sb),
                                      sb_stride_n, sb_stride_k, bscale, _p(c), ldc, out, _stream(stream))
     return _check("fp8_blockscaled_gemm", st, raise_on_error)
+
+
+def fp8_blockscaled_gemm_plan(M, N, K):
+    """Tiling of a BLOCK128 problem: ((waves, weight rows per tile) for columns
+    [0, split), (waves, rows) for [split, N) or None, split).  Host only."""
+    out = (ctypes.c_int32 * 5)()
+    _check("fp8_blockscaled_gemm_plan", load().fp8_blockscaled_gemm_plan(M, N, K, ctypes.cast(out, ctypes.c_void_p)))
+    return (out[0], out[1]), ((out[2], out[3]) if out[2] else None), out[4]
 
 
 def fp8_grouped_gemm(total_rows, N, K, G, offsets, a_rows, a_count, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb,

@@ -4,13 +4,15 @@
         per-kernel duration table from a `rocprofv3 --kernel-trace --stats` run
 
     python -m fp8_block_scaled_x128_amd.profiling traffic --fetch CSV --write CSV
-            --copy-mib N --command-fetch CMD --command-write CMD --out FILE.json
-        HBM bytes per launch of the dense GEMM from two `rocprofv3 --pmc`
-        runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch).  Each counter
-        is scaled by what it reads for the plain device copy of N MiB that
-        bench.py --copy-probe-mib N runs after its timed region (known bytes
-        read and written).  The record carries a hash of the GEMM sources, so
-        bench.py reports it only while the kernel is unchanged.
+            --copy-mib N --gemm-calls C --command-fetch CMD --command-write CMD --out FILE.json
+        HBM bytes per dense GEMM call from two `rocprofv3 --pmc` runs
+        (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) of a program that
+        makes C dense BLOCK128 GEMM calls, half of them the MLP up projection
+        and half the down projection (a call may launch two tilings).  Each
+        counter is scaled by what it reads for the plain device copy of N MiB
+        that bench.py --copy-probe-mib N runs after its timed region (known
+        bytes read and written).  The record carries a hash of the GEMM
+        sources, so bench.py reports it only while the kernel is unchanged.
 """
 from __future__ import annotations
 
@@ -24,7 +26,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemm.hip", "device_common.h", "internal.h")]
-DENSE_GEMM_KERNEL = "k_gemm<0, false, false, 8>"      # BLOCK128 mode, dense, bf16 out, 256x256 tile
+DENSE_GEMM_KERNEL = "k_gemm<0, false, false, "       # BLOCK128 mode, dense, bf16 out, every tiling
 COPY_KERNEL = "copyBuffer"
 
 
@@ -67,7 +69,7 @@ def _per_kernel(counter_csv: str, counter: str):
     return res
 
 
-def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, cmd_fetch: str, cmd_write: str) -> dict:
+def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, calls: int, cmd_fetch: str, cmd_write: str) -> dict:
     fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
     write = _per_kernel(write_csv, "WRITE_SIZE")
     copy_bytes = copy_mib * (1 << 20)
@@ -88,8 +90,8 @@ def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, cmd_fetch: str
         by_grid.setdefault(grid, {"fetch": [], "write": []})["fetch"].append(v * 1024 * f_scale)
     for grid, v in g_w:
         by_grid.setdefault(grid, {"fetch": [], "write": []})["write"].append(v * 1024 * w_scale)
-    fetch_pl = statistics.mean(v * 1024 * f_scale for _, v in g_f)
-    write_pl = statistics.mean(v * 1024 * w_scale for _, v in g_w)
+    fetch_pl = sum(v * 1024 * f_scale for _, v in g_f) / calls
+    write_pl = sum(v * 1024 * w_scale for _, v in g_w) / calls
     # the two GEMMs of the MLP step: up (M 4096, N 9728, K 2560) and down (M 4096, N 2560, K 9728);
     # minimum bytes = both FP8 operands, their FP32 scales and the bf16 output, once each
     mins = []
@@ -98,11 +100,13 @@ def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, cmd_fetch: str
     return {
         "kernel": DENSE_GEMM_KERNEL,
         "gemm_sources_sha256": gemm_sources_hash(),
+        "gemm_calls": calls,
         "hbm_bytes_per_launch": fetch_pl + write_pl,
         "fetch_bytes_per_launch": fetch_pl,
         "write_bytes_per_launch": write_pl,
         "algorithmic_min_bytes_per_launch": statistics.mean(mins),
-        "per_grid_size": {str(g): {"fetch_bytes": statistics.mean(v["fetch"]), "write_bytes": statistics.mean(v["write"])}
+        "per_grid_size": {str(g): {"dispatches": len(v["fetch"]), "fetch_bytes": statistics.mean(v["fetch"]),
+                                   "write_bytes": statistics.mean(v["write"])}
                           for g, v in by_grid.items()},
         "copy_calibration": {"bytes": copy_bytes, "fetch_counter_bytes": f_copy, "write_counter_bytes": w_copy,
                              "fetch_scale": f_scale, "write_scale": w_scale},
@@ -121,6 +125,7 @@ def main(argv=None):
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--gemm-calls", type=int, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out", required=True)
@@ -129,7 +134,7 @@ def main(argv=None):
         with open(a.out, "w") as fh:
             fh.write(stats_markdown(a.stats_csv, a.command))
     else:
-        rec = traffic_record(a.fetch, a.write, a.copy_mib, a.command_fetch, a.command_write)
+        rec = traffic_record(a.fetch, a.write, a.copy_mib, a.gemm_calls, a.command_fetch, a.command_write)
         with open(a.out, "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")

@@ -142,6 +142,22 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
                                   void* c, int64_t ldc, fp8bs_out out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_blockscaled_gemm_plan -- the tiling fp8_blockscaled_gemm launches for
+ * an FP8BS_BSCALE_BLOCK128 problem of this shape.  Host only: launches
+ * nothing and needs no device.  (A description of the launch, not an
+ * operation of the layer.)
+ *
+ * plan : int32[5], written on FP8BS_OK:
+ *   plan[0], plan[1]  waves per workgroup and weight rows (n) per tile for
+ *                     output columns [0, plan[4]);
+ *   plan[2], plan[3]  the same for columns [plan[4], N), or 0, 0 when one
+ *                     tiling covers all columns (then plan[4] == N);
+ *   a tile covers 32 * waves activation rows (m).
+ * Requirements: M, N, K >= 0; K % 128 == 0; N % 128 == 0.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_blockscaled_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t* plan);
+
+/* ------------------------------------------------------------------------
  * fp8_grouped_gemm -- the block-scaled GEMM over G expert groups of rows
  * (the MoE layers the pages run the recipe on, Qwen3-30B-A3B, "Low
  * Precision RL", table "Choose a precision").

@@ -153,11 +153,13 @@ def sample_indices(M, N, count, seed):
     rng = np.random.default_rng(seed)
     mi = rng.integers(0, M, count)
     ni = rng.integers(0, N, count)
-    # corners of every 256 x 256 output tile and the matrix edges
-    tm = np.arange(0, M, 256)
-    tn = np.arange(0, N, 256)
-    cm, cn = np.meshgrid(np.concatenate([tm, np.minimum(tm + 255, M - 1)]),
-                         np.concatenate([tn, np.minimum(tn + 255, N - 1)]), indexing="ij")
+    # corners of every output tile of each tiling (128 or 256 rows of M;
+    # 160, 192 or 256 columns of N) and the matrix edges
+    tm = np.unique(np.concatenate([np.arange(0, M, 128), np.arange(0, M, 256)]))
+    tn = np.unique(np.concatenate([np.arange(0, N, t) for t in (160, 192, 256)]))
+    em = np.unique(np.concatenate([tm, np.minimum(np.arange(128, M + 128, 128), M) - 1]))
+    en = np.unique(np.concatenate([tn] + [np.minimum(np.arange(t, N + t, t), N) - 1 for t in (160, 192, 256)]))
+    cm, cn = np.meshgrid(em, en, indexing="ij")
     return np.concatenate([mi, cm.reshape(-1)]), np.concatenate([ni, cn.reshape(-1)])
 
 

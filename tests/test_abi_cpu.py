@@ -86,3 +86,27 @@ def test_host_validation_rejects_before_launch(lib):
     # empty inputs are a successful no-op
     assert ops.fp8_quant_rowblock(None, 0, 128, 128, 0, None, 128, None, 1, 1, stream=0,
                                   raise_on_error=False) == 0
+
+
+def test_dense_tile_plan(lib):
+    """The tiling query (host only): regions cover N on a 128-column boundary,
+    every region's tiling is one the library builds, and the MLP shapes get
+    tilings that fill whole rounds of 256 compute units."""
+    from fp8_block_scaled_x128_amd import ops
+    tilings = {(8, 256), (4, 256), (8, 160), (4, 192)}
+    for M in (1, 130, 1000, 4096, 4100, 16384):
+        for N in (128, 640, 1408, 2560, 4096, 9728):
+            for K in (128, 2560, 9728):
+                first, second, split = ops.fp8_blockscaled_gemm_plan(M, N, K)
+                assert first in tilings
+                if second is None:
+                    assert split == N
+                else:
+                    assert second in tilings and second != first
+                    assert 0 < split < N and split % 128 == 0 and split % first[1] == 0
+    # down projection: 16 x 16 tiles of 160 x 256; up projection: two full
+    # rounds of 256 x 256 tiles, then one round of 192 x 128 tiles
+    assert ops.fp8_blockscaled_gemm_plan(4096, 2560, 9728) == ((8, 160), None, 2560)
+    assert ops.fp8_blockscaled_gemm_plan(4096, 9728, 2560) == ((8, 256), (4, 192), 8192)
+    assert lib.fp8_blockscaled_gemm_plan(128, 100, 128, ctypes.c_void_p(1 << 20)) == 2
+    assert lib.fp8_blockscaled_gemm_plan(128, 128, 128, None) == 1

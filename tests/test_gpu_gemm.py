@@ -86,17 +86,53 @@ def test_exact_integer_case_bit_exact(M, N, K):
     assert np.array_equal(y16, oracle.f64_to_bf16(yref))
 
 
-def test_exact_integer_case_256x256_tiles_ragged():
-    """Large enough for the 256 x 256 tile configuration, with M not a multiple
-    of the tile: sampled outputs (all of the last rows) bit-exact."""
-    M, N, K = 4100, 4096, 512
-    qa, sa, qb, sb = _exact_case(M, N, K, 77)
-    _, y32 = _run_both(dev(qa), dev(sa), dev(qb), dev(sb))
+def _plan(M, N, K):
+    (w1, n1), second, split = ops.fp8_blockscaled_gemm_plan(M, N, K)
+    return ((w1, n1), second, split)
+
+
+# Every dense tiling, each on a shape that the planner routes to it: M not a
+# multiple of the tile's rows, N not a multiple of its columns where the
+# tiling allows, and both two-region plans.
+PLAN_CASES = [
+    ((4100, 2688, 512), ((8, 256), None, 2688)),
+    ((3000, 2560, 640), ((8, 160), None, 2560)),
+    ((4100, 4096, 512), ((8, 160), None, 4096)),
+    ((1000, 1408, 384), ((4, 192), None, 1408)),
+    ((130, 128, 128), ((4, 192), None, 128)),
+    ((4096, 9728, 512), ((8, 256), (4, 192), 8192)),
+    ((4100, 9728, 384), ((8, 256), (8, 160), 7424)),
+]
+
+
+@pytest.mark.parametrize("shape,plan", PLAN_CASES)
+def test_exact_integer_case_every_tiling(shape, plan):
+    """Sampled outputs plus every output in the last rows, the last columns and
+    the columns around a region boundary, bit-exact."""
+    M, N, K = shape
+    assert _plan(M, N, K) == plan
+    _say("tiling", shape, plan)
+    qa, sa, qb, sb = _exact_case(M, N, K, M + N)
+    y16, y32 = _run_both(dev(qa), dev(sa), dev(qb), dev(sb))
     mi, ni = sample_indices(M, N, 4000, 3)
-    mi = np.concatenate([mi, np.repeat(np.arange(M - 4, M), N)])
-    ni = np.concatenate([ni, np.tile(np.arange(N), 4)])
+    edge_cols = np.unique(np.concatenate([np.arange(N - 48, N), np.arange(max(plan[2] - 48, 0), min(plan[2] + 48, N))]))
+    mi = np.concatenate([mi, np.repeat(np.arange(M - 4, M), N), np.repeat(np.arange(0, M, 7), edge_cols.size)])
+    ni = np.concatenate([ni, np.tile(np.arange(N), 4), np.tile(edge_cols, (M + 6) // 7)])
     yref, _ = oracle.gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni)
     assert np.array_equal(y32[mi, ni].astype(np.float64), yref)
+    assert np.array_equal(y16[mi, ni], oracle.f64_to_bf16(yref))
+
+
+@pytest.mark.parametrize("M,N,K", [(3000, 2560, 640), (1000, 1408, 384)])
+def test_other_tilings_real_data(M, N, K):
+    """Quantized N(0,1) activations with outliers and N(0, 0.02) weights on the
+    160- and 192-row tilings: every output within tolerance."""
+    _say("tiling real data", M, N, K, _plan(M, N, K))
+    x = _bits((M, K), 50 + M, 1.0, 0.001, 100.0)
+    w = _bits((N, K), 51 + N, 0.02)
+    qa, sa, qb, sb = _linear_operands(x, w)
+    y16, y32 = _run_both(qa, sa, qb, sb)
+    verify(host(qa), host(sa), host(qb), host(sb), y32, y16)
 
 
 def test_dgrad_through_transposed_weight_copy():
