@@ -22,10 +22,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
-// Streaming global accesses (the "nt" cache policy): every quantizer reads its
-// bf16 input and writes its codes exactly once.  Measured on MI355X with a
-// 1 GiB stream: 7.2 TB/s read and 6.0 TB/s copy with nt, against 6.3 and 5.5
-// TB/s with the default policy.
+// Streaming global accesses (the "nt" cache policy) for data read or written
+// once and not consumed right after: the quantizers' bf16 inputs and the
+// SiLU kernel's bf16 h.  Measured on MI355X with a 1 GiB stream: 7.2 TB/s
+// read and 6.0 TB/s copy with nt, against 6.3 and 5.5 TB/s with the default
+// policy.  FP8 codes keep the default policy: the GEMM that follows reads
+// them, and with nt stores it fetched them from HBM instead of the last-level
+// cache (down projection 137 -> 122 us in the MLP step).
 typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 load_nt16(const void* p) {

@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
                     static_cast<uint8_t*>(p.s)[(int64_t)r * p.ssr + (int64_t)(g * 4 + (sub >> 2)) * p.ssg] =
                         (uint8_t)(e + 127);
             }
-            if (valid) store_nt8(p.q + (int64_t)r * p.ld_q + c, w0, w1);
+            if (valid) *reinterpret_cast<uint2*>(p.q + (int64_t)r * p.ld_q + c) = make_uint2(w0, w1);
         }
     }
 }
@@ -303,7 +303,7 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
         encode8(v, sc, w0, w1);
         const int rl = (t >> 4) + 16 * i;
         const int32_t r = r0 + rl, c = c0 + cc * 8;
-        if (r < rows && c < cols) store_nt8(q + (int64_t)r * ld_q + c, w0, w1);
+        if (r < rows && c < cols) *reinterpret_cast<uint2*>(q + (int64_t)r * ld_q + c) = make_uint2(w0, w1);
         if (TRANS) { ctile[rl][2 * cc] = w0; ctile[rl][2 * cc + 1] = w1; }
     }
     if (t == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = sc;
