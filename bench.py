@@ -48,8 +48,11 @@ WORKLOADS = ("tiny_linear", "mlp_backward", "moe_blockwise", "moe_mxfp8")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # the shader clock takes tens of milliseconds of sustained load to settle
+    # (GEMM time falls by 10-20% over the first ~10 ms): 200 untimed steps
+    # (about 70 ms) come first
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--copies", type=int, default=4, help="activation copies rotated across steps")
     ap.add_argument("--reps", type=int, default=10, help="repetitions per kernel of the other workloads")
     ap.add_argument("--workloads", default=",".join(WORKLOADS),
@@ -410,7 +413,7 @@ def main():
             sys.exit(2)
         print("timing %s" % wname, file=sys.stderr, flush=True)
         seq, cfg = table[wname](torch, ops, inputs, to_dev, R)
-        ms = time_sequence(torch, stream, [fn for _, fn, _ in seq], args.reps, 3)
+        ms = time_sequence(torch, stream, [fn for _, fn, _ in seq], args.reps, 10)
         ks = {n: kernel_entry(*wk, t) for (n, _, wk), t in zip(seq, ms)}
         others[wname] = {"config": cfg, "ms_per_pass": round(float(sum(ms)), 5), "kernels": ks}
         del seq

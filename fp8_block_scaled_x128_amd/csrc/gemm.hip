@@ -507,6 +507,18 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
                 copy_step(nt);
                 if (!C::kDefer) promote(nt, 0);
                 else if (nt > 0) promote(nt - 1, (nt - 1) & 1);
+                if (C::kDefer && nt > 0) {
+                    // issue order: one matrix instruction, then four of the
+                    // promotion FMAs, four times, so that a wave running alone
+                    // on its SIMD keeps the matrix unit busy while its vector
+                    // FMAs issue (a block of four matrix instructions followed
+                    // by sixteen FMAs leaves the unit idle during the FMAs)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (C::kDefer) promote(NF - 1, (NF - 1) & 1);
