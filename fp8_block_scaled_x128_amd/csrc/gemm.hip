@@ -219,7 +219,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     // per-row weight scales are copied by waves 0..3 in 64-row pieces
     static_assert(MODE == MODE_BLOCK128 || NF == 8, "ROW128 and MX modes use 256-row weight tiles");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
-    __shared__ int s_tile[2];
+    __shared__ int s_tile[3];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -250,11 +250,34 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         m_end = min(p.M, m_begin + BM);
         n0 = tn * BN;
     } else {
-        // Work item blockIdx.y is the blockIdx.y-th BM-row tile in the list of
-        // all groups' tiles; wave 0 scans the per-group tile counts.
+        // Work items are (row tile, n-tile) pairs, row-tile major, over the
+        // list of all groups' BM-row tiles.  Workgroups are dealt round-robin
+        // to the 8 XCDs, and each XCD takes one contiguous range of work
+        // items: the n-tiles of a row tile and the row tiles of one expert
+        // then run on the same XCD and share their operand panels in its L2
+        // (dealing n-tiles across XCDs fetched the grouped gate/up operands
+        // 4.8 times from HBM).  Wave 0 counts all row tiles (pass 1), maps
+        // the workgroup to its work item, then finds the group of the item's
+        // row tile with a prefix scan of the per-group counts (pass 2).
+        const int ntn = (p.N + BN - 1) / BN;
         if (threadIdx.x == 0) s_tile[0] = -1;
         if (wave == 0) {
-            const int t = blockIdx.y;
+            int total = 0;
+            for (int gb = 0; gb < p.G; gb += 128) {
+                const int g0 = gb + 2 * lane, g1 = g0 + 1;
+                int c = 0;
+                if (g0 < p.G) c += (p.offsets[g0 + 1] - p.offsets[g0] + BM - 1) / BM;
+                if (g1 < p.G) c += (p.offsets[g1 + 1] - p.offsets[g1] + BM - 1) / BM;
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+                total += c;
+            }
+            const int items = total * ntn;
+            const int per = (items + 7) / 8;
+            const int bid = blockIdx.x;
+            const int item = bid / 8 < per ? (bid % 8) * per + bid / 8 : items;
+            const int t = item < items ? item / ntn : -1;   // row tile, -1: no work
+            if (lane == 0) s_tile[2] = item - (item / ntn) * ntn;
             int carry = 0;
             for (int gb = 0; gb < p.G; gb += 128) {
                 const int g0 = gb + 2 * lane, g1 = g0 + 1;
@@ -281,7 +304,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         const int lt = s_tile[1];
         m_begin = p.offsets[g] + lt * BM;
         m_end = min(p.offsets[g + 1], m_begin + BM);
-        n0 = blockIdx.x * BN;
+        n0 = s_tile[2] * BN;
         bptr += (int64_t)g * p.b_sg;
         sbp += (int64_t)g * p.sb_sg * (MODE == MODE_MX ? 1 : 4);
     }
@@ -574,8 +597,10 @@ hipError_t launch(const KArgs& p, bool out_f32, hipStream_t st) {
     if (!GROUPED) {
         grid = dim3((unsigned)(((int64_t)(p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN)));
     } else {
-        // upper bound on the number of BM-row tiles over all groups
-        grid = dim3((unsigned)((p.N + C::BN - 1) / C::BN), (unsigned)((p.M + C::BM - 1) / C::BM + p.G));
+        // upper bound on the work items (row tiles over all groups x n-tiles),
+        // rounded up to a multiple of the 8 XCDs
+        const int64_t items = ((int64_t)(p.M + C::BM - 1) / C::BM + p.G) * ((p.N + C::BN - 1) / C::BN);
+        grid = dim3((unsigned)((items + 7) / 8 * 8));
     }
     if (out_f32)
         hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES, NF>), grid, dim3(C::kThreads), 0, st, p);
