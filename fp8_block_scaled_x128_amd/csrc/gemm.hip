@@ -238,8 +238,12 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         // consecutive tile ids on one XCD (workgroups are dealt round-robin to the 8 XCDs)
         const int per = nblk / 8;
         const int tile = bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
-        // groups of GM m-tiles sweep n, so co-resident tiles share operand panels in L2
-        constexpr int GM = 8;
+        // groups of GM m-tiles sweep n, so co-resident tiles share operand
+        // panels in L2.  An XCD runs 32 tiles at a time, GM m-tiles x 32/GM
+        // n-tiles, and fetches GM A panels (BM rows) and 32/GM B panels (BN
+        // rows) per round: GM = 4 when BN < BM (160 x 256: 4 x 256 + 8 x 160
+        // rows against 8 x 256 + 4 x 160), else 8.
+        constexpr int GM = BN < BM ? 4 : 8;
         const int gsz = GM * ntn;
         const int grp = tile / gsz;
         const int fm = grp * GM;
