@@ -11,6 +11,8 @@
 // All kernels are HBM-bound.  They read bf16 with 16-byte loads (8 values
 // per lane), reduce the group maximum with lane shuffles inside the 16-lane
 // DPP row that owns a 1x128 group, and write codes with 8- or 16-byte stores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -260,7 +262,7 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
     o[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-template <bool TRANS>
+template <bool TRANS, bool NT>
 __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __restrict__ w, int32_t rows, int32_t cols,
                                                             int64_t ld_w, uint8_t* __restrict__ q, int64_t ld_q,
                                                             uint8_t* __restrict__ qt, int64_t ld_qt,
@@ -280,7 +282,10 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
     for (int i = 0; i < 8; ++i) {
         const int32_t r = r0 + (t >> 4) + 16 * i, c = c0 + cc * 8;
         raw[i] = make_uint4(0, 0, 0, 0);
-        if (r < rows && c < cols) raw[i] = *reinterpret_cast<const uint4*>(w + (int64_t)r * ld_w + c);
+        if (r < rows && c < cols) {
+            const uint16_t* src = w + (int64_t)r * ld_w + c;
+            raw[i] = NT ? load_nt16(src) : *reinterpret_cast<const uint4*>(src);
+        }
     }
     float m = 0.0f;
 #pragma unroll
@@ -303,7 +308,11 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
         encode8(v, sc, w0, w1);
         const int rl = (t >> 4) + 16 * i;
         const int32_t r = r0 + rl, c = c0 + cc * 8;
-        if (r < rows && c < cols) *reinterpret_cast<uint2*>(q + (int64_t)r * ld_q + c) = make_uint2(w0, w1);
+        if (r < rows && c < cols) {
+            uint8_t* dst = q + (int64_t)r * ld_q + c;
+            if (NT) store_nt8(dst, w0, w1);
+            else *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+        }
         if (TRANS) { ctile[rl][2 * cc] = w0; ctile[rl][2 * cc + 1] = w1; }
     }
     if (t == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = sc;
@@ -326,9 +335,12 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int32_t c = c0 + cb * 4 + k;
-                if (c < cols)
-                    *reinterpret_cast<uint4*>(qt + (int64_t)c * ld_qt + rs) =
-                        make_uint4(col[k][0], col[k][1], col[k][2], col[k][3]);
+                if (c < cols) {
+                    uint8_t* dst = qt + (int64_t)c * ld_qt + rs;
+                    const uint4 v = make_uint4(col[k][0], col[k][1], col[k][2], col[k][3]);
+                    if (NT) store_nt16(dst, v);
+                    else *reinterpret_cast<uint4*>(dst) = v;
+                }
             }
         }
     }
@@ -393,12 +405,22 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, 
     if (rows == 0 || cols == 0 || batch == 0) return hipSuccess;
     const int32_t nbr = (int32_t)((rows + 127) / 128), nbc = (int32_t)((cols + 127) / 128);
     dim3 grid((unsigned)nbc, (unsigned)nbr, (unsigned)batch);
-    if (qt)
-        hipLaunchKernelGGL(k_quant_128x128<true>, grid, dim3(kThreads), 0, st, w, (int32_t)rows, (int32_t)cols, ld_w, q,
-                           ld_q, qt, ld_qt, s, nbr, nbc);
-    else
-        hipLaunchKernelGGL(k_quant_128x128<false>, grid, dim3(kThreads), 0, st, w, (int32_t)rows, (int32_t)cols, ld_w, q,
-                           ld_q, qt, ld_qt, s, nbr, nbc);
+    // Weights larger than the 256 MB last-level cache (the MoE expert stacks)
+    // stream through it with the nt policy: their codes cannot stay cached for
+    // the GEMM anyway.  Smaller weights keep the default policy (the nt loads
+    // lost on them, and their codes should stay cached for the GEMM).
+    const bool nt = batch * rows * cols * 2 > ((int64_t)256 << 20);
+    auto go = [&](auto trans, auto ntt) {
+        hipLaunchKernelGGL((k_quant_128x128<decltype(trans)::value, decltype(ntt)::value>), grid, dim3(kThreads), 0, st,
+                           w, (int32_t)rows, (int32_t)cols, ld_w, q, ld_q, qt, ld_qt, s, nbr, nbc);
+    };
+    if (qt) {
+        if (nt) go(std::true_type{}, std::true_type{});
+        else go(std::true_type{}, std::false_type{});
+    } else {
+        if (nt) go(std::false_type{}, std::true_type{});
+        else go(std::false_type{}, std::false_type{});
+    }
     return hipGetLastError();
 }
 
