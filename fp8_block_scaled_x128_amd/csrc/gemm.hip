@@ -12,10 +12,11 @@
 // section "3. Unified MXFP8 (Blackwell)") hands its power-of-two block scales
 // to the scaled matrix instruction, which applies them exactly.
 //
-// Kernel structure: one workgroup per output tile of 256 weight rows (n) x
-// 128 (4 waves, one per SIMD) or 256 (8 waves, two per SIMD) activation rows.
-//  - K advances in 128-byte slices.  The slice of the weight tile (32 KB), of
-//    the activation tile (16 or 32 KB) and the slice's scales are copied
+// Kernel structure: one workgroup per output tile of 32 NF weight rows (n;
+// NF = 8, 6 or 5) x 128 (4 waves, one per SIMD) or 256 (8 waves, two per
+// SIMD) activation rows; the host picks the tiling (waves_for, plan_dense).
+//  - K advances in 128-byte slices.  The slice of the weight tile (32 NF
+//    rows x 128 B), of the activation tile and the slice's scales are copied
 //    straight from global memory into LDS with global_load_lds (no register
 //    staging), through the multi-buffer pipeline described at Cfg.
 //  - LDS rows are 128 bytes; 16-byte chunk c of row r sits in slot
@@ -23,8 +24,8 @@
 //    (measured with the LDS bank-conflict counter; the variant
 //    (r & 7) ^ ((r >> 3) & 1) costs 4 conflict cycles per read).  The copy
 //    realizes the swizzle by choosing which global chunk each lane fetches.
-//  - Wave w owns n rows [128 * (w & 1), +128) and m rows [64 * (w >> 1), +64):
-//    8 x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4 per slice.  Weight rows
+//  - Wave w owns n rows [16 NF (w & 1), +16 NF) and m rows [64 (w >> 1), +64):
+//    NF x 4 tiles of v_mfma_scale_f32_16x16x128_f8f6f4 per slice.  Weight rows
 //    are the instruction's A operand and activation rows its B operand, so a
 //    lane's 4 outputs share one activation row m and four consecutive n.
 //  - FP32-scale modes: each MFMA produces a fresh FP32 partial for its slice

@@ -21,6 +21,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -30,11 +31,19 @@ DENSE_GEMM_KERNEL = "k_gemm<0, false, false, "       # BLOCK128 mode, dense, bf1
 COPY_KERNEL = "copyBuffer"
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed, so that a
+    comment edit does not invalidate a counter record of unchanged code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def gemm_sources_hash() -> str:
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
