@@ -167,6 +167,8 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t
     if (!aligned(sa, 4) || !aligned(sb, 4)) return fail(FP8BS_ERR_ALIGN, "scales must be 4-byte aligned");
     if ((uint64_t)M * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
         return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
+    // tiles (at least 128 rows x 160 columns) are counted in int32 on the device
+    if (((M + 127) / 128) * ((N + 159) / 160) >= (1ll << 31) - 8) return fail(FP8BS_ERR_SHAPE, "too many tiles");
     if ((v = check_scale_extent("sa", M, sa_stride_m, K / 128, sa_stride_k, 4)) != FP8BS_OK) return v;
     if ((v = check_scale_extent("sb", bscale == FP8BS_BSCALE_ROW128 ? N : N / 128, sb_stride_n, K / 128,
                                 sb_stride_k, 4)) != FP8BS_OK)
@@ -204,7 +206,10 @@ fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t 
     if (a_rows && a_count < 1) return fail(FP8BS_ERR_SHAPE, "a_count must be >= 1 with a_rows");
     if ((uint64_t)arows * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
         return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
-    if ((total_rows + 255) / 256 + G > 65535) return fail(FP8BS_ERR_SHAPE, "too many row tiles");
+    // work items (row tiles of at least 128 rows over all groups x 256-column
+    // n-tiles) are counted in int32 on the device
+    if (((total_rows + 127) / 128 + G) * ((N + 255) / 256) >= (1ll << 31) - 8)
+        return fail(FP8BS_ERR_SHAPE, "too many tiles");
     if ((v = check_scale_extent("sa", arows, sa_stride_m, K / 128, sa_stride_k, 4)) != FP8BS_OK) return v;
     if ((v = check_scale_extent("sb", N / 128, sb_stride_n, K / 128, sb_stride_k, 4)) != FP8BS_OK) return v;
     if (sb_stride_g < 0 || b_stride_g < 0) return fail(FP8BS_ERR_STRIDE, "negative group stride");
@@ -274,7 +279,10 @@ fp8bs_status mxfp8_gemm(int64_t rows, int64_t N, int64_t K, int32_t G, const int
     if (G > 0 && a_rows && a_count < 1) return fail(FP8BS_ERR_SHAPE, "a_count must be >= 1 with a_rows");
     if ((uint64_t)arows * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
         return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
-    if ((rows + 255) / 256 + G > 65535) return fail(FP8BS_ERR_SHAPE, "too many row tiles");
+    // work items (row tiles of at least 128 rows, over all groups) x n-tiles
+    // are counted in int32 on the device
+    if (((rows + 127) / 128 + G) * ((N + 255) / 256) >= (1ll << 31) - 8)
+        return fail(FP8BS_ERR_SHAPE, "too many tiles");
     if ((v = check_scale_extent("sa", arows, lds_a, 1, 0, 1)) != FP8BS_OK) return v;
     if ((v = check_scale_extent("sb", N, lds_b, 1, 0, 1)) != FP8BS_OK) return v;
     if (G > 0 && (sb_stride_g < 0 || b_stride_g < 0)) return fail(FP8BS_ERR_STRIDE, "negative group stride");
