@@ -186,6 +186,30 @@ def quant_128x128(x):
     return q, s
 
 
+def quant_rowwise(x):
+    """One group per row (rowwise scaling; the tensorwise/rowwise comparison
+    of "Towards Full Pipeline FP8 Reinforcement Learning for LLMs").
+    x: [rows, cols] -> (q [rows, cols], s [rows] float32)."""
+    x = _bf16_view(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows,), np.float32)
+    _load().or_quant_rowwise(_ptr(x), rows, cols, cols, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_tensorwise(x):
+    """One group for the whole tensor ("per-tensor", "Unified FP8...",
+    section "FP8 Quantization").  x: [rows, cols] -> (q [rows, cols],
+    s [1] float32)."""
+    x = _bf16_view(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((1,), np.float32)
+    _load().or_quant_tensorwise(_ptr(x), rows, cols, cols, _ptr(q), _ptr(s))
+    return q, s
+
+
 def mx_quant_1x32(x):
     """MXFP8: 1x32 blocks along the contiguous axis, UE8M0 codes.
     x: [rows, cols] -> (q [rows, cols], s [rows, ceil(cols/32)] uint8)."""
@@ -242,6 +266,27 @@ def gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni, bmode=BSCALE_BLOCK128):
                                         _ptr(qb), K, _ptr(sb), sb.shape[1], 1, int(bmode),
                                         _ptr(mi), _ptr(ni), mi.size, _ptr(y), _ptr(yabs))
     return y, yabs
+
+
+def expand_rowscales(sa, sb, M, N, K):
+    """Scales constant along K (rowwise: sa [M], sb [N]; tensorwise: one value
+    each) written out per 128-wide K slice, as the block-scaled GEMM takes
+    them: (sa [M, K/128], sb [N, K/128]) for BSCALE_ROW128."""
+    nk = K // 128
+    sa = np.broadcast_to(np.asarray(sa, np.float32).reshape(-1, 1), (M, nk))
+    sb = np.broadcast_to(np.asarray(sb, np.float32).reshape(-1, 1), (N, nk))
+    return np.ascontiguousarray(sa), np.ascontiguousarray(sb)
+
+
+def gemm_rowscaled(qa, sa, qb, sb, with_abs=True):
+    """GEMM with scales constant along K: Y[m,n] = sa[m] sb[n] sum_k
+    dec(qa[m,k]) dec(qb[n,k]) (sa, sb of length M and N, or 1 for a
+    tensorwise scale).  It is the block-scaled GEMM whose per-slice scales are
+    the same in every slice."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    sae, sbe = expand_rowscales(sa, sb, M, N, K)
+    return gemm_blockscaled(qa, sae, qb, sbe, BSCALE_ROW128, with_abs)
 
 
 def gemm_mx_sampled(qa, sa, qb, sb, mi, ni):

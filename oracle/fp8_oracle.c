@@ -26,6 +26,12 @@
  *    "2. Unified block-wise FP8 (DeepSeek-style)".  Activations use 1x128
  *    groups along the contraction axis; weight-gradient operands use 128x1
  *    groups along the token axis.
+ *  - Per-tensor and per-row (whole-row) groups: the "per-tensor" strategy of
+ *    "Unified FP8: Beyond Mixed Precision...", section "FP8 Quantization",
+ *    and the tensorwise and rowwise scalings that "Towards Full Pipeline FP8
+ *    Reinforcement Learning for LLMs" (agihunt.info) compares with
+ *    blockwise scaling in its accuracy and throughput results.  The same two
+ *    steps, with one group per tensor or per row.
  *  - MXFP8: 32 consecutive E4M3 values share one UE8M0 (power-of-two) scale:
  *    "Low Precision RL", table "Choose a precision" and section
  *    "3. Unified MXFP8 (Blackwell)".  The exponent is the smallest e with
@@ -231,6 +237,47 @@ OR_EXPORT void or_quant_128x128(const uint16_t* x, int64_t rows, int64_t cols, i
                 q[(r0 + i) * cols + c0 + j] = (sc == 0.0f) ? (uint8_t)0 : or_e4m3_encode(v / sc);
             }
     }
+}
+
+/* One group per row (rowwise scaling): q: [rows][cols]; s: [rows]. */
+OR_EXPORT void or_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                uint8_t* q, float* s)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) {
+            float a = fabsf(or_bf16_to_f32(x[r * ld_x + c]));
+            if (a > amax) amax = a;
+        }
+        float sc = amax / 448.0f;
+        s[r] = sc;
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = or_bf16_to_f32(x[r * ld_x + c]);
+            q[r * cols + c] = (sc == 0.0f) ? (uint8_t)0 : or_e4m3_encode(v / sc);
+        }
+    }
+}
+
+/* One group for the whole tensor (tensorwise scaling): q: [rows][cols];
+ * s: one float. */
+OR_EXPORT void or_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                   uint8_t* q, float* s)
+{
+    float amax = 0.0f;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float a = fabsf(or_bf16_to_f32(x[r * ld_x + c]));
+            if (a > amax) amax = a;
+        }
+    float sc = amax / 448.0f;
+    *s = sc;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = or_bf16_to_f32(x[r * ld_x + c]);
+            q[r * cols + c] = (sc == 0.0f) ? (uint8_t)0 : or_e4m3_encode(v / sc);
+        }
 }
 
 /* ------------------------------------------------------------------ */

@@ -151,3 +151,21 @@ def test_silu_mul_vs_torch():
     # gate / up order matters: swapping them changes the result
     swapped = oracle.silu_mul(np.concatenate([gu[:, 128:], gu[:, :128]], axis=1))
     assert not np.array_equal(swapped, h)
+
+
+def test_gemm_rowscaled_vs_numpy():
+    """Scales constant along K (rowwise and tensorwise): fp64 product of the
+    independently decoded operands, each row scaled once."""
+    M, N, K = 40, 96, 384
+    rng = np.random.default_rng(5)
+    xa = inputs.normal_bf16(rng, (M, K), 1.0, 0.01, 30.0)
+    xb = inputs.normal_bf16(rng, (N, K), 0.02)
+    for quant in (oracle.quant_rowwise, oracle.quant_tensorwise):
+        qa, sa = quant(xa)
+        qb, sb = quant(xb)
+        y, yabs = oracle.gemm_rowscaled(qa, sa, qb, sb)
+        A = _dequant_torch(qa) * np.broadcast_to(sa.astype(np.float64).reshape(-1, 1), (M, 1))
+        B = _dequant_torch(qb) * np.broadcast_to(sb.astype(np.float64).reshape(-1, 1), (N, 1))
+        ref = A @ B.T
+        assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(A) @ np.abs(B).T)
+        assert np.allclose(yabs, np.abs(A) @ np.abs(B).T, rtol=1e-12, atol=0)

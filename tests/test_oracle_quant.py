@@ -202,3 +202,61 @@ def test_mx_amax_code_range():
     idx = np.abs(xf).argmax(axis=2)
     picked = np.take_along_axis(q.reshape(32, 16, 32), idx[:, :, None], axis=2)[:, :, 0] & 0x7F
     assert np.all((picked >= 0x76) & (picked <= 0x7E))
+
+
+# ----------------------------------------------------- rowwise / tensorwise
+# One group per row or per tensor: the per-tensor strategy of "Unified FP8:
+# Beyond Mixed Precision..." (section "FP8 Quantization") and the tensorwise
+# and rowwise scalings compared in "Towards Full Pipeline FP8 Reinforcement
+# Learning for LLMs".
+
+@pytest.mark.parametrize("shape", [(5, 300), (16, 2560), (3, 9728), (1, 8)])
+def test_rowwise_matches_independent(shape):
+    """Each row is one 1xcols group: the numpy/torch re-derivation with the
+    group as wide as the row."""
+    x = _rand_bits(shape, 20)
+    q, s = oracle.quant_rowwise(x)
+    q2, s2 = independent_rowblock(x, group=shape[1])
+    assert np.array_equal(s.view(np.uint32), s2[:, 0].view(np.uint32))
+    assert np.array_equal(q, q2)
+
+
+def test_rowwise_on_128_columns_is_1x128():
+    x = _rand_bits((40, 128), 21)
+    q, s = oracle.quant_rowwise(x)
+    q2, s2 = oracle.quant_1x128(x)
+    assert np.array_equal(q, q2) and np.array_equal(s.view(np.uint32), s2[:, 0].view(np.uint32))
+
+
+def test_tensorwise_on_one_block_is_128x128():
+    x = _rand_bits((128, 128), 22)
+    q, s = oracle.quant_tensorwise(x)
+    q2, s2 = oracle.quant_128x128(x)
+    assert np.array_equal(q, q2) and s[0].view(np.uint32) == s2[0, 0].view(np.uint32)
+
+
+def test_tensorwise_matches_independent():
+    """S = max|x| / 448 over the whole tensor (fp32), codes E4M3(x / S)."""
+    x = _rand_bits((300, 520), 23)
+    q, s = oracle.quant_tensorwise(x)
+    xf = _f32(x)
+    sc = np.float32(np.float32(np.abs(xf).max()) / np.float32(448.0))
+    assert s[0].view(np.uint32) == sc.view(np.uint32)
+    assert np.array_equal(q, _torch_e4m3((xf / sc).astype(np.float32)))
+    # the amax element of the tensor lands on +-448, and every element obeys
+    # the dequantization bound
+    i = np.unravel_index(np.abs(xf).argmax(), xf.shape)
+    assert q[i] in (0x7E, 0xFE)
+    r = np.abs(xf.astype(np.float64) / np.float64(sc))
+    e = np.floor(np.log2(np.maximum(r, 2.0 ** -9)))
+    ulp = np.exp2(np.maximum(e, -6) - 3)
+    deq = oracle.e4m3_decode(q) * np.float64(sc)
+    assert np.all(np.abs(deq - xf) <= sc * (ulp / 2 + 2.0 ** -24 * r) * (1 + 1e-12))
+
+
+def test_rowwise_and_tensorwise_zero_input():
+    x = np.zeros((3, 64), np.uint16)
+    q, s = oracle.quant_rowwise(x)
+    assert np.all(q == 0) and np.all(s == 0)
+    q, s = oracle.quant_tensorwise(x)
+    assert np.all(q == 0) and s[0] == 0
