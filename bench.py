@@ -42,7 +42,7 @@ PEAK_FP8_TFLOPS = 5030.0     # 256 CUs x 2.4 GHz x 8192 dense FP8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 M_TOK, HID, INTER = 4096, 2560, 9728
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
-WORKLOADS = ("tiny_linear", "mlp_backward", "moe_blockwise", "moe_mxfp8")
+WORKLOADS = ("tiny_linear", "mlp_backward", "moe_blockwise", "moe_mxfp8", "up_proj_rowwise")
 
 
 def parse():
@@ -86,12 +86,19 @@ def kernel_entry(unit, amount, ms):
     return {"ms": round(ms, 5), unit: round(r, 2), "frac_of_peak": round(f, 4)}
 
 
-def time_sequence(torch, stream, launches, reps, warmup):
-    """Run the list of launches `warmup` + `reps` times, each launch bracketed
-    by events; returns the per-launch median ms."""
-    for i in range(warmup):
+def time_sequence(torch, stream, launches, reps, warmup, warm_ms=60.0):
+    """Run the list of launches at least `warmup` times and for at least
+    `warm_ms` of wall time (the shader clock settles under sustained load),
+    then `reps` times with each launch bracketed by events; returns the
+    per-launch median ms."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
         for fn in launches:
             fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(reps)]
     for i in range(reps):
@@ -161,6 +168,31 @@ def wl_mlp_backward(torch, ops, inputs, to_dev, R):
                                                               ops.BSCALE_ROW128, dw, I, ops.OUT_FP32),
          ("TFLOP/s", 2.0 * O * I * T)),
     ], {"workload": "mlp_backward", "tokens": T, "hidden": I, "intermediate": O, "seeds": [1, 2]}
+
+
+def wl_up_proj_rowwise(torch, ops, inputs, to_dev, R):
+    """The up projection of the headline step with rowwise and tensorwise
+    scales instead of 1x128 / 128x128 blocks."""
+    d = inputs.qwen3_4b_mlp(1)
+    M, K, N = M_TOK, HID, INTER
+    xs = [to_dev(d["x_up"]) for _ in range(R)]
+    w = to_dev(d["w_up"])
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+    qx, sx, qw, sw, st = u8(M, K), f32(M), u8(N, K), f32(N), f32(1)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    return [
+        ("quant_x_rowwise", lambda i: ops.fp8_quant_rowwise(xs[i % R], M, K, K, qx, K, sx),
+         ("GB/s", qbytes_row(M, K, group=K))),
+        ("quant_x_tensorwise", lambda i: ops.fp8_quant_tensorwise(xs[i % R], M, K, K, qx, K, st),
+         ("GB/s", M * K * 3 + 4)),
+        ("quant_w_rowwise", lambda i: ops.fp8_quant_rowwise(w, N, K, K, qw, K, sw),
+         ("GB/s", qbytes_row(N, K, group=K))),
+        # scales constant along K: views of K stride 0
+        ("gemm_rowscaled_bf16", lambda i: ops.fp8_blockscaled_gemm(M, N, K, qx, K, sx, 1, 0, qw, K, sw, 1, 0,
+                                                                  ops.BSCALE_ROW128, y, N, ops.OUT_BF16),
+         ("TFLOP/s", 2.0 * M * N * K)),
+    ], {"workload": "up_proj_rowwise", "tokens": M, "in": K, "out": N, "seed": 1}
 
 
 def _moe_inputs(inputs, cache={}):
@@ -423,7 +455,7 @@ def main():
     # ------------------------------------------------- the other workloads
     wanted = [w for w in args.workloads.split(",") if w and w != "none"]
     table = {"tiny_linear": wl_tiny_linear, "mlp_backward": wl_mlp_backward,
-             "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8}
+             "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8, "up_proj_rowwise": wl_up_proj_rowwise}
     others = {}
     for wname in wanted:
         if wname not in table:

@@ -104,6 +104,40 @@ fp8bs_status fp8_quant_rowblock(const uint16_t* x, int64_t rows, int64_t cols, i
                     "fp8_quant_rowblock");
 }
 
+fp8bs_status fp8_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                               float* s, hipStream_t stream) {
+    if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    if (cols % 8) return fail(FP8BS_ERR_SHAPE, "cols %% 8 != 0 (cols=%lld)", (long long)cols);
+    if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2) return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0) return ok();
+    if (!x || !q || !s) return fail(FP8BS_ERR_NULL, "x, q and s are required");
+    if (ld_x < cols || ld_q < cols) return fail(FP8BS_ERR_STRIDE, "ld_x and ld_q must be >= cols");
+    if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    if (!aligned(s, 4)) return fail(FP8BS_ERR_ALIGN, "s must be 4-byte aligned");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_quant_rowwise(x, rows, cols, ld_x, q, ld_q, s, stream), "fp8_quant_rowwise");
+}
+
+fp8bs_status fp8_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                  int64_t ld_q, float* s, hipStream_t stream) {
+    if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    if (cols % 8) return fail(FP8BS_ERR_SHAPE, "cols %% 8 != 0 (cols=%lld)", (long long)cols);
+    if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2) return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (!s) return fail(FP8BS_ERR_NULL, "s is required");
+    if (!aligned(s, 4)) return fail(FP8BS_ERR_ALIGN, "s must be 4-byte aligned");
+    if (rows > 0 && cols > 0) {
+        if (!x || !q) return fail(FP8BS_ERR_NULL, "x and q are required");
+        if (ld_x < cols || ld_q < cols) return fail(FP8BS_ERR_STRIDE, "ld_x and ld_q must be >= cols");
+        if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+        if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    }
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_quant_tensorwise(x, rows, cols, ld_x, q, ld_q, s, stream), "fp8_quant_tensorwise");
+}
+
 fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, int64_t cols, int64_t ld_w,
                                uint8_t* q, int64_t ld_q, uint8_t* q_t, int64_t ld_qt, float* s, hipStream_t stream) {
     if (batch < 1 || rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "batch=%lld rows=%lld cols=%lld",

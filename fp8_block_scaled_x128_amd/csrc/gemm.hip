@@ -111,7 +111,10 @@ struct Cfg {
     static_assert(kLeadB != 1 || kDmaB <= NF, "one weight copy per n-tile step");
 };
 
-enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2 };
+// MODE_KINV: scales constant along K (rowwise / tensorwise scaling); the
+// matrix unit accumulates the whole contraction with unit scales and the
+// epilogue multiplies each output by sa(m) * sb(n).
+enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2, MODE_KINV = 3 };
 
 struct KArgs {
     int32_t M, N, K;
@@ -121,6 +124,7 @@ struct KArgs {
     const uint8_t* sb; int64_t sb_sg, sb_sn, sb_sk;
     void* c; int64_t ldc;
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
+    int32_t kinv_row;                          // MODE_KINV: sb indexed by n (1) or n / 128 (0)
 };
 
 __device__ __forceinline__ int swz(int r) { return r & 7; }
@@ -218,7 +222,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     using C = Cfg<WAVES, NF>;
     constexpr int BM = C::BM, BN = C::BN;
     // per-row weight scales are copied by waves 0..3 in 64-row pieces
-    static_assert(MODE == MODE_BLOCK128 || NF == 8, "ROW128 and MX modes use 256-row weight tiles");
+    static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || NF == 8, "ROW128 and MX modes use 256-row weight tiles");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
     __shared__ int s_tile[3];
 
@@ -341,8 +345,8 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     // Scale copies (4-byte lanes).  Activation scales: waves [0, BM/64) copy
     // rows [64 w, +64).  Weight scales: MODE_BLOCK128 -> wave BM/64 copies the
     // two 128-row blocks of the tile; ROW128 / MX -> waves 0..3 copy rows [64 w, +64).
-    const bool has_sa = wave < BM / 64;
-    const bool has_sb = (MODE == MODE_BLOCK128) ? wave == BM / 64 : wave < 4;
+    const bool has_sa = MODE != MODE_KINV && wave < BM / 64;
+    const bool has_sb = MODE != MODE_KINV && ((MODE == MODE_BLOCK128) ? wave == BM / 64 : wave < 4);
     uint32_t sa_off = 0, sb_off = 0;            // byte offsets without the slice term (< 4 GiB)
     if (has_sa) {
         const int m = arow(wave * 64 + lane);
@@ -351,7 +355,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     if (MODE == MODE_BLOCK128) {
         const int nb = min(n0 / 128 + (lane & 1), (p.N - 1) / 128);
         sb_off = (uint32_t)((int64_t)nb * p.sb_sn * 4);
-    } else {
+    } else if (MODE != MODE_KINV) {
         const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
         sb_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4);
     }
@@ -451,6 +455,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
+            else if (MODE == MODE_KINV) mxa[mt] = kE8M0One;
             else sam[mt] = lds_readf(sa_lds + mt * 64);
         }
         if (C::kABarrier) {
@@ -471,13 +476,13 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
                 if (CB && C::b_slot(t) == nt) copy_b(b_kb, cst, t);
         };
 
-        if (MODE == MODE_MX) {
+        if (MODE == MODE_MX || MODE == MODE_KINV) {
             const uint32_t sb8 = opaque(tB + BN * BK + (wn * 16 * NF + r16) * 4 + q);
             const FragOff bb = frag_base(tB + wn * 16 * NF * BK, fo);
 #pragma unroll
             for (int nt = 0; nt < NF; ++nt) {
                 const v8i fb = read_frag(bb, nt * 16 * BK);
-                const int mxb = lds_readu8(sb8 + nt * 64);
+                const int mxb = MODE == MODE_KINV ? kE8M0One : lds_readu8(sb8 + nt * 64);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
                     acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[mt], acc[nt][mt], 0, 0, 0,
@@ -573,6 +578,24 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     // One base address per m-tile, the n-tiles at constant offsets from it.
     const int nw0 = n0 + wn * 16 * NF;
     if (nw0 >= p.N) return;
+    if (MODE == MODE_KINV) {
+        // scales constant along K: each output times sa(m) * sb(n), once
+        const float* sa = reinterpret_cast<const float*>(p.sa);
+        const float* sb = reinterpret_cast<const float*>(p.sb);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int m = min(m_begin + wm * 64 + mt * 16 + r16, m_end - 1);
+            const float sam = sa[(int64_t)m * p.sa_sm];
+#pragma unroll
+            for (int nt = 0; nt < NF; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = min(nw0 + nt * 16 + 4 * q + r, p.N - 1);
+                    const float sbn = sb[(int64_t)(p.kinv_row ? n : n / 128) * p.sb_sn];
+                    acc[nt][mt][r] *= sam * sbn;
+                }
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int m = m_begin + wm * 64 + mt * 16 + r16;
@@ -679,12 +702,13 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K) {
     return best;
 }
 
+template <int MODE>
 hipError_t launch_dense(int ci, const KArgs& p, bool out_f32, hipStream_t st) {
     switch (ci) {
-        case 0: return launch<MODE_BLOCK128, false, 8, 8>(p, out_f32, st);
-        case 1: return launch<MODE_BLOCK128, false, 4, 8>(p, out_f32, st);
-        case 2: return launch<MODE_BLOCK128, false, 8, 5>(p, out_f32, st);
-        default: return launch<MODE_BLOCK128, false, 4, 6>(p, out_f32, st);
+        case 0: return launch<MODE, false, 8, 8>(p, out_f32, st);
+        case 1: return launch<MODE, false, 4, 8>(p, out_f32, st);
+        case 2: return launch<MODE, false, 8, 5>(p, out_f32, st);
+        default: return launch<MODE, false, 4, 6>(p, out_f32, st);
     }
 }
 
@@ -704,20 +728,26 @@ hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
     KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
     p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
-    if (g.bscale_row)
+    // scales constant along K: accumulate in the matrix unit, scale once
+    const bool kinv = g.sa_sk == 0 && g.sb_sk == 0;
+    p.kinv_row = g.bscale_row ? 1 : 0;
+    auto go = [&](int ci, const KArgs& q) {
+        return kinv ? launch_dense<MODE_KINV>(ci, q, g.out_f32, st) : launch_dense<MODE_BLOCK128>(ci, q, g.out_f32, st);
+    };
+    if (g.bscale_row && !kinv)
         return waves_for(g.M, g.N) == 8 ? launch<MODE_ROW128, false, 8, 8>(p, g.out_f32, st)
                                         : launch<MODE_ROW128, false, 4, 8>(p, g.out_f32, st);
     const DensePlan plan = plan_dense(g.M, g.N, g.K);
-    if (plan.c2 < 0) return launch_dense(plan.c1, p, g.out_f32, st);
+    if (plan.c2 < 0) return go(plan.c1, p);
     KArgs p1 = p, p2 = p;
     p1.N = (int32_t)plan.split;
     p2.N = (int32_t)(g.N - plan.split);
     p2.b = p.b + plan.split * p.ldb;
-    p2.sb = p.sb + (plan.split / 128) * p.sb_sn * 4;
+    p2.sb = p.sb + (g.bscale_row ? plan.split : plan.split / 128) * p.sb_sn * 4;
     p2.c = static_cast<uint8_t*>(p.c) + plan.split * (g.out_f32 ? 4 : 2);
-    const hipError_t e = launch_dense(plan.c1, p1, g.out_f32, st);
+    const hipError_t e = go(plan.c1, p1);
     if (e != hipSuccess) return e;
-    return launch_dense(plan.c2, p2, g.out_f32, st);
+    return go(plan.c2, p2);
 }
 
 void plan_gemm_blockscaled(int64_t M, int64_t N, int64_t K, int32_t out[5]) {

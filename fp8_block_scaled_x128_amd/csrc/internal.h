@@ -18,6 +18,10 @@ hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_
 hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t rows, int64_t I, int64_t ld_in, int mx, uint8_t* q,
                                  int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint16_t* h, int64_t ld_h,
                                  hipStream_t st);
+hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                                float* s, hipStream_t st);
+hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                   int64_t ld_q, float* s, hipStream_t st);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st);
 
 // gemm.hip

@@ -374,6 +374,88 @@ __global__ void __launch_bounds__(kThreads) k_e4m3_encode(const float* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Rowwise and tensorwise scaling: one group per row or per tensor (the same
+// two steps).  Rowwise: one workgroup per row; the maximum is reduced over
+// the row's 16-byte chunks, then the chunks are read again (from L2) and
+// encoded.  Tensorwise: a fill kernel zeroes s[0], every workgroup folds its
+// chunk maximum into s[0] with an atomic max on the fp32 bits (non-negative
+// floats order like their bit patterns), the encode kernel reads the maximum,
+// and a last one-thread kernel replaces it by the scale max / 448.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_max(float m, float* red) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, red[i]);
+    return m;
+}
+
+__global__ void __launch_bounds__(kThreads) k_quant_rowwise(const uint16_t* __restrict__ x, int32_t cols, int64_t ld_x,
+                                                            uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s) {
+    __shared__ float red[kThreads / 64];
+    const int64_t r = blockIdx.x;
+    const uint16_t* xr = x + r * ld_x;
+    uint8_t* qr = q + r * ld_q;
+    const int nch = cols / 8;
+    float m = 0.0f;
+    for (int c = threadIdx.x; c < nch; c += kThreads) {
+        float v[8];
+        unpack8(*reinterpret_cast<const uint4*>(xr + 8 * c), v);
+        m = fmaxf(m, absmax8(v));
+    }
+    m = block_max(m, red);
+    const float sc = m / kE4M3Max;
+    for (int c = threadIdx.x; c < nch; c += kThreads) {
+        float v[8];
+        unpack8(*reinterpret_cast<const uint4*>(xr + 8 * c), v);
+        uint32_t w0, w1;
+        encode8(v, sc, w0, w1);
+        *reinterpret_cast<uint2*>(qr + 8 * c) = make_uint2(w0, w1);
+    }
+    if (threadIdx.x == 0) s[r] = sc;
+}
+
+__global__ void k_fill_zero(float* s) { s[0] = 0.0f; }
+
+__global__ void __launch_bounds__(kThreads) k_tensor_amax(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
+                                                          int64_t ld_x, float* s) {
+    __shared__ float red[kThreads / 64];
+    const int nch = cols / 8;
+    const int64_t total = (int64_t)rows * nch;
+    float m = 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = i / nch, c = i - r * nch;
+        float v[8];
+        unpack8(*reinterpret_cast<const uint4*>(x + r * ld_x + 8 * c), v);
+        m = fmaxf(m, absmax8(v));
+    }
+    m = block_max(m, red);
+    // fl(m / 448) is monotone in m, so the maximum of the blocks' scales is
+    // the scale of the tensor's amax; non-negative floats order as their bits
+    if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(s), __float_as_uint(m / kE4M3Max));
+}
+
+__global__ void __launch_bounds__(kThreads) k_tensor_encode(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
+                                                            int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
+                                                            const float* s) {
+    const float sc = s[0];
+    const int nch = cols / 8;
+    const int64_t total = (int64_t)rows * nch;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = i / nch, c = i - r * nch;
+        float v[8];
+        unpack8(*reinterpret_cast<const uint4*>(x + r * ld_x + 8 * c), v);
+        uint32_t w0, w1;
+        encode8(v, sc, w0, w1);
+        *reinterpret_cast<uint2*>(q + r * ld_q + 8 * c) = make_uint2(w0, w1);
+    }
+}
+
+
 }  // namespace
 
 hipError_t launch_quant_1x128(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
@@ -438,6 +520,31 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, 
         if (nt) go(std::false_type{}, std::true_type{});
         else go(std::false_type{}, std::false_type{});
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
+                                float* s, hipStream_t st) {
+    if (rows == 0) return hipSuccess;                 // cols == 0: every scale 0
+    hipLaunchKernelGGL(k_quant_rowwise, dim3((unsigned)rows), dim3(kThreads), 0, st, x, (int32_t)cols, ld_x, q, ld_q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                   int64_t ld_q, float* s, hipStream_t st) {
+    if (rows == 0 || cols == 0) {
+        hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(1), 0, st, s);
+        return hipGetLastError();
+    }
+    const int64_t chunks = rows * (cols / 8);
+    int64_t blocks = (chunks + kThreads * 4 - 1) / (kThreads * 4);
+    if (blocks > 256 * 8) blocks = 256 * 8;
+    hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(1), 0, st, s);
+    hipLaunchKernelGGL(k_tensor_amax, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, s);
+    int64_t eblocks = (chunks + kThreads - 1) / kThreads;
+    if (eblocks > 256 * 64) eblocks = 256 * 64;
+    hipLaunchKernelGGL(k_tensor_encode, dim3((unsigned)eblocks), dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols,
+                       ld_x, q, ld_q, (const float*)s);
     return hipGetLastError();
 }
 

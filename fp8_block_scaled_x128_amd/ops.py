@@ -24,7 +24,7 @@ AXIS_ROW, AXIS_COL = 0, 1
 OUT_BF16, OUT_FP32 = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
-EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
+EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
            "fp8_grouped_gemm",
            "fp8_silu_mul_quant", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
@@ -55,6 +55,8 @@ def load():
         sig = {
             "fp8_quant_rowblock": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P],
             "fp8_quant_block2d": [P, I64, I64, I64, I64, P, I64, P, I64, P, P],
+            "fp8_quant_rowwise": [P, I64, I64, I64, P, I64, P, P],
+            "fp8_quant_tensorwise": [P, I64, I64, I64, P, I64, P, P],
             "fp8_blockscaled_gemm": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P, I64, INT, P],
             "fp8_blockscaled_gemm_plan": [I64, I64, I64, P],
             "fp8_grouped_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64,
@@ -111,6 +113,16 @@ def fp8_quant_block2d(w, batch, rows, cols, ld_w, q, ld_q, q_t, ld_qt, s, stream
     st = load().fp8_quant_block2d(_p(w), batch, rows, cols, ld_w, _p(q), ld_q, _p(q_t), ld_qt, _p(s),
                                   _stream(stream))
     return _check("fp8_quant_block2d", st, raise_on_error)
+
+
+def fp8_quant_rowwise(x, rows, cols, ld_x, q, ld_q, s, stream=None, raise_on_error=True):
+    st = load().fp8_quant_rowwise(_p(x), rows, cols, ld_x, _p(q), ld_q, _p(s), _stream(stream))
+    return _check("fp8_quant_rowwise", st, raise_on_error)
+
+
+def fp8_quant_tensorwise(x, rows, cols, ld_x, q, ld_q, s, stream=None, raise_on_error=True):
+    st = load().fp8_quant_tensorwise(_p(x), rows, cols, ld_x, _p(q), ld_q, _p(s), _stream(stream))
+    return _check("fp8_quant_tensorwise", st, raise_on_error)
 
 
 def fp8_blockscaled_gemm(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, sb, sb_stride_n, sb_stride_k,
@@ -207,6 +219,35 @@ def quant_block2d(w: torch.Tensor, transposed: bool = False):
         q, s = q[0], s[0]
         qt = qt[0] if qt is not None else None
     return q, s, qt
+
+
+def quant_rowwise(x: torch.Tensor):
+    """One scale per row of a bf16 [rows, cols] tensor -> (q, s [rows])."""
+    rows, cols = x.shape
+    q = _u8((rows, cols), x.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    fp8_quant_rowwise(x, rows, cols, x.stride(0), q, cols, s)
+    return q, s
+
+
+def quant_tensorwise(x: torch.Tensor):
+    """One scale for a whole bf16 [rows, cols] tensor -> (q, s [1])."""
+    rows, cols = x.shape
+    q = _u8((rows, cols), x.device)
+    s = torch.empty((1,), dtype=torch.float32, device=x.device)
+    fp8_quant_tensorwise(x, rows, cols, x.stride(0), q, cols, s)
+    return q, s
+
+
+def gemm_rowscaled(a, sa, b, sb, out_dtype=torch.bfloat16):
+    """C = diag(sa) (A B^T) diag(sb) for codes a [M, K], b [N, K] and scales
+    sa [M] or [1], sb [N] or [1] (rowwise or tensorwise): the block-scaled GEMM
+    with scale views of K stride 0."""
+    M, K = a.shape
+    N = b.shape[0]
+    sa_v = sa.view(-1, 1).expand(M, K // 128)
+    sb_v = sb.view(-1, 1).expand(N, K // 128)
+    return gemm(a, sa_v, b, sb_v, bscale=BSCALE_ROW128, out_dtype=out_dtype)
 
 
 def gemm(a, sa, b, sb, bscale=BSCALE_BLOCK128, out_dtype=torch.bfloat16):

@@ -96,6 +96,32 @@ fp8bs_status fp8_quant_rowblock(const uint16_t* x, int64_t rows, int64_t cols, i
                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_quant_rowwise / fp8_quant_tensorwise -- one group per row, or one group
+ * for the whole tensor: the coarser granularities named next to the
+ * block-wise one ("per-tensor" in "Unified FP8: Beyond Mixed Precision...",
+ * section "FP8 Quantization"; the tensorwise and rowwise scalings compared
+ * with blockwise in "Towards Full Pipeline FP8 Reinforcement Learning for
+ * LLMs").  The same two steps: S = max|x| / 448 over the group (fp32 IEEE
+ * division), codes E4M3(x / S) (RNE, saturating); an all-zero group has
+ * S = 0 and codes 0x00.
+ *
+ * x : bf16 [rows][ld_x];  q : [rows][ld_q] codes.
+ * s : rowwise: fp32 [rows], s[r] the scale of row r;
+ *     tensorwise: fp32 [1] (it holds the running maximum of the per-block
+ *     scales while the call's kernels run, the tensor's scale when they end:
+ *     fl(m / 448) is monotone in m).
+ * Requirements: rows, cols >= 0; cols % 8 == 0; x 16-byte aligned with
+ * ld_x % 8 == 0, ld_x >= cols; q 8-byte aligned with ld_q % 8 == 0,
+ * ld_q >= cols.  The GEMM takes these scales as scales constant along K:
+ * sa_stride_k = sb_stride_k = 0 in fp8_blockscaled_gemm (and
+ * sa_stride_m = 0 or sb_stride_n = 0 for a tensorwise operand).
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                               uint8_t* q, int64_t ld_q, float* s, hipStream_t stream);
+fp8bs_status fp8_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint8_t* q, int64_t ld_q, float* s, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_quant_block2d -- 128x128 block quantization of `batch` matrices
  * (weights: "Low Precision RL", table "Choose a precision" and section
  * "2. Unified block-wise FP8 (DeepSeek-style)").
@@ -130,6 +156,11 @@ fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, i
  *      The data-gradient GEMM dX = dY W reads W through the transposed copy
  *      q_t of fp8_quant_block2d and W's scales with the two strides swapped.
  * c  : [M][ldc] bf16 (round to nearest even) or fp32, per `out`.
+ * Scales constant along K (sa_stride_k == 0 and sb_stride_k == 0: the
+ * rowwise and tensorwise scalings of fp8_quant_rowwise/_tensorwise, or any
+ * other K-invariant scale) take a path on which the matrix unit accumulates
+ * the whole contraction and sa * sb multiplies each output once; with the
+ * same product in every slice this is the formula above.
  * Requirements: M, N >= 0; K % 128 == 0; N % 128 == 0; lda >= K, ldb >= K,
  * lda % 16 == 0, ldb % 16 == 0, a and b 16-byte aligned; ldc >= N.
  * ------------------------------------------------------------------------ */

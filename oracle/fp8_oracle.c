@@ -41,7 +41,7 @@
  *    The pages require the trainer and rollout forward GEMMs to consume the
  *    same quantized operands ("Low Precision RL", "Unified training recipe").
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - an all-zero group has S = 0 and every code 0x00 (also -0 inputs);
  *  - the division x/S is one IEEE fp32 division, then one E4M3 rounding;
  *  - a group that extends past the end of a row/column covers only the
