@@ -73,6 +73,12 @@ def qbytes_block2d(batch, rows, cols, transposed=False):
     return batch * (rows * cols * (4 if transposed else 3) + ((rows + 127) // 128) * ((cols + 127) // 128) * 4)
 
 
+def combine_bytes(rows, H, T, k):
+    """MoE combine: every grouped row read once (bf16), one bf16 row written
+    per token, and the token's k positions and weights."""
+    return rows * H * 2 + T * H * 2 + T * k * 8
+
+
 def rate(unit, amount, ms):
     if unit == "TFLOP/s":
         r = amount / (ms * 1e-3) / 1e12
@@ -220,6 +226,9 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R):
     gu = torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
     qh, sh = u8(rows, I), f32(I // 128, rows)
     y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    pos, wts = torch.from_numpy(r.token_rows).cuda(), torch.from_numpy(r.weights).cuda()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    k = r.token_rows.shape[1]
     n_gu = 2.0 * rows * N2 * H
     n_dn = 2.0 * rows * H * I
     return [
@@ -238,6 +247,8 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R):
         ("grouped_gemm_down", lambda i: ops.fp8_grouped_gemm(
             rows, H, I, G, offs, None, rows, qh, I, sh, 1, rows, qdt, I, H * I, sd, (I // 128) * (H // 128),
             1, H // 128, y, H, ops.OUT_BF16), ("TFLOP/s", n_dn)),
+        ("combine", lambda i: ops.fp8_moe_combine(y, rows, H, H, pos, wts, T, k, out, H, ops.OUT_BF16),
+         ("GB/s", combine_bytes(rows, H, T, k))),
     ], {"workload": "moe_blockwise", "tokens": T, "hidden": H, "experts": E, "intermediate": I, "top_k": 8,
         "grouped_rows": rows, "seed": 3}
 
@@ -261,6 +272,9 @@ def wl_moe_mxfp8(torch, ops, inputs, to_dev, R):
     gu = torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
     qh, sh = u8(rows, I), u8(rows, I // 32)
     y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    pos, wts = torch.from_numpy(r.token_rows).cuda(), torch.from_numpy(r.weights).cuda()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    k = r.token_rows.shape[1]
     return [
         ("mx_quant_x", lambda i: ops.mxfp8_quant(xs[i % R], T, H, H, qx, H, sx, H // 32, 1),
          ("GB/s", qbytes_row(T, H, 32, 1))),
@@ -276,6 +290,8 @@ def wl_moe_mxfp8(torch, ops, inputs, to_dev, R):
         ("mx_grouped_gemm_down", lambda i: ops.mxfp8_gemm(
             rows, H, I, G, offs, None, rows, qh, I, sh, I // 32, qdt, I, H * I, sdt, I // 32, H * (I // 32),
             y, H, ops.OUT_BF16), ("TFLOP/s", 2.0 * rows * H * I)),
+        ("combine", lambda i: ops.fp8_moe_combine(y, rows, H, H, pos, wts, T, k, out, H, ops.OUT_BF16),
+         ("GB/s", combine_bytes(rows, H, T, k))),
     ], {"workload": "moe_mxfp8", "tokens": T, "hidden": H, "experts": E, "intermediate": I, "top_k": 8,
         "grouped_rows": rows, "seed": 3}
 

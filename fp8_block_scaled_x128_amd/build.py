@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8bs.so")
-SOURCES = ["quant.hip", "gemm.hip", "capi.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "capi.hip"]
 # The GEMM promotes MFMA results with VALU FMAs, so the results must land in
 # VGPRs (not AGPRs, which would need a v_accvgpr_read per value).
 EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

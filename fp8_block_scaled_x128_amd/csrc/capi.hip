@@ -279,6 +279,29 @@ fp8bs_status fp8_silu_mul_quant(const uint16_t* gate_up, int64_t rows, int64_t I
                     "fp8_silu_mul_quant");
 }
 
+fp8bs_status fp8_moe_combine(const uint16_t* y, int64_t rows, int64_t H, int64_t ld_y, const int32_t* token_rows,
+                             const float* weights, int64_t T, int32_t k, void* out, int64_t ld_out, fp8bs_out out_type,
+                             hipStream_t stream) {
+    if (out_type != FP8BS_OUT_BF16 && out_type != FP8BS_OUT_FP32) return fail(FP8BS_ERR_UNSUPPORTED, "out %d", out_type);
+    if (rows < 0 || H < 0 || T < 0 || k < 1) return fail(FP8BS_ERR_SHAPE, "rows, H, T >= 0 and k >= 1 required");
+    if (H % 8) return fail(FP8BS_ERR_SHAPE, "H %% 8 != 0 (H=%lld)", (long long)H);
+    // one work-item per (token, 8-column chunk), all in grid dimension x
+    if (rows > INT32_MAX || H > INT32_MAX / 2 || T > INT32_MAX / 2 || T * (H / 8) > (1ll << 31))
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (T == 0 || H == 0) return ok();
+    if (rows == 0) return fail(FP8BS_ERR_SHAPE, "rows == 0 with T > 0");
+    if (!y || !token_rows || !weights || !out) return fail(FP8BS_ERR_NULL, "y, token_rows, weights and out are required");
+    if (ld_y < H || ld_out < H) return fail(FP8BS_ERR_STRIDE, "ld_y and ld_out must be >= H");
+    if (ld_y % 8 || !aligned(y, 16)) return fail(FP8BS_ERR_ALIGN, "y must be 16-byte aligned with ld_y %% 8 == 0");
+    if (ld_out % 8 || !aligned(out, 16)) return fail(FP8BS_ERR_ALIGN, "out must be 16-byte aligned with ld_out %% 8 == 0");
+    if (!aligned(token_rows, 4) || !aligned(weights, 4)) return fail(FP8BS_ERR_ALIGN, "token_rows, weights misaligned");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_moe_combine(y, rows, H, ld_y, token_rows, weights, T, k, out, ld_out,
+                                       out_type == FP8BS_OUT_FP32, stream),
+                    "fp8_moe_combine");
+}
+
 fp8bs_status mxfp8_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
                          uint8_t* s, int64_t s_stride_row, int64_t s_stride_group, hipStream_t stream) {
     if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "negative size");

@@ -24,6 +24,11 @@ hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols
                                    int64_t ld_q, float* s, hipStream_t st);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st);
 
+// moe.hip
+hipError_t launch_moe_combine(const uint16_t* y, int64_t rows, int64_t H, int64_t ld_y, const int32_t* pos,
+                              const float* w, int64_t T, int32_t k, void* out, int64_t ld_out, int out_f32,
+                              hipStream_t st);
+
 // gemm.hip
 struct GemmArgs {
     int64_t M, N, K;                 // M = total rows (grouped: rows of all groups)

@@ -100,12 +100,17 @@ class MoERouting:
     row_token: np.ndarray        # int32 [tokens * top_k]
     topk_experts: np.ndarray     # int32 [tokens, top_k]
     counts: np.ndarray = field(default=None)
+    token_rows: np.ndarray = field(default=None)   # int32 [tokens, top_k]: grouped row of (token, slot)
+    weights: np.ndarray = field(default=None)      # float32 [tokens, top_k]: routing weights
 
 
 def route_topk(logits: np.ndarray, top_k: int) -> MoERouting:
     """Top-k experts per token by router logit (the softmax is monotone, so
     ranking logits ranks probabilities); ties go to the lower expert index.
-    Assignments are then stably sorted by (expert, token)."""
+    Assignments are then stably sorted by (expert, token).  The routing
+    weights are the softmax of the token's selected logits in float32 (the
+    router's probabilities renormalized over the top k); they are inputs of
+    the combine, computed here like any other synthetic input."""
     T, G = logits.shape
     order = np.argsort(-logits, axis=1, kind="stable")[:, :top_k].astype(np.int32)
     experts = order.reshape(-1)
@@ -114,8 +119,14 @@ def route_topk(logits: np.ndarray, top_k: int) -> MoERouting:
     counts = np.bincount(experts, minlength=G).astype(np.int64)
     offsets = np.zeros(G + 1, np.int32)
     offsets[1:] = np.cumsum(counts)
+    token_rows = np.empty(T * top_k, np.int32)
+    token_rows[perm] = np.arange(T * top_k, dtype=np.int32)
+    sel = np.take_along_axis(logits, order, axis=1).astype(np.float32)
+    e = np.exp(sel - sel[:, :1])                    # order[:, 0] holds the largest logit
+    weights = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
     return MoERouting(offsets=offsets, row_token=tokens[perm].astype(np.int32),
-                      topk_experts=order, counts=counts)
+                      topk_experts=order, counts=counts, token_rows=token_rows.reshape(T, top_k),
+                      weights=weights)
 
 
 def qwen3_30b_a3b_moe(seed: int = 3, tokens: int = 16384, hidden: int = 2048, experts: int = 128,

@@ -26,7 +26,7 @@ BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
 EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
            "fp8_grouped_gemm",
-           "fp8_silu_mul_quant", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
+           "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
 
 
@@ -62,6 +62,7 @@ def load():
             "fp8_grouped_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64,
                                  P, I64, INT, P],
             "fp8_silu_mul_quant": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P, I64, P],
+            "fp8_moe_combine": [P, I64, I64, I64, P, P, I64, I32, P, I64, INT, P],
             "mxfp8_quant": [P, I64, I64, I64, P, I64, P, I64, I64, P],
             "mxfp8_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, INT, P],
             "fp8bs_e4m3_encode": [P, P, I64, P],
@@ -154,6 +155,13 @@ def fp8_silu_mul_quant(gate_up, rows, I, ld_in, mx, q, ld_q, s, s_stride_row, s_
     st = load().fp8_silu_mul_quant(_p(gate_up), rows, I, ld_in, mx, _p(q), ld_q, _p(s), s_stride_row,
                                    s_stride_group, _p(h_out), ld_h, _stream(stream))
     return _check("fp8_silu_mul_quant", st, raise_on_error)
+
+
+def fp8_moe_combine(y, rows, H, ld_y, token_rows, weights, T, k, out, ld_out, out_type, stream=None,
+                    raise_on_error=True):
+    st = load().fp8_moe_combine(_p(y), rows, H, ld_y, _p(token_rows), _p(weights), T, k, _p(out), ld_out,
+                                out_type, _stream(stream))
+    return _check("fp8_moe_combine", st, raise_on_error)
 
 
 def mxfp8_quant(x, rows, cols, ld_x, q, ld_q, s, s_stride_row, s_stride_group, stream=None, raise_on_error=True):
@@ -268,6 +276,17 @@ def mx_quant(x: torch.Tensor):
     s = _u8((rows, cols // 32), x.device)
     mxfp8_quant(x, rows, cols, x.stride(0), q, cols, s, cols // 32, 1)
     return q, s
+
+
+def moe_combine(y: torch.Tensor, token_rows: torch.Tensor, weights: torch.Tensor, out_dtype=torch.bfloat16):
+    """out[t] = sum_j weights[t, j] * y[token_rows[t, j]] for y bf16 [rows, H],
+    token_rows int32 [T, k], weights fp32 [T, k]."""
+    rows, H = y.shape
+    T, k = token_rows.shape
+    out = torch.empty((T, H), dtype=out_dtype, device=y.device)
+    fp8_moe_combine(y, rows, H, y.stride(0), token_rows.contiguous(), weights.contiguous(), T, k, out, H,
+                    OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
+    return out
 
 
 def e4m3_encode(v: torch.Tensor):

@@ -239,6 +239,32 @@ fp8bs_status fp8_silu_mul_quant(const uint16_t* gate_up, int64_t rows, int64_t I
                                 uint16_t* h_out, int64_t ld_h, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_moe_combine -- the step after the MoE down GEMM: each token's output is
+ * the routing-weighted sum of its k experts' outputs,
+ *
+ *   out[t][n] = sum_{j=0}^{k-1} weights[t*k + j] * y[token_rows[t*k + j]][n]
+ *
+ * (the MoE layer of Qwen3-30B-A3B that "Low Precision RL" runs in block-wise
+ * FP8, section "2. Unified block-wise FP8 (DeepSeek-style)").  The sum is an
+ * fp32 FMA chain in slot order j = 0, 1, ..., k-1 starting from 0
+ * (deterministic), then rounded to nearest even for bf16 output.
+ *
+ * y          : bf16 [rows][ld_y], the grouped down-projection output in
+ *              expert-sorted order (fp8_grouped_gemm's c).
+ * token_rows : device int32 [T][k]: the row of y that holds token t's j-th
+ *              assignment.  Entries outside [0, rows) are clamped into it
+ *              (never read outside y; the result is then meaningless).
+ * weights    : device fp32 [T][k] routing weights.
+ * out        : [T][ld_out], bf16 or fp32 per `out_type`.
+ * Requirements: rows, H, T >= 0, k >= 1; rows >= 1 if T > 0; H % 8 == 0;
+ * ld_y >= H, ld_y % 8 == 0, y 16-byte aligned; ld_out >= H, ld_out % 8 == 0,
+ * out 16-byte aligned; token_rows and weights 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_moe_combine(const uint16_t* y, int64_t rows, int64_t H, int64_t ld_y,
+                             const int32_t* token_rows, const float* weights, int64_t T, int32_t k,
+                             void* out, int64_t ld_out, fp8bs_out out_type, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * mxfp8_quant -- MXFP8 quantization: 32 consecutive values along a row share
  * one UE8M0 scale ("Low Precision RL", section "3. Unified MXFP8
  * (Blackwell)").  The block exponent is the smallest integer e with

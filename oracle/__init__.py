@@ -86,6 +86,8 @@ def _load():
         lib.or_gemm_mx_sampled.restype = None
         lib.or_silu_mul.argtypes = [P, I64, I64, I64, P]
         lib.or_silu_mul.restype = None
+        lib.or_moe_combine.argtypes = [P, I64, I64, P, P, I64, I64, P]
+        lib.or_moe_combine.restype = None
         lib.or_num_threads.argtypes = []
         lib.or_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -337,3 +339,22 @@ def grouped_gemm_blockscaled(qa, sa, offsets, qb, sb):
         if r1 > r0:
             y[r0:r1], yabs[r0:r1] = gemm_blockscaled(qa[r0:r1], sa[r0:r1], qb[g], sb[g])
     return y, yabs
+
+
+def moe_combine(y, pos, w):
+    """MoE combine: out[t] = sum_j w[t, j] * y[pos[t, j]] in fp64 (the
+    weighted sum of a token's expert outputs that closes the MoE layer whose
+    grouped GEMMs "Low Precision RL" runs in FP8, section "2. Unified
+    block-wise FP8 (DeepSeek-style)", Qwen3-30B-A3B).  y: [rows, H] bf16 bit
+    patterns in grouped order; pos: [T, k] int grouped rows; w: [T, k] fp32.
+    Returns [T, H] float64."""
+    y = _bf16_view(y)
+    pos = np.ascontiguousarray(pos, np.int32)
+    w = np.ascontiguousarray(w, np.float32)
+    T, k = pos.shape
+    assert w.shape == (T, k) and y.ndim == 2
+    assert pos.size == 0 or (pos.min() >= 0 and pos.max() < y.shape[0])
+    H = y.shape[1]
+    out = np.empty((T, H), np.float64)
+    _load().or_moe_combine(_ptr(y), H, H, _ptr(pos), _ptr(w), T, k, _ptr(out))
+    return out

@@ -443,6 +443,28 @@ OR_EXPORT void or_silu_mul(const uint16_t* gu, int64_t rows, int64_t I, int64_t 
         }
 }
 
+/* ------------------------------------------------------------------ */
+/* MoE combine after the down projection                                */
+/* ------------------------------------------------------------------ */
+
+/* Each token's output is the sum of its experts' outputs weighted by its
+ * routing weights: out[t][n] = sum_j w[t][j] * y[pos[t][j]][n] over the
+ * token's k slots, j = 0..k-1, in fp64.  y: [rows][ld_y] bf16 expert
+ * outputs in grouped (expert-sorted) order; pos[t][j]: the grouped row of
+ * token t's j-th assignment; w: [T][k] fp32.  out: [T][H] fp64. */
+OR_EXPORT void or_moe_combine(const uint16_t* y, int64_t H, int64_t ld_y, const int32_t* pos,
+                              const float* w, int64_t T, int64_t k, double* out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < H; ++n) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += (double)w[t * k + j] * (double)or_bf16_to_f32(y[(int64_t)pos[t * k + j] * ld_y + n]);
+            out[t * H + n] = acc;
+        }
+}
+
 /* Number of OpenMP threads the parallel loops above use. */
 OR_EXPORT int or_num_threads(void)
 {

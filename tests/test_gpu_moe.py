@@ -11,6 +11,13 @@ Every stage is checked on the device's own inputs to that stage (stage-wise
 parity): quantizer codes and scales bit-exact on sampled rows and experts,
 SiLU within one bf16 ulp, and each GEMM on sampled outputs of sampled groups
 against the fp64 oracle and the datapath truncation model.
+
+The combine that closes the layer (each token's output = routing-weighted sum
+of its experts' down-projection rows) is checked on sampled tokens of the
+chain, and on its own at full size on seeded synthetic expert outputs and on
+edge shapes, against the oracle's fp64 sum: the device's fp32 FMA chain over
+k slots is within k * 2^-24 * sum_j |w_j y_j| of it, plus half a bf16 ulp for
+bf16 output.
 """
 import numpy as np
 import pytest
@@ -112,6 +119,23 @@ def _check_h(gate_up, h, qh, sh, rows, mx):
         assert np.array_equal(host(sh[idx].contiguous()).view(np.uint32), sr.view(np.uint32))
 
 
+def _check_combine(y_bits, pos, w, out32, out16):
+    """y_bits: host bf16 rows, pos/w: host [T, k]; out32 / out16: host device
+    results for those T tokens."""
+    ref = oracle.moe_combine(y_bits, pos, w)
+    mag = oracle.moe_combine(y_bits & np.uint16(0x7FFF), pos, np.abs(w))
+    k = pos.shape[1]
+    chain = k * 2.0 ** -24 * mag + 1e-30
+    if out32 is not None:
+        err = np.abs(out32.astype(np.float64) - ref)
+        assert np.all(err <= chain), "fp32 combine: worst ratio %.3g" % np.max(err / chain)
+    if out16 is not None:
+        y = oracle.bf16_to_f32(out16).astype(np.float64)
+        half = 0.5 * np.exp2(np.floor(np.log2(np.maximum(np.maximum(np.abs(ref), np.abs(y)), 2.0 ** -126))) - 7)
+        err = np.abs(y - ref)
+        assert np.all(err <= chain + half), "bf16 combine: worst ratio %.3g" % np.max(err / (chain + half))
+
+
 def _grouped(rows, N, K, G, offs, a_rows, a_count, a, sa, b, sb, out_dtype):
     c = torch.empty((rows, N), dtype=out_dtype, device="cuda")
     ops.fp8_grouped_gemm(rows, N, K, G, offs, a_rows, a_count, a, a.stride(0), sa, sa.stride(0), sa.stride(1),
@@ -173,6 +197,19 @@ def _blockwise_chain(d, routing, seed, check_down=True, weights=None):
     qh_h, sh_h = host(qh), host(sh)
     _check_grouped(r.offsets, groups, seed + 3, dn16, dn32,
                    lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g]), host(sdt[g])))
+    del dn32
+    _say("combine")
+    T = r.token_rows.shape[0]
+    pos_d, w_d = dev(r.token_rows), dev(r.weights)
+    out16 = ops.moe_combine(dn16, pos_d, w_d, torch.bfloat16)
+    out32 = ops.moe_combine(dn16, pos_d, w_d, torch.float32)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(seed + 4).integers(0, T, 256)]))
+    pos = r.token_rows[toks]
+    yrows = host(dn16[torch.from_numpy(pos.reshape(-1).astype(np.int64)).cuda()])
+    local = np.arange(pos.size, dtype=np.int32).reshape(pos.shape)
+    tidx = torch.from_numpy(toks).cuda()
+    _check_combine(yrows, local, r.weights[toks], host(out32[tidx]), host(out16[tidx]))
 
 
 @pytest.fixture(scope="module")
@@ -247,3 +284,58 @@ def test_moe_mxfp8_chain_full_size(moe):
                    lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g * HID:(g + 1) * HID]),
                                       host(sdt[g * HID:(g + 1) * HID])),
                    mx=True)
+
+
+# ------------------------------------------------------------------ combine
+def test_moe_combine_full_size_synthetic(moe):
+    """The full-size combine (16384 tokens x 2048, top-8 over 131072 grouped
+    rows) on seeded synthetic expert outputs, every output."""
+    r = moe["routing"]
+    rows, (T, k) = r.row_token.size, r.token_rows.shape
+    _say("synthetic expert outputs %d x %d" % (rows, HID))
+    y = inputs.normal_bf16(np.random.default_rng(50), (rows, HID), 0.05, 0.001, 20.0)
+    yd = dev_bf16(y)
+    pos_d, w_d = dev(r.token_rows), dev(r.weights)
+    out16 = ops.moe_combine(yd, pos_d, w_d, torch.bfloat16)
+    out32 = ops.moe_combine(yd, pos_d, w_d, torch.float32)
+    torch.cuda.synchronize()
+    _say("checking")
+    _check_combine(y, r.token_rows, r.weights, host(out32), host(out16))
+
+
+@pytest.mark.parametrize("T,k,H,rows", [(1, 1, 8, 1), (5, 3, 264, 9), (37, 9, 128, 50), (64, 16, 2048, 300),
+                                        (300, 8, 776, 2400)])
+def test_moe_combine_shapes(T, k, H, rows):
+    """k below, at and above the 8-slot load batch; H not a multiple of the
+    workgroup's 256 chunks; repeated rows; negative weights; a row stride
+    larger than H."""
+    _say("combine", T, k, H, rows)
+    rng = np.random.default_rng(T + k + H)
+    ld = H + 16
+    y = inputs.normal_bf16(rng, (rows, ld), 1.0)
+    pos = rng.integers(0, rows, (T, k)).astype(np.int32)
+    w = rng.standard_normal((T, k)).astype(np.float32)
+    yd = dev_bf16(y)
+    out32 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    out16 = torch.empty((T, H + 8), dtype=torch.bfloat16, device="cuda")
+    ops.fp8_moe_combine(yd, rows, H, ld, dev(pos), dev(w), T, k, out32, H, ops.OUT_FP32)
+    ops.fp8_moe_combine(yd, rows, H, ld, dev(pos), dev(w), T, k, out16, H + 8, ops.OUT_BF16)
+    torch.cuda.synchronize()
+    _check_combine(np.ascontiguousarray(y[:, :H]), pos, w, host(out32), host(out16)[:, :H])
+
+
+def test_moe_combine_clamps_positions_and_rejects_bad_shapes():
+    rng = np.random.default_rng(7)
+    y = inputs.normal_bf16(rng, (10, 64), 1.0)
+    pos = np.array([[-5, 3], [12, 9]], np.int32)
+    w = np.array([[0.5, 0.25], [1.0, -2.0]], np.float32)
+    out = torch.empty((2, 64), dtype=torch.float32, device="cuda")
+    ops.fp8_moe_combine(dev_bf16(y), 10, 64, 64, dev(pos), dev(w), 2, 2, out, 64, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    _check_combine(y, np.clip(pos, 0, 9), w, host(out), None)
+    empty = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    ops.fp8_moe_combine(dev_bf16(y), 10, 64, 64, None, None, 0, 2, empty, 64, ops.OUT_FP32)
+    for args in ((10, 60, 64), (0, 64, 64), (10, 64, 56)):          # H % 8, no rows, ld_y < H
+        with pytest.raises(ops.Fp8bsError):
+            ops.fp8_moe_combine(dev_bf16(y), args[0], args[1], args[2], dev(pos), dev(w), 2, 2, out, 64,
+                                ops.OUT_FP32)
