@@ -42,7 +42,7 @@ PEAK_FP8_TFLOPS = 5030.0     # 256 CUs x 2.4 GHz x 8192 dense FP8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 M_TOK, HID, INTER = 4096, 2560, 9728
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
-WORKLOADS = ("tiny_linear", "mlp_backward", "moe_blockwise", "moe_mxfp8", "up_proj_rowwise")
+WORKLOADS = ("tiny_linear", "mlp_backward", "mlp_backward_mxfp8", "moe_blockwise", "moe_mxfp8", "up_proj_rowwise")
 
 
 def parse():
@@ -199,6 +199,41 @@ def wl_up_proj_rowwise(torch, ops, inputs, to_dev, R):
                                                                   ops.BSCALE_ROW128, y, N, ops.OUT_BF16),
          ("TFLOP/s", 2.0 * M * N * K)),
     ], {"workload": "up_proj_rowwise", "tokens": M, "in": K, "out": N, "seed": 1}
+
+
+def wl_mlp_backward_mxfp8(torch, ops, inputs, to_dev, R):
+    """The backward GEMMs of mlp_backward in MXFP8: dY 1x32 along O for
+    dgrad, W re-quantized 32x1 along O (transposed), dY and X re-quantized
+    32x1 along tokens (transposed) for wgrad."""
+    d = inputs.qwen3_4b_mlp_backward(2)
+    T, O = d["dy"].shape
+    I = d["x"].shape[1]
+    dys = [to_dev(d["dy"]) for _ in range(R)]
+    xs = [to_dev(d["x"]) for _ in range(R)]
+    w = to_dev(d["w"])
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    qdy, sdy = u8(T, O), u8(T, O // 32)
+    qdyt, sdyt = u8(O, T), u8(O, T // 32)
+    qxt, sxt = u8(I, T), u8(I, T // 32)
+    qwt, swt = u8(I, O), u8(I, O // 32)
+    dx = torch.empty((T, I), dtype=torch.float32, device="cuda")
+    dw = torch.empty((O, I), dtype=torch.float32, device="cuda")
+    return [
+        ("mx_quant_dy", lambda i: ops.mxfp8_quant(dys[i % R], T, O, O, qdy, O, sdy, O // 32, 1),
+         ("GB/s", qbytes_row(T, O, 32, 1))),
+        ("mx_quant_dy_t", lambda i: ops.mxfp8_quant_t(dys[i % R], T, O, O, qdyt, T, sdyt, T // 32, 1),
+         ("GB/s", qbytes_row(O, T, 32, 1))),
+        ("mx_quant_x_t", lambda i: ops.mxfp8_quant_t(xs[i % R], T, I, I, qxt, T, sxt, T // 32, 1),
+         ("GB/s", qbytes_row(I, T, 32, 1))),
+        ("mx_quant_w_t", lambda i: ops.mxfp8_quant_t(w, O, I, I, qwt, O, swt, O // 32, 1),
+         ("GB/s", qbytes_row(I, O, 32, 1))),
+        ("mx_gemm_dgrad_fp32", lambda i: ops.mxfp8_gemm(T, I, O, 0, None, None, T, qdy, O, sdy, O // 32, qwt, O, 0,
+                                                       swt, O // 32, 0, dx, I, ops.OUT_FP32),
+         ("TFLOP/s", 2.0 * T * I * O)),
+        ("mx_gemm_wgrad_fp32", lambda i: ops.mxfp8_gemm(O, I, T, 0, None, None, O, qdyt, T, sdyt, T // 32, qxt, T, 0,
+                                                       sxt, T // 32, 0, dw, I, ops.OUT_FP32),
+         ("TFLOP/s", 2.0 * O * I * T)),
+    ], {"workload": "mlp_backward_mxfp8", "tokens": T, "hidden": I, "intermediate": O, "seeds": [1, 2]}
 
 
 def _moe_inputs(inputs, cache={}):
@@ -471,6 +506,7 @@ def main():
     # ------------------------------------------------- the other workloads
     wanted = [w for w in args.workloads.split(",") if w and w != "none"]
     table = {"tiny_linear": wl_tiny_linear, "mlp_backward": wl_mlp_backward,
+             "mlp_backward_mxfp8": wl_mlp_backward_mxfp8,
              "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8, "up_proj_rowwise": wl_up_proj_rowwise}
     others = {}
     for wname in wanted:

@@ -318,6 +318,24 @@ fp8bs_status mxfp8_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
     return launched(launch_mx_quant(x, rows, cols, ld_x, q, ld_q, s, s_stride_row, s_stride_group, stream), "mxfp8_quant");
 }
 
+fp8bs_status mxfp8_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt, int64_t ld_qt,
+                           uint8_t* s, int64_t s_stride_row, int64_t s_stride_group, hipStream_t stream) {
+    if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "negative size");
+    if (rows % 32) return fail(FP8BS_ERR_SHAPE, "rows %% 32 != 0 (rows=%lld)", (long long)rows);
+    if (cols % 8) return fail(FP8BS_ERR_SHAPE, "cols %% 8 != 0 (cols=%lld)", (long long)cols);
+    // grid: 64-column tiles in x, 128-row tiles in y (at most 65535)
+    if ((rows + 127) / 128 > 65535 || cols > INT32_MAX / 2) return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || cols == 0) return ok();
+    if (!x || !qt || !s) return fail(FP8BS_ERR_NULL, "x, qt and s are required");
+    if (ld_x < cols || ld_qt < rows) return fail(FP8BS_ERR_STRIDE, "ld_x >= cols and ld_qt >= rows required");
+    if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (ld_qt % 16 || !aligned(qt, 16)) return fail(FP8BS_ERR_ALIGN, "qt must be 16-byte aligned with ld_qt %% 16 == 0");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_mx_quant_t(x, rows, cols, ld_x, qt, ld_qt, s, s_stride_row, s_stride_group, stream),
+                    "mxfp8_quant_t");
+}
+
 fp8bs_status mxfp8_gemm(int64_t rows, int64_t N, int64_t K, int32_t G, const int32_t* offsets, const int32_t* a_rows,
                         int64_t a_count, const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t lds_a,
                         const uint8_t* b, int64_t ldb, int64_t b_stride_g, const uint8_t* sb, int64_t lds_b,

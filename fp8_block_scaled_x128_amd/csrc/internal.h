@@ -15,6 +15,8 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, 
                                 uint8_t* q, int64_t ld_q, uint8_t* qt, int64_t ld_qt, float* s, hipStream_t st);
 hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
                            uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st);
+hipError_t launch_mx_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt, int64_t ld_qt,
+                             uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st);
 hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t rows, int64_t I, int64_t ld_in, int mx, uint8_t* q,
                                  int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint16_t* h, int64_t ld_h,
                                  hipStream_t st);

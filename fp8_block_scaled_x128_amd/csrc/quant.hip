@@ -205,15 +205,18 @@ hipError_t launch_rowgroup(RowArgs p, bool row_fast, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// 128x1 token-axis groups with transposed output.  Tile: 128 rows x 64 cols,
-// staged in LDS as [column pair][row] words (a word is a bf16 pair of one
-// row).  Thread t then owns column t/4 and rows 32*(t%4) .. +32; the four
-// threads of a column reduce the 128-row maximum with shuffles and each
-// writes 32 contiguous codes of the transposed row.
+// Token-axis groups with transposed output: 128x1 with FP32 scales, or (MX)
+// 32x1 with UE8M0 scales.  Tile: 128 rows x 64 cols, staged in LDS as
+// [column pair][row] words (a word is a bf16 pair of one row).  Thread t then
+// owns column t/4 and rows 32*(t%4) .. +32 and writes those 32 contiguous
+// codes of the transposed row.  128x1: the four threads of a column reduce
+// the 128-row maximum with shuffles.  MX: each thread's 32 rows are one
+// block.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads) k_quant_128x1_t(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
-                                                            int64_t ld_x, uint8_t* __restrict__ qt, int64_t ld_qt,
-                                                            float* __restrict__ s, int64_t ssr, int64_t ssg) {
+template <bool MX>
+__global__ void __launch_bounds__(kThreads) k_quant_col_t(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
+                                                          int64_t ld_x, uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                          void* __restrict__ s, int64_t ssr, int64_t ssg) {
     __shared__ __attribute__((aligned(16))) uint32_t tile[32][132];
     const int t = threadIdx.x;
     const int32_t r0 = (int32_t)blockIdx.y * 128;
@@ -246,18 +249,32 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x1_t(const uint16_t* __re
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = group4_max(m);
-    const float sc = m / kE4M3Max;
     uint32_t w[8];
+    float sc = 0.0f;
+    int e = 0;
+    if (!MX) {
+        m = group4_max(m);
+        sc = m / kE4M3Max;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) encode8(&v[8 * i], sc, w[2 * i], w[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) encode8(&v[8 * i], sc, w[2 * i], w[2 * i + 1]);
+    } else {
+        e = mx_exponent(m);
+        const float f = pow2_neg(e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            w[i] = m == 0.0f ? 0u : enc4(v[4 * i] * f, v[4 * i + 1] * f, v[4 * i + 2] * f, v[4 * i + 3] * f);
+    }
     const int32_t c = c0 + cl;
     if (c < cols) {
         const int32_t rs = r0 + rq * 32;
         uint8_t* dst = qt + (int64_t)c * ld_qt + rs;
         if (rs < rows) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
         if (rs + 16 < rows) *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-        if (rq == 0) s[(int64_t)c * ssr + (int64_t)blockIdx.y * ssg] = sc;
+        if (!MX) {
+            if (rq == 0) static_cast<float*>(s)[(int64_t)c * ssr + (int64_t)blockIdx.y * ssg] = sc;
+        } else if (rs < rows) {
+            static_cast<uint8_t*>(s)[(int64_t)c * ssr + (int64_t)(blockIdx.y * 4 + rq) * ssg] = (uint8_t)(e + 127);
+        }
     }
 }
 
@@ -494,8 +511,17 @@ hipError_t launch_quant_128x1_t(const uint16_t* x, int64_t rows, int64_t cols, i
                                 int64_t ld_qt, float* s, int64_t ssr, int64_t ssg, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
     dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
-    hipLaunchKernelGGL(k_quant_128x1_t, grid, dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, qt, ld_qt,
-                       s, ssr, ssg);
+    hipLaunchKernelGGL(k_quant_col_t<false>, grid, dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, qt,
+                       ld_qt, (void*)s, ssr, ssg);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt, int64_t ld_qt,
+                             uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
+    hipLaunchKernelGGL(k_quant_col_t<true>, grid, dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, qt,
+                       ld_qt, (void*)s, ssr, ssg);
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
 EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
            "fp8_grouped_gemm",
-           "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
+           "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
 
 
@@ -64,6 +64,7 @@ def load():
             "fp8_silu_mul_quant": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P, I64, P],
             "fp8_moe_combine": [P, I64, I64, I64, P, P, I64, I32, P, I64, INT, P],
             "mxfp8_quant": [P, I64, I64, I64, P, I64, P, I64, I64, P],
+            "mxfp8_quant_t": [P, I64, I64, I64, P, I64, P, I64, I64, P],
             "mxfp8_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, INT, P],
             "fp8bs_e4m3_encode": [P, P, I64, P],
         }
@@ -168,6 +169,13 @@ def mxfp8_quant(x, rows, cols, ld_x, q, ld_q, s, s_stride_row, s_stride_group, s
     st = load().mxfp8_quant(_p(x), rows, cols, ld_x, _p(q), ld_q, _p(s), s_stride_row, s_stride_group,
                             _stream(stream))
     return _check("mxfp8_quant", st, raise_on_error)
+
+
+def mxfp8_quant_t(x, rows, cols, ld_x, qt, ld_qt, s, s_stride_row, s_stride_group, stream=None,
+                  raise_on_error=True):
+    st = load().mxfp8_quant_t(_p(x), rows, cols, ld_x, _p(qt), ld_qt, _p(s), s_stride_row, s_stride_group,
+                              _stream(stream))
+    return _check("mxfp8_quant_t", st, raise_on_error)
 
 
 def mxfp8_gemm(rows, N, K, G, offsets, a_rows, a_count, a, lda, sa, lds_a, b, ldb, b_stride_g, sb, lds_b,
@@ -287,6 +295,27 @@ def moe_combine(y: torch.Tensor, token_rows: torch.Tensor, weights: torch.Tensor
     fp8_moe_combine(y, rows, H, y.stride(0), token_rows.contiguous(), weights.contiguous(), T, k, out, H,
                     OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
     return out
+
+
+def mx_quant_t(x: torch.Tensor):
+    """MXFP8 32x1 quantization along the rows of bf16 [rows, cols], written
+    transposed -> (qt [cols, rows], s [cols, rows/32] uint8)."""
+    rows, cols = x.shape
+    qt = _u8((cols, rows), x.device)
+    s = _u8((cols, rows // 32), x.device)
+    mxfp8_quant_t(x, rows, cols, x.stride(0), qt, rows, s, rows // 32, 1)
+    return qt, s
+
+
+def mx_gemm(a, sa, b, sb, out_dtype=torch.float32):
+    """Dense MXFP8 GEMM C = A B^T: a [M, K], b [N, K] codes, sa [M, K/32],
+    sb [N, K/32] UE8M0 bytes (row-major)."""
+    M, K = a.shape
+    N = b.shape[0]
+    c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    mxfp8_gemm(M, N, K, 0, None, None, M, a, a.stride(0), sa, sa.stride(0), b, b.stride(0), 0, sb, sb.stride(0), 0,
+               c, N, OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
+    return c
 
 
 def e4m3_encode(v: torch.Tensor):

@@ -282,6 +282,29 @@ fp8bs_status mxfp8_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * mxfp8_quant_t -- MXFP8 quantization along the other axis: 32 consecutive
+ * values of a COLUMN share one UE8M0 scale (same exponent rule and encoding
+ * as mxfp8_quant), written transposed.  It equals mxfp8_quant applied to the
+ * transpose of x.  1x32 blocks are not transpose-invariant, so the MXFP8
+ * backward GEMMs ("Low Precision RL", section "3. Unified MXFP8
+ * (Blackwell)": the recipe runs the weight-gradient and data-gradient GEMMs
+ * in MXFP8) need their operands re-quantized along the contraction axis:
+ *   dgrad dX = dY W : B operand = W quantized along its rows (output features);
+ *   wgrad dW = dY^T X : both operands quantized along tokens.
+ *
+ * x  : bf16 [rows][ld_x].   qt : [cols][ld_qt] codes, the row axis contiguous.
+ * s  : uint8, scale of (column c, block g = row / 32) at
+ *      s[c * s_stride_row + g * s_stride_group] (s_stride_row = lds,
+ *      s_stride_group = 1 gives mxfp8_gemm's [cols][lds] layout).
+ * Requirements: rows % 32 == 0, rows <= 65535 * 128; cols % 8 == 0;
+ * ld_x % 8 == 0, x 16-byte aligned; ld_qt >= rows, ld_qt % 16 == 0,
+ * qt 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status mxfp8_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                           uint8_t* qt, int64_t ld_qt, uint8_t* s, int64_t s_stride_row,
+                           int64_t s_stride_group, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * mxfp8_gemm -- C = A B^T on MXFP8 operands (dense when G == 0, grouped over
  * experts when G >= 1), exact power-of-two block scaling inside gfx950's
  * scaled FP8 matrix instructions, FP32 accumulation.

@@ -228,6 +228,15 @@ BSCALE_BLOCK128 = 0   # sb[n // 128, k // 128]
 BSCALE_ROW128 = 1     # sb[n, k // 128]
 
 
+def mx_quant_32x1_t(x):
+    """MXFP8 blocks of 32 consecutive values down each column, written
+    transposed: the 1x32 quantization of the transpose (the operand layout of
+    the MXFP8 weight- and data-gradient GEMMs, "Low Precision RL", section
+    "3. Unified MXFP8 (Blackwell)").  x: [rows, cols] -> (qt [cols, rows],
+    s [cols, rows/32] uint8)."""
+    return mx_quant_1x32(np.ascontiguousarray(_bf16_view(x).T))
+
+
 def _f32c(a):
     return np.ascontiguousarray(a, dtype=np.float32)
 

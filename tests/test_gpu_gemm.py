@@ -366,3 +366,61 @@ def test_mx_grouped_small_moe():
         r0, r1 = int(r.offsets[g]), int(r.offsets[g + 1])
         if r1 > r0:
             verify(qa_h[r0:r1], sa_h[r0:r1], qw_h[g], sw_h[g], ch[r0:r1], mx=True)
+
+
+# ------------------------------------------------------- MXFP8 backward
+@pytest.mark.parametrize("shape", [(256, 512), (96, 264), (32, 8), (4096, 2560), (9728, 2560)])
+def test_mx_quant_t_bit_exact(shape):
+    """32x1 MX blocks down each column, written transposed: codes and scale
+    bytes equal the oracle's 1x32 quantization of the transpose (partial
+    128-row and 64-column tiles included)."""
+    _say("mx_quant_t", shape)
+    x = _bits(shape, 60, 1.0, 0.01, 50.0)
+    if shape[0] >= 64 and shape[1] >= 3:
+        x[:32, 0] = 0                                   # an all-zero block
+        x[32:64, 1] = inputs.to_bf16_bits(np.full(32, 3e38, np.float32))
+        x[:32, 2] = inputs.to_bf16_bits((np.arange(32) * 1e-39).astype(np.float32))
+    qt, s = ops.mx_quant_t(dev_bf16(x))
+    torch.cuda.synchronize()
+    qr, sr = oracle.mx_quant_32x1_t(x)
+    assert np.array_equal(host(qt), qr)
+    assert np.array_equal(host(s), sr)
+
+
+def test_mx_backward_full_size_sampled():
+    """MXFP8 backward of the MLP up-projection at full size, FP32 outputs:
+    dgrad dX = dY W with dY 1x32 along O and W re-quantized 32x1 along O;
+    wgrad dW = dY^T X with both re-quantized 32x1 along tokens."""
+    d = inputs.qwen3_4b_mlp_backward(2)
+    dy, x, w = d["dy"], d["x"], d["w"]
+    qdy, sdy = ops.mx_quant(dev_bf16(dy))
+    qwt, swt = ops.mx_quant_t(dev_bf16(w))
+    dx = ops.mx_gemm(qdy, sdy, qwt, swt)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(23).integers(0, w.shape[1], 64)
+    qr, sr = oracle.mx_quant_1x32(np.ascontiguousarray(w.T[rows]))
+    assert np.array_equal(host(qwt)[rows], qr) and np.array_equal(host(swt)[rows], sr)
+    _say("mx dgrad", tuple(dx.shape))
+    mi, ni = sample_indices(dx.shape[0], dx.shape[1], 3000, 24)
+    verify(host(qdy), host(sdy), host(qwt), host(swt), host(dx), mi=mi, ni=ni, mx=True)
+    del dx
+    qa, sa = ops.mx_quant_t(dev_bf16(dy))
+    qb, sb = ops.mx_quant_t(dev_bf16(x))
+    dw = ops.mx_gemm(qa, sa, qb, sb)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(25).integers(0, dy.shape[1], 64)
+    qr, sr = oracle.mx_quant_1x32(np.ascontiguousarray(dy.T[rows]))
+    assert np.array_equal(host(qa)[rows], qr) and np.array_equal(host(sa)[rows], sr)
+    _say("mx wgrad", tuple(dw.shape))
+    mi, ni = sample_indices(dw.shape[0], dw.shape[1], 3000, 26)
+    verify(host(qa), host(sa), host(qb), host(sb), host(dw), mi=mi, ni=ni, mx=True)
+
+
+def test_mx_quant_t_rejects_bad_shapes():
+    x = dev_bf16(_bits((48, 64), 61))
+    qt = torch.empty((64, 48), dtype=torch.uint8, device="cuda")
+    s = torch.empty((64, 2), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ops.Fp8bsError):
+        ops.mxfp8_quant_t(x, 48, 64, 64, qt, 48, s, 2, 1)       # rows % 32
+    with pytest.raises(ops.Fp8bsError):
+        ops.mxfp8_quant_t(x, 32, 64, 64, qt, 40, s, 2, 1)       # ld_qt % 16
