@@ -86,6 +86,8 @@ def _load():
         lib.or_gemm_mx_sampled.restype = None
         lib.or_silu_mul.argtypes = [P, I64, I64, I64, P]
         lib.or_silu_mul.restype = None
+        lib.or_quant_pow2.argtypes = [P, I64, I64, I64, I64, P, P, I64]
+        lib.or_quant_pow2.restype = None
         lib.or_moe_combine.argtypes = [P, I64, I64, P, P, I64, I64, P]
         lib.or_moe_combine.restype = None
         lib.or_num_threads.argtypes = []
@@ -226,6 +228,37 @@ def mx_quant_1x32(x):
 # ---------------------------------------------------------------- GEMMs
 BSCALE_BLOCK128 = 0   # sb[n // 128, k // 128]
 BSCALE_ROW128 = 1     # sb[n, k // 128]
+
+
+def _quant_pow2(x, block_rows):
+    x = _bf16_view(x)
+    rows, cols = x.shape
+    ngr, ngc = (rows + block_rows - 1) // block_rows, (cols + 127) // 128
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((ngr, ngc), np.uint8)
+    _load().or_quant_pow2(_ptr(x), rows, cols, cols, block_rows, _ptr(q), _ptr(s), ngc)
+    return q, s
+
+
+def quant_1x128_pow2(x):
+    """1x128 groups with power-of-two scales: the group's scale is rounded up
+    to a power of two (the MX exponent rule on the 128-element group), kept
+    as a UE8M0 byte; "Low Precision RL", section "2. Unified block-wise FP8
+    (DeepSeek-style)": the block-wise recipe with power-of-two scales, as
+    TransformerEngine runs it on Blackwell through MXFP8.  x: [rows, cols] ->
+    (q [rows, cols], s [rows, ceil(cols/128)] uint8)."""
+    return _quant_pow2(x, 1)
+
+
+def quant_128x128_pow2(x):
+    """128x128 blocks with power-of-two UE8M0 scales (see quant_1x128_pow2).
+    x: [rows, cols] -> (q, s [ceil(rows/128), ceil(cols/128)] uint8)."""
+    return _quant_pow2(x, 128)
+
+
+def pow2_scales(s):
+    """UE8M0 scale bytes -> their float32 values 2^(c - 127) (exact)."""
+    return ue8m0_decode(np.asarray(s, np.uint8)).astype(np.float32)
 
 
 def mx_quant_32x1_t(x):

@@ -336,6 +336,40 @@ OR_EXPORT void or_mx_quant_1x32(const uint16_t* x, int64_t rows, int64_t cols, i
     }
 }
 
+/* Block-wise groups with power-of-two scales: 1x128 groups along a row
+ * (block_rows == 1) or 128x128 blocks (block_rows == 128).  Each group takes
+ * the MX exponent rule on its own amax (e = or_mx_exponent(amax), the
+ * smallest e with amax <= 448 * 2^e), stores the UE8M0 byte e + 127 and
+ * encodes enc(x * 2^-e).  q: [rows][cols]; s: scale byte of (row group i,
+ * column group g) at s[i * ld_s + g]. */
+OR_EXPORT void or_quant_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int64_t block_rows,
+                             uint8_t* q, uint8_t* s, int64_t ld_s)
+{
+    int64_t ngr = (rows + block_rows - 1) / block_rows, ngc = (cols + 127) / 128;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < ngr; ++i) {
+        int64_t r0 = i * block_rows, r1 = r0 + block_rows < rows ? r0 + block_rows : rows;
+        for (int64_t g = 0; g < ngc; ++g) {
+            int64_t c0 = g * 128, c1 = c0 + 128 < cols ? c0 + 128 : cols;
+            float amax = 0.0f;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) {
+                    float a = fabsf(or_bf16_to_f32(x[r * ld_x + c]));
+                    if (a > amax) amax = a;
+                }
+            int e = or_mx_exponent(amax);
+            s[i * ld_s + g] = (uint8_t)(e + 127);
+            double inv = ldexp(1.0, -e);
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) {
+                    float v = or_bf16_to_f32(x[r * ld_x + c]);
+                    float scaled = (float)((double)v * inv);
+                    q[r * cols + c] = (amax == 0.0f) ? (uint8_t)0 : or_e4m3_encode(scaled);
+                }
+        }
+    }
+}
+
 /* UE8M0 decode: 2^(c-127); 0xFF is NaN. */
 OR_EXPORT double or_ue8m0_decode(uint8_t c)
 {
