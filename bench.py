@@ -42,7 +42,8 @@ PEAK_FP8_TFLOPS = 5030.0     # 256 CUs x 2.4 GHz x 8192 dense FP8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 M_TOK, HID, INTER = 4096, 2560, 9728
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
-WORKLOADS = ("tiny_linear", "mlp_backward", "mlp_backward_mxfp8", "moe_blockwise", "moe_mxfp8", "up_proj_rowwise")
+WORKLOADS = ("tiny_linear", "mlp_backward", "mlp_backward_mxfp8", "moe_blockwise", "moe_mxfp8", "up_proj_rowwise",
+             "up_proj_pow2")
 
 
 def parse():
@@ -234,6 +235,29 @@ def wl_mlp_backward_mxfp8(torch, ops, inputs, to_dev, R):
                                                        sxt, T // 32, 0, dw, I, ops.OUT_FP32),
          ("TFLOP/s", 2.0 * O * I * T)),
     ], {"workload": "mlp_backward_mxfp8", "tokens": T, "hidden": I, "intermediate": O, "seeds": [1, 2]}
+
+
+def wl_up_proj_pow2(torch, ops, inputs, to_dev, R):
+    """The up projection of the headline step with power-of-two (UE8M0)
+    block scales: 1x128 activation groups, 128x128 weight blocks, the GEMM
+    applying the scales inside the scaled matrix instruction."""
+    d = inputs.qwen3_4b_mlp(1, parts=("up",))
+    M, K, N = M_TOK, HID, INTER
+    xs = [to_dev(d["x_up"]) for _ in range(R)]
+    w = to_dev(d["w_up"])
+    lds = 4 * ((K + 511) // 512)
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8, device="cuda")
+    qx, sx, qw, sw = u8(M, K), u8(M, lds), u8(N, K), u8(N // 128, lds)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    return [
+        ("quant_x_1x128_pow2", lambda i: ops.fp8_quant_pow2(xs[i % R], M, K, K, 1, qx, K, sx, lds),
+         ("GB/s", qbytes_row(M, K, 128, 1))),
+        ("quant_w_128x128_pow2", lambda i: ops.fp8_quant_pow2(w, N, K, K, 128, qw, K, sw, lds),
+         ("GB/s", N * K * 3 + (N // 128) * (K // 128))),
+        ("gemm_pow2_bf16", lambda i: ops.fp8_blockscaled_gemm_pow2(M, N, K, qx, K, sx, lds, qw, K, sw, lds, y, N,
+                                                                  ops.OUT_BF16),
+         ("TFLOP/s", 2.0 * M * N * K)),
+    ], {"workload": "up_proj_pow2", "tokens": M, "in": K, "out": N, "seed": 1}
 
 
 def _moe_inputs(inputs, cache={}):
@@ -506,7 +530,7 @@ def main():
     # ------------------------------------------------- the other workloads
     wanted = [w for w in args.workloads.split(",") if w and w != "none"]
     table = {"tiny_linear": wl_tiny_linear, "mlp_backward": wl_mlp_backward,
-             "mlp_backward_mxfp8": wl_mlp_backward_mxfp8,
+             "mlp_backward_mxfp8": wl_mlp_backward_mxfp8, "up_proj_pow2": wl_up_proj_pow2,
              "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8, "up_proj_rowwise": wl_up_proj_rowwise}
     others = {}
     for wname in wanted:

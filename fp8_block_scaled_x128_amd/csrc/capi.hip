@@ -336,6 +336,51 @@ fp8bs_status mxfp8_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_
                     "mxfp8_quant_t");
 }
 
+fp8bs_status fp8_quant_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block_rows, uint8_t* q,
+                            int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t stream) {
+    if (block_rows != 1 && block_rows != 128) return fail(FP8BS_ERR_UNSUPPORTED, "block_rows %d", (int)block_rows);
+    if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "negative size");
+    if (cols % 8) return fail(FP8BS_ERR_SHAPE, "cols %% 8 != 0 (cols=%lld)", (long long)cols);
+    if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2 || (block_rows == 1 && rows * ((cols + 127) / 128) > kMaxRuns) ||
+        (block_rows == 128 && (rows + 127) / 128 > 65535))
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || cols == 0) return ok();
+    if (!x || !q || !s) return fail(FP8BS_ERR_NULL, "x, q and s are required");
+    if (ld_x < cols || ld_q < cols || ld_s < (cols + 127) / 128)
+        return fail(FP8BS_ERR_STRIDE, "ld_x, ld_q >= cols and ld_s >= ceil(cols / 128) required");
+    if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_quant_pow2(x, rows, cols, ld_x, block_rows, q, ld_q, s, ld_s, stream), "fp8_quant_pow2");
+}
+
+fp8bs_status fp8_blockscaled_gemm_pow2(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                       const uint8_t* sa, int64_t lds_a, const uint8_t* b, int64_t ldb,
+                                       const uint8_t* sb, int64_t lds_b, void* c, int64_t ldc, fp8bs_out out,
+                                       hipStream_t stream) {
+    fp8bs_status v = check_gemm_common(M, N, K, a, lda, b, ldb, c, ldc, out, 128);
+    if (v != FP8BS_OK) return v;
+    if (M == 0 || N == 0) return ok();
+    if (!sa || !sb) return fail(FP8BS_ERR_NULL, "sa and sb are required");
+    // each 128-K slice's byte is read as part of the 4-byte word of slices 4(kb/4) .. +3
+    const int64_t words = 4 * ((K / 128 + 3) / 4);
+    if (lds_a < words || lds_b < words) return fail(FP8BS_ERR_STRIDE, "lds_a, lds_b must be >= 4 * ceil(K / 512)");
+    if (lds_a % 4 || lds_b % 4 || !aligned(sa, 4) || !aligned(sb, 4))
+        return fail(FP8BS_ERR_ALIGN, "scale arrays must be 4-byte aligned with lds %% 4 == 0");
+    if ((uint64_t)M * (uint64_t)lda >= (1ull << 32) || (uint64_t)N * (uint64_t)ldb >= (1ull << 32))
+        return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
+    if (((M + 127) / 128) * ((N + 159) / 160) >= (1ll << 31) - 8) return fail(FP8BS_ERR_SHAPE, "too many tiles");
+    if ((v = check_scale_extent("sa", M, lds_a, 1, 0, 1)) != FP8BS_OK) return v;
+    if ((v = check_scale_extent("sb", N / 128, lds_b, 1, 0, 1)) != FP8BS_OK) return v;
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    Pow2GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.a = a; g.lda = lda; g.sa = sa; g.lds_a = lds_a;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.lds_b = lds_b; g.c = c; g.ldc = ldc; g.out_f32 = out == FP8BS_OUT_FP32;
+    return launched(launch_gemm_pow2(g, stream), "fp8_blockscaled_gemm_pow2");
+}
+
 fp8bs_status mxfp8_gemm(int64_t rows, int64_t N, int64_t K, int32_t G, const int32_t* offsets, const int32_t* a_rows,
                         int64_t a_count, const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t lds_a,
                         const uint8_t* b, int64_t ldb, int64_t b_stride_g, const uint8_t* sb, int64_t lds_b,

@@ -114,7 +114,10 @@ struct Cfg {
 // MODE_KINV: scales constant along K (rowwise / tensorwise scaling); the
 // matrix unit accumulates the whole contraction with unit scales and the
 // epilogue multiplies each output by sa(m) * sb(n).
-enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2, MODE_KINV = 3 };
+// MODE_P2: 1x128 / 128x128 groups with power-of-two UE8M0 scales (bytes,
+// sa [M][lds_a], sb [N/128][lds_b]); the matrix instruction applies them
+// exactly, one scale byte per lane for its whole 128-K slice.
+enum { MODE_BLOCK128 = 0, MODE_ROW128 = 1, MODE_MX = 2, MODE_KINV = 3, MODE_P2 = 4 };
 
 struct KArgs {
     int32_t M, N, K;
@@ -222,7 +225,8 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     using C = Cfg<WAVES, NF>;
     constexpr int BM = C::BM, BN = C::BN;
     // per-row weight scales are copied by waves 0..3 in 64-row pieces
-    static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || NF == 8, "ROW128 and MX modes use 256-row weight tiles");
+    static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || NF == 8,
+                  "ROW128 and MX modes use 256-row weight tiles");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
     __shared__ int s_tile[3];
 
@@ -315,7 +319,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         m_end = min(p.offsets[g + 1], m_begin + BM);
         n0 = s_tile[2] * BN;
         bptr += (int64_t)g * p.b_sg;
-        sbp += (int64_t)g * p.sb_sg * (MODE == MODE_MX ? 1 : 4);
+        sbp += (int64_t)g * p.sb_sg * ((MODE == MODE_MX || MODE == MODE_P2) ? 1 : 4);
     }
     auto arow = [&](int m_local) {             // physical A row of tile row m_local (clamped)
         int m = min(m_begin + m_local, m_end - 1);
@@ -346,15 +350,15 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     // rows [64 w, +64).  Weight scales: MODE_BLOCK128 -> wave BM/64 copies the
     // two 128-row blocks of the tile; ROW128 / MX -> waves 0..3 copy rows [64 w, +64).
     const bool has_sa = MODE != MODE_KINV && wave < BM / 64;
-    const bool has_sb = MODE != MODE_KINV && ((MODE == MODE_BLOCK128) ? wave == BM / 64 : wave < 4);
+    const bool has_sb = MODE != MODE_KINV && ((MODE == MODE_BLOCK128 || MODE == MODE_P2) ? wave == BM / 64 : wave < 4);
     uint32_t sa_off = 0, sb_off = 0;            // byte offsets without the slice term (< 4 GiB)
     if (has_sa) {
         const int m = arow(wave * 64 + lane);
-        sa_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4);
+        sa_off = (uint32_t)((MODE == MODE_MX || MODE == MODE_P2) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4);
     }
-    if (MODE == MODE_BLOCK128) {
+    if (MODE == MODE_BLOCK128 || MODE == MODE_P2) {
         const int nb = min(n0 / 128 + (lane & 1), (p.N - 1) / 128);
-        sb_off = (uint32_t)((int64_t)nb * p.sb_sn * 4);
+        sb_off = (uint32_t)((int64_t)nb * p.sb_sn * (MODE == MODE_P2 ? 1 : 4));
     } else if (MODE != MODE_KINV) {
         const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
         sb_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4);
@@ -375,6 +379,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         if (!has_sb) return;
         const uint32_t st = bstage(stage) + BN * BK;
         if (MODE == MODE_MX) dma4(sbp, sb_off + (uint32_t)(kb * 4), st + wave * 64 * 4);
+        else if (MODE == MODE_P2) dma4(sbp, sb_off + (uint32_t)((kb >> 2) * 4), st);   // slices 4(kb/4) .. +3
         else if (MODE == MODE_BLOCK128) dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st);
         else dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st + wave * 64 * 4);
     };
@@ -382,6 +387,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         if (!has_sa) return;
         const uint32_t st = abuf(buf) + BM * BK + wave * 64 * 4;
         if (MODE == MODE_MX) dma4(p.sa, sa_off + (uint32_t)(kb * 4), st);
+        else if (MODE == MODE_P2) dma4(p.sa, sa_off + (uint32_t)((kb >> 2) * 4), st);
         else dma4(p.sa, sa_off + (uint32_t)(kb * p.sa_sk * 4), st);
     };
     auto copy_a = [&](int kb, int buf, int t) {
@@ -455,6 +461,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
+            else if (MODE == MODE_P2) mxa[mt] = lds_readu8(sa_lds + mt * 64 + (kb & 3));
             else if (MODE == MODE_KINV) mxa[mt] = kE8M0One;
             else sam[mt] = lds_readf(sa_lds + mt * 64);
         }
@@ -476,13 +483,23 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
                 if (CB && C::b_slot(t) == nt) copy_b(b_kb, cst, t);
         };
 
-        if (MODE == MODE_MX || MODE == MODE_KINV) {
+        if (MODE == MODE_MX || MODE == MODE_KINV || MODE == MODE_P2) {
             const uint32_t sb8 = opaque(tB + BN * BK + (wn * 16 * NF + r16) * 4 + q);
+            // P2: the tile's two 128-row weight blocks, byte kb % 4 of each
+            // block's copied word (chosen per n-tile as in BLOCK128)
+            int pb0 = kE8M0One, pb1 = kE8M0One;
+            if (MODE == MODE_P2) {
+                const uint32_t sbw = tB + BN * BK + (kb & 3);
+                pb0 = lds_readu8(sbw + (NF == 8 ? wn * 4 : 0));
+                pb1 = NF == 8 ? pb0 : lds_readu8(sbw + 4);
+            }
             const FragOff bb = frag_base(tB + wn * 16 * NF * BK, fo);
 #pragma unroll
             for (int nt = 0; nt < NF; ++nt) {
                 const v8i fb = read_frag(bb, nt * 16 * BK);
-                const int mxb = MODE == MODE_KINV ? kE8M0One : lds_readu8(sb8 + nt * 64);
+                const int mxb = MODE == MODE_KINV ? kE8M0One
+                                : MODE == MODE_P2 ? ((NF == 8 || nt < nb_w) ? pb0 : pb1)
+                                                  : lds_readu8(sb8 + nt * 64);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
                     acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb, fa[mt], acc[nt][mt], 0, 0, 0,
@@ -766,6 +783,23 @@ hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st) {
     p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
     return waves_for(g.M, g.N, g.G / 2) == 8 ? launch<MODE_BLOCK128, true, 8, 8>(p, g.out_f32, st)
                                               : launch<MODE_BLOCK128, true, 4, 8>(p, g.out_f32, st);
+}
+
+hipError_t launch_gemm_pow2(const Pow2GemmArgs& g, hipStream_t st) {
+    if (g.M == 0 || g.N == 0) return hipSuccess;
+    KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
+    p.sa_sm = g.lds_a; p.sa_sk = 1; p.sb_sn = g.lds_b; p.sb_sk = 1;
+    const DensePlan plan = plan_dense(g.M, g.N, g.K);
+    if (plan.c2 < 0) return launch_dense<MODE_P2>(plan.c1, p, g.out_f32, st);
+    KArgs p1 = p, p2 = p;
+    p1.N = (int32_t)plan.split;
+    p2.N = (int32_t)(g.N - plan.split);
+    p2.b = p.b + plan.split * p.ldb;
+    p2.sb = p.sb + (plan.split / 128) * p.sb_sn;
+    p2.c = static_cast<uint8_t*>(p.c) + plan.split * (g.out_f32 ? 4 : 2);
+    const hipError_t e = launch_dense<MODE_P2>(plan.c1, p1, g.out_f32, st);
+    if (e != hipSuccess) return e;
+    return launch_dense<MODE_P2>(plan.c2, p2, g.out_f32, st);
 }
 
 hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st) {

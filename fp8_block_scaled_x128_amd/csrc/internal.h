@@ -24,6 +24,8 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, i
                                 float* s, hipStream_t st);
 hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
                                    int64_t ld_q, float* s, hipStream_t st);
+hipError_t launch_quant_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int block_rows, uint8_t* q,
+                             int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t st);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st);
 
 // moe.hip
@@ -56,5 +58,15 @@ struct MxGemmArgs {
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
 };
 hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st);
+
+// Block-wise GEMM with power-of-two UE8M0 scales: sa(m, kb) = sa[m * lds_a + kb],
+// sb(n / 128, kb) = sb[(n / 128) * lds_b + kb] (bytes).
+struct Pow2GemmArgs {
+    int64_t M, N, K;
+    const uint8_t* a; int64_t lda; const uint8_t* sa; int64_t lds_a;
+    const uint8_t* b; int64_t ldb; const uint8_t* sb; int64_t lds_b;
+    void* c; int64_t ldc; int out_f32;
+};
+hipError_t launch_gemm_pow2(const Pow2GemmArgs& g, hipStream_t st);
 
 }  // namespace fp8bs

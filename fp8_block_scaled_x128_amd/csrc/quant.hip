@@ -100,7 +100,9 @@ struct RowArgs {
     int32_t runs_per_row, total_runs;
 };
 
-template <bool SILU, bool MX, bool ROW_FAST, int U, bool NTQ>
+// P2: 128-element groups with power-of-two scales (the MX exponent rule on
+// the group's amax, a UE8M0 byte per group, codes E4M3(x * 2^-e)).
+template <bool SILU, bool MX, bool ROW_FAST, int U, bool NTQ, bool P2>
 __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
     const int sub = threadIdx.x & 15;
     const int32_t rid = (int32_t)blockIdx.x * (kThreads / 16) + (int32_t)(threadIdx.x >> 4);
@@ -148,12 +150,24 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
                 }
             }
             uint32_t w0, w1;
-            if (!MX) {
+            if (!MX && !P2) {
                 const float amax = group16_max(absmax8(v));
                 const float s = amax / kE4M3Max;
                 encode8(v, s, w0, w1);
                 if (valid && sub == 0)
                     static_cast<float*>(p.s)[(int64_t)r * p.ssr + (int64_t)g * p.ssg] = s;
+            } else if (P2) {
+                const float amax = group16_max(absmax8(v));
+                const int e = mx_exponent(amax);
+                const float f = pow2_neg(e);
+                if (amax == 0.0f) {
+                    w0 = 0u; w1 = 0u;
+                } else {
+                    w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+                    w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+                }
+                if (valid && sub == 0)
+                    static_cast<uint8_t*>(p.s)[(int64_t)r * p.ssr + (int64_t)g * p.ssg] = (uint8_t)(e + 127);
             } else {
                 const float amax = group4_max(absmax8(v));
                 const int e = mx_exponent(amax);
@@ -177,7 +191,7 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
     }
 }
 
-template <bool SILU, bool MX>
+template <bool SILU, bool MX, bool P2 = false>
 hipError_t launch_rowgroup(RowArgs p, bool row_fast, hipStream_t st) {
     constexpr int U = 4;
     if (p.total_runs == 0) return hipSuccess;
@@ -191,7 +205,7 @@ hipError_t launch_rowgroup(RowArgs p, bool row_fast, hipStream_t st) {
     // written with the streaming policy; smaller ones stay cached for the GEMM
     const bool ntq = (int64_t)p.total_runs * 128 > ((int64_t)256 << 20);
     auto go = [&](auto rf, auto nt) {
-        hipLaunchKernelGGL((k_rowgroup<SILU, MX, decltype(rf)::value, U, decltype(nt)::value>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((k_rowgroup<SILU, MX, decltype(rf)::value, U, decltype(nt)::value, P2>), dim3((unsigned)blocks),
                            dim3(kThreads), 0, st, p);
     };
     if (row_fast) {
@@ -296,11 +310,13 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
     o[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-template <bool TRANS, bool NT>
+// P2: power-of-two scale (MX exponent rule on the block's amax) stored as a
+// UE8M0 byte, codes E4M3(x * 2^-e); s is then uint8 with row stride lds.
+template <bool TRANS, bool NT, bool P2>
 __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __restrict__ w, int32_t rows, int32_t cols,
                                                             int64_t ld_w, uint8_t* __restrict__ q, int64_t ld_q,
                                                             uint8_t* __restrict__ qt, int64_t ld_qt,
-                                                            float* __restrict__ s, int32_t nbr, int32_t nbc) {
+                                                            void* __restrict__ s, int32_t nbr, int32_t lds) {
     __shared__ float red[kThreads / 64];
     __shared__ __attribute__((aligned(16))) uint32_t ctile[TRANS ? 128 : 1][33];
     const int t = threadIdx.x;
@@ -308,7 +324,7 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
     w += bz * (int64_t)rows * ld_w;
     q += bz * (int64_t)rows * ld_q;
     if (TRANS) qt += bz * (int64_t)cols * ld_qt;
-    s += bz * (int64_t)nbr * nbc;
+    const int64_t s_idx = bz * (int64_t)nbr * lds + (int64_t)blockIdx.y * lds + blockIdx.x;
     const int32_t r0 = (int32_t)blockIdx.y * 128, c0 = (int32_t)blockIdx.x * 128;
     const int cc = t & 15;
     uint4 raw[8];
@@ -334,12 +350,21 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = m / kE4M3Max;
+    const int e = P2 ? mx_exponent(m) : 0;
+    const float f = P2 ? pow2_neg(e) : 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float v[8];
         unpack8(raw[i], v);
         uint32_t w0, w1;
-        encode8(v, sc, w0, w1);
+        if (!P2) {
+            encode8(v, sc, w0, w1);
+        } else if (m == 0.0f) {
+            w0 = 0u; w1 = 0u;
+        } else {
+            w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+            w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+        }
         const int rl = (t >> 4) + 16 * i;
         const int32_t r = r0 + rl, c = c0 + cc * 8;
         if (r < rows && c < cols) {
@@ -349,7 +374,10 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
         }
         if (TRANS) { ctile[rl][2 * cc] = w0; ctile[rl][2 * cc + 1] = w1; }
     }
-    if (t == 0) s[(int64_t)blockIdx.y * nbc + blockIdx.x] = sc;
+    if (t == 0) {
+        if (P2) static_cast<uint8_t*>(s)[s_idx] = (uint8_t)(e + 127);
+        else static_cast<float*>(s)[s_idx] = sc;
+    }
     if (TRANS) {
         __syncthreads();
         // thread -> 4 columns (cb) x 16 rows (rb); 8 consecutive lanes cover one
@@ -536,8 +564,8 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, 
     // lost on them, and their codes should stay cached for the GEMM).
     const bool nt = batch * rows * cols * 2 > ((int64_t)256 << 20);
     auto go = [&](auto trans, auto ntt) {
-        hipLaunchKernelGGL((k_quant_128x128<decltype(trans)::value, decltype(ntt)::value>), grid, dim3(kThreads), 0, st,
-                           w, (int32_t)rows, (int32_t)cols, ld_w, q, ld_q, qt, ld_qt, s, nbr, nbc);
+        hipLaunchKernelGGL((k_quant_128x128<decltype(trans)::value, decltype(ntt)::value, false>), grid, dim3(kThreads),
+                           0, st, w, (int32_t)rows, (int32_t)cols, ld_w, q, ld_q, qt, ld_qt, (void*)s, nbr, nbc);
     };
     if (qt) {
         if (nt) go(std::true_type{}, std::true_type{});
@@ -571,6 +599,24 @@ hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols
     if (eblocks > 256 * 64) eblocks = 256 * 64;
     hipLaunchKernelGGL(k_tensor_encode, dim3((unsigned)eblocks), dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols,
                        ld_x, q, ld_q, (const float*)s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int block_rows, uint8_t* q,
+                             int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t st) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (block_rows == 1) {
+        RowArgs p{};
+        p.x = x; p.ld_x = ld_x; p.rows = (int32_t)rows; p.cols = (int32_t)cols; p.up_off = 0;
+        p.q = q; p.ld_q = ld_q; p.s = s; p.ssr = ld_s; p.ssg = 1; p.h = nullptr; p.ld_h = 0;
+        p.runs_per_row = (int32_t)((cols + 127) / 128);
+        p.total_runs = (int32_t)(rows * p.runs_per_row);
+        return launch_rowgroup<false, false, true>(p, false, st);
+    }
+    const int32_t nbr = (int32_t)((rows + 127) / 128), nbc = (int32_t)((cols + 127) / 128);
+    hipLaunchKernelGGL((k_quant_128x128<false, false, true>), dim3((unsigned)nbc, (unsigned)nbr, 1u), dim3(kThreads), 0,
+                       st, x, (int32_t)rows, (int32_t)cols, ld_x, q, ld_q, (uint8_t*)nullptr, (int64_t)0, (void*)s, nbr,
+                       (int32_t)ld_s);
     return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
 EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
            "fp8_grouped_gemm",
-           "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t", "mxfp8_gemm", "fp8bs_e4m3_encode",
+           "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
+           "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
 
 
@@ -65,6 +66,8 @@ def load():
             "fp8_moe_combine": [P, I64, I64, I64, P, P, I64, I32, P, I64, INT, P],
             "mxfp8_quant": [P, I64, I64, I64, P, I64, P, I64, I64, P],
             "mxfp8_quant_t": [P, I64, I64, I64, P, I64, P, I64, I64, P],
+            "fp8_quant_pow2": [P, I64, I64, I64, I32, P, I64, P, I64, P],
+            "fp8_blockscaled_gemm_pow2": [I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P, I64, INT, P],
             "mxfp8_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, INT, P],
             "fp8bs_e4m3_encode": [P, P, I64, P],
         }
@@ -176,6 +179,18 @@ def mxfp8_quant_t(x, rows, cols, ld_x, qt, ld_qt, s, s_stride_row, s_stride_grou
     st = load().mxfp8_quant_t(_p(x), rows, cols, ld_x, _p(qt), ld_qt, _p(s), s_stride_row, s_stride_group,
                               _stream(stream))
     return _check("mxfp8_quant_t", st, raise_on_error)
+
+
+def fp8_quant_pow2(x, rows, cols, ld_x, block_rows, q, ld_q, s, ld_s, stream=None, raise_on_error=True):
+    st = load().fp8_quant_pow2(_p(x), rows, cols, ld_x, block_rows, _p(q), ld_q, _p(s), ld_s, _stream(stream))
+    return _check("fp8_quant_pow2", st, raise_on_error)
+
+
+def fp8_blockscaled_gemm_pow2(M, N, K, a, lda, sa, lds_a, b, ldb, sb, lds_b, c, ldc, out, stream=None,
+                              raise_on_error=True):
+    st = load().fp8_blockscaled_gemm_pow2(M, N, K, _p(a), lda, _p(sa), lds_a, _p(b), ldb, _p(sb), lds_b, _p(c), ldc,
+                                          out, _stream(stream))
+    return _check("fp8_blockscaled_gemm_pow2", st, raise_on_error)
 
 
 def mxfp8_gemm(rows, N, K, G, offsets, a_rows, a_count, a, lda, sa, lds_a, b, ldb, b_stride_g, sb, lds_b,
@@ -315,6 +330,29 @@ def mx_gemm(a, sa, b, sb, out_dtype=torch.float32):
     c = torch.empty((M, N), dtype=out_dtype, device=a.device)
     mxfp8_gemm(M, N, K, 0, None, None, M, a, a.stride(0), sa, sa.stride(0), b, b.stride(0), 0, sb, sb.stride(0), 0,
                c, N, OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
+    return c
+
+
+def quant_pow2(x: torch.Tensor, block_rows: int):
+    """Power-of-two-scale quantization of bf16 [rows, cols] in 1x128
+    (block_rows 1) or 128x128 (128) groups -> (q, s) with s a
+    [row groups, ld_s] uint8 buffer, ld_s = 4 * ceil(cols / 512) (the GEMM's
+    layout); s[:, :ceil(cols/128)] holds the bytes."""
+    rows, cols = x.shape
+    q = _u8((rows, cols), x.device)
+    ld_s = 4 * ((cols + 511) // 512)
+    s = torch.zeros(((rows + block_rows - 1) // block_rows, ld_s), dtype=torch.uint8, device=x.device)
+    fp8_quant_pow2(x, rows, cols, x.stride(0), block_rows, q, cols, s, ld_s)
+    return q, s
+
+
+def gemm_pow2(a, sa, b, sb, out_dtype=torch.bfloat16):
+    """C = A B^T with power-of-two scale bytes sa [M, lds_a], sb [N/128, lds_b]."""
+    M, K = a.shape
+    N = b.shape[0]
+    c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    fp8_blockscaled_gemm_pow2(M, N, K, a, a.stride(0), sa, sa.stride(0), b, b.stride(0), sb, sb.stride(0), c, N,
+                              OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
     return c
 
 

@@ -265,6 +265,43 @@ fp8bs_status fp8_moe_combine(const uint16_t* y, int64_t rows, int64_t H, int64_t
                              void* out, int64_t ld_out, fp8bs_out out_type, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_quant_pow2 / fp8_blockscaled_gemm_pow2 -- the block-wise recipe with
+ * power-of-two scales: the form TransformerEngine uses when it runs the
+ * 1x128 / 128x128 recipe on Blackwell through MXFP8 ("Low Precision RL",
+ * section "2. Unified block-wise FP8 (DeepSeek-style)", on
+ * NVTE_FP8_BLOCK_SCALING_FP32_SCALES).  Each group's scale is 2^e with e the
+ * smallest integer such that max|x| <= 448 * 2^e, clamped to [-127, 127]
+ * (-127 for an all-zero group), stored as the UE8M0 byte e + 127; the codes
+ * are E4M3(x * 2^-e) (exact scaling, one rounding).  The GEMM applies the
+ * scales inside the scaled matrix instruction (exact), so it needs no
+ * per-slice FP32 promotion.
+ *
+ * fp8_quant_pow2:
+ *   block_rows : 1 (1x128 groups along each row) or 128 (128x128 blocks).
+ *   x : bf16 [rows][ld_x];  q : [rows][ld_q];
+ *   s : uint8, byte of (row group i, column group g = col / 128) at
+ *       s[i * ld_s + g], i = row / block_rows.
+ *   Requirements: cols % 8 == 0; ld_x % 8 == 0, x 16-byte aligned;
+ *   ld_q >= cols, ld_q % 8 == 0, q 8-byte aligned; ld_s >= ceil(cols / 128).
+ *   For the GEMM, choose ld_s % 4 == 0 and ld_s >= 4 * ceil(cols / 512).
+ *
+ * fp8_blockscaled_gemm_pow2:  C = A B^T,
+ *   C[m, n] = sum_kb 2^(sa(m, kb) - 127) * 2^(sb(n/128, kb) - 127) * sum_{k in kb} dec(a[m,k]) dec(b[n,k])
+ *   a : [M][lda] codes (1x128 groups), sa(m, kb) = sa[m * lds_a + kb];
+ *   b : [N][ldb] codes (128x128 blocks), sb(n / 128, kb) = sb[(n / 128) * lds_b + kb];
+ *   c : [M][ldc] bf16 or fp32.
+ *   Requirements: as fp8_blockscaled_gemm for a, b, c; lds_a and lds_b
+ *   multiples of 4 and >= 4 * ceil(K / 512) (each slice's byte is read with
+ *   the 4-byte word of its group of four slices); sa, sb 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_quant_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block_rows,
+                            uint8_t* q, int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t stream);
+fp8bs_status fp8_blockscaled_gemm_pow2(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                       const uint8_t* sa, int64_t lds_a, const uint8_t* b, int64_t ldb,
+                                       const uint8_t* sb, int64_t lds_b, void* c, int64_t ldc, fp8bs_out out,
+                                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * mxfp8_quant -- MXFP8 quantization: 32 consecutive values along a row share
  * one UE8M0 scale ("Low Precision RL", section "3. Unified MXFP8
  * (Blackwell)").  The block exponent is the smallest integer e with
