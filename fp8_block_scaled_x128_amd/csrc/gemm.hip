@@ -65,7 +65,9 @@ constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
 // right after the fragment reads lets the current activation buffer be
 // refilled at once.  A slice's copies are issued kLeadA / kLeadB steps before
 // it is consumed.
-template <int WAVES, int NF>
+// ROWSC: the weight scales are per row (ROW128, MX), copied in 64-row pieces,
+// so their LDS region is padded to whole pieces.
+template <int WAVES, int NF, bool ROWSC = false>
 struct Cfg {
     static constexpr int kWaves = WAVES;
     static constexpr int kNF = NF;
@@ -79,7 +81,7 @@ struct Cfg {
     // the second); 256x128 tile: 3 + 2 without the second barrier is 2-3%
     // faster than with it.
     static constexpr int kBStages = 3;
-    static constexpr int kBStageBytes = BN * BK + BN * 4;   // weight tile + weight scales
+    static constexpr int kBStageBytes = BN * BK + (ROWSC ? (BN + 63) / 64 * 64 : BN) * 4;   // weight tile + scales
     static constexpr int kABufBytes = BM * BK + BM * 4;     // activation tile + activation scales
     static constexpr int kAStages = kBStages * kBStageBytes + 2 * kABufBytes <= 160 * 1024 ? 2 : 1;
     static constexpr bool kABarrier = kAStages == 1;
@@ -222,11 +224,11 @@ __device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
 
 template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF>
 __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p) {
-    using C = Cfg<WAVES, NF>;
+    using C = Cfg<WAVES, NF, (MODE == MODE_ROW128 || MODE == MODE_MX)>;
     constexpr int BM = C::BM, BN = C::BN;
-    // per-row weight scales are copied by waves 0..3 in 64-row pieces
-    static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || NF == 8,
-                  "ROW128 and MX modes use 256-row weight tiles");
+    // per-row weight scales are copied by waves 0 .. ceil(BN / 64) - 1 in 64-row pieces
+    static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || (BN + 63) / 64 <= WAVES,
+                  "one wave per 64 rows of per-row weight scales");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
     __shared__ int s_tile[3];
 
@@ -347,10 +349,13 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         offA[j] = (uint32_t)((int64_t)arow(row) * p.lda + chunk * 16);
     }
     // Scale copies (4-byte lanes).  Activation scales: waves [0, BM/64) copy
-    // rows [64 w, +64).  Weight scales: MODE_BLOCK128 -> wave BM/64 copies the
-    // two 128-row blocks of the tile; ROW128 / MX -> waves 0..3 copy rows [64 w, +64).
+    // rows [64 w, +64).  Weight scales: BLOCK128 / P2 -> wave BM/64 copies the
+    // two 128-row blocks of the tile; ROW128 / MX -> waves [0, ceil(BN/64))
+    // copy rows [64 w, +64) (the last piece may pass the tile's rows: they
+    // land in the padded scale region and read clamped rows of B's scales).
     const bool has_sa = MODE != MODE_KINV && wave < BM / 64;
-    const bool has_sb = MODE != MODE_KINV && ((MODE == MODE_BLOCK128 || MODE == MODE_P2) ? wave == BM / 64 : wave < 4);
+    const bool has_sb = MODE != MODE_KINV &&
+                        ((MODE == MODE_BLOCK128 || MODE == MODE_P2) ? wave == BM / 64 : wave < (BN + 63) / 64);
     uint32_t sa_off = 0, sb_off = 0;            // byte offsets without the slice term (< 4 GiB)
     if (has_sa) {
         const int m = arow(wave * 64 + lane);
@@ -749,11 +754,10 @@ hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st) {
     const bool kinv = g.sa_sk == 0 && g.sb_sk == 0;
     p.kinv_row = g.bscale_row ? 1 : 0;
     auto go = [&](int ci, const KArgs& q) {
-        return kinv ? launch_dense<MODE_KINV>(ci, q, g.out_f32, st) : launch_dense<MODE_BLOCK128>(ci, q, g.out_f32, st);
+        if (kinv) return launch_dense<MODE_KINV>(ci, q, g.out_f32, st);
+        if (g.bscale_row) return launch_dense<MODE_ROW128>(ci, q, g.out_f32, st);
+        return launch_dense<MODE_BLOCK128>(ci, q, g.out_f32, st);
     };
-    if (g.bscale_row && !kinv)
-        return waves_for(g.M, g.N) == 8 ? launch<MODE_ROW128, false, 8, 8>(p, g.out_f32, st)
-                                        : launch<MODE_ROW128, false, 4, 8>(p, g.out_f32, st);
     const DensePlan plan = plan_dense(g.M, g.N, g.K);
     if (plan.c2 < 0) return go(plan.c1, p);
     KArgs p1 = p, p2 = p;
@@ -807,9 +811,19 @@ hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st) {
     KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, g.c, g.ldc);
     p.sa_sm = g.lds_a; p.sa_sk = 1; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.lds_b; p.sb_sk = 1;
     p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
-    if (g.G == 0)
-        return waves_for(g.M, g.N) == 8 ? launch<MODE_MX, false, 8, 8>(p, g.out_f32, st)
-                                        : launch<MODE_MX, false, 4, 8>(p, g.out_f32, st);
+    if (g.G == 0) {
+        const DensePlan plan = plan_dense(g.M, g.N, g.K);
+        if (plan.c2 < 0) return launch_dense<MODE_MX>(plan.c1, p, g.out_f32, st);
+        KArgs p1 = p, p2 = p;
+        p1.N = (int32_t)plan.split;
+        p2.N = (int32_t)(g.N - plan.split);
+        p2.b = p.b + plan.split * p.ldb;
+        p2.sb = p.sb + plan.split * p.sb_sn;
+        p2.c = static_cast<uint8_t*>(p.c) + plan.split * (g.out_f32 ? 4 : 2);
+        const hipError_t e = launch_dense<MODE_MX>(plan.c1, p1, g.out_f32, st);
+        if (e != hipSuccess) return e;
+        return launch_dense<MODE_MX>(plan.c2, p2, g.out_f32, st);
+    }
     return waves_for(g.M, g.N, g.G / 2) == 8 ? launch<MODE_MX, true, 8, 8>(p, g.out_f32, st)
                                               : launch<MODE_MX, true, 4, 8>(p, g.out_f32, st);
 }

@@ -123,6 +123,35 @@ def test_exact_integer_case_every_tiling(shape, plan):
     assert np.array_equal(y16[mi, ni], oracle.f64_to_bf16(yref))
 
 
+@pytest.mark.parametrize("shape,plan", PLAN_CASES)
+def test_row_scale_modes_exact_every_tiling(shape, plan):
+    """The modes with per-row weight scales on every planned tiling: ROW128
+    (FP32 scales per weight row and 128-K slice, the wgrad GEMM) and dense
+    MXFP8 (UE8M0 per row and 32-K block).  Power-of-two scales and small
+    integer codes make every sum exact: sampled outputs, the last rows and
+    columns and the columns around a region boundary, bit for bit."""
+    M, N, K = shape
+    _say("row-scale modes", shape, plan)
+    rng = np.random.default_rng(M + 2 * N)
+    qa = oracle.e4m3_encode(rng.integers(-8, 9, size=(M, K)).astype(np.float32))
+    qb = oracle.e4m3_encode(rng.integers(-8, 9, size=(N, K)).astype(np.float32))
+    sa = np.exp2(rng.integers(-1, 2, size=(M, K // 128))).astype(np.float32)
+    sb = np.exp2(rng.integers(-1, 2, size=(N, K // 128))).astype(np.float32)
+    ea = rng.integers(126, 129, size=(M, K // 32)).astype(np.uint8)
+    eb = rng.integers(126, 129, size=(N, K // 32)).astype(np.uint8)
+    y_row = ops.gemm(dev(qa), dev(sa), dev(qb), dev(sb), ops.BSCALE_ROW128, torch.float32)
+    y_mx = ops.mx_gemm(dev(qa), dev(ea), dev(qb), dev(eb))
+    torch.cuda.synchronize()
+    mi, ni = sample_indices(M, N, 4000, 4)
+    edge_cols = np.unique(np.concatenate([np.arange(N - 48, N), np.arange(max(plan[2] - 48, 0), min(plan[2] + 48, N))]))
+    mi = np.concatenate([mi, np.repeat(np.arange(M - 4, M), N), np.repeat(np.arange(0, M, 7), edge_cols.size)])
+    ni = np.concatenate([ni, np.tile(np.arange(N), 4), np.tile(edge_cols, (M + 6) // 7)])
+    yref, _ = oracle.gemm_blockscaled_sampled(qa, sa, qb, sb, mi, ni, oracle.BSCALE_ROW128)
+    assert np.array_equal(host(y_row)[mi, ni].astype(np.float64), yref)
+    yref, _ = oracle.gemm_mx_sampled(qa, ea, qb, eb, mi, ni)
+    assert np.array_equal(host(y_mx)[mi, ni].astype(np.float64), yref)
+
+
 @pytest.mark.parametrize("M,N,K", [(3000, 2560, 640), (1000, 1408, 384)])
 def test_other_tilings_real_data(M, N, K):
     """Quantized N(0,1) activations with outliers and N(0, 0.02) weights on the
