@@ -67,23 +67,32 @@ constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
 // it is consumed.
 // ROWSC: the weight scales are per row (ROW128, MX), copied in 64-row pieces,
 // so their LDS region is padded to whole pieces.
-template <int WAVES, int NF, bool ROWSC = false>
+template <int WAVES, int NF, bool ROWSC = false, int WN = 2>
 struct Cfg {
     static constexpr int kWaves = WAVES;
     static constexpr int kNF = NF;
     static constexpr int kThreads = WAVES * 64;
-    static constexpr int BN = 32 * NF;
-    static constexpr int BM = 64 * (WAVES / 2);
+    static constexpr int BN = 16 * NF * WN;
+    static constexpr int BM = 64 * (WAVES / WN);
     static constexpr bool kDefer = true;
+    // Workgroups resident per compute unit.  A 4-wave tile with one wave
+    // column (WN = 1) is sized for two per CU: each SIMD then runs two waves
+    // of different workgroups, so one workgroup's barriers, fragment reads,
+    // pipeline fill and output writes overlap the other's matrix work (the
+    // two waves of a SIMD in an 8-wave workgroup meet the same barriers).
+    static constexpr int kPerCU = WN == 1 ? 2 : 1;
+    static constexpr int kMinWavesPerEU = kPerCU * WAVES / 4;
+    static constexpr int kLdsMax = 160 * 1024 / kPerCU;
     // Measured on the MLP shapes (M 4096; N 9728, K 2560 and N 2560, K 9728):
     // 256x256 tile: 3 weight stages + 1 activation buffer with the second
     // barrier beats 2 + 2 without it (equal on the first shape, 9% faster on
     // the second); 256x128 tile: 3 + 2 without the second barrier is 2-3%
-    // faster than with it.
-    static constexpr int kBStages = 3;
+    // faster than with it.  Two workgroups per CU leave room for 2 weight
+    // stages and 1 activation buffer.
+    static constexpr int kBStages = kPerCU == 2 ? 2 : 3;
     static constexpr int kBStageBytes = BN * BK + (ROWSC ? (BN + 63) / 64 * 64 : BN) * 4;   // weight tile + scales
     static constexpr int kABufBytes = BM * BK + BM * 4;     // activation tile + activation scales
-    static constexpr int kAStages = kBStages * kBStageBytes + 2 * kABufBytes <= 160 * 1024 ? 2 : 1;
+    static constexpr int kAStages = kBStages * kBStageBytes + 2 * kABufBytes <= kLdsMax ? 2 : 1;
     static constexpr bool kABarrier = kAStages == 1;
     static constexpr int kLdsBytes = kBStages * kBStageBytes + kAStages * kABufBytes;
     // 16-byte copies per wave per slice: a wave copy moves 8 rows.  When the
@@ -103,7 +112,7 @@ struct Cfg {
     // That count assumes the steps in between issued full copies, which holds
     // for leads of 1 or 2 (a step short of copies is then the last one).
     static_assert(kLeadA >= 1 && kLeadB >= 1 && kLeadMax <= 2, "pipeline leads must be 1 or 2");
-    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    static_assert(kLdsBytes + 64 <= kLdsMax, "LDS budget");
     static_assert(kDmaA <= NF, "one activation copy per n-tile step");
     // tile copy slots: activation copy t in n-tile step t; weight copies
     // after the activation copies when they must follow them, else in step t
@@ -222,9 +231,10 @@ __device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
 }
 
-template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF>
-__global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p) {
-    using C = Cfg<WAVES, NF, (MODE == MODE_ROW128 || MODE == MODE_MX)>;
+template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF, int WN>
+__global__ void __launch_bounds__((Cfg<WAVES, NF, false, WN>::kThreads), (Cfg<WAVES, NF, false, WN>::kMinWavesPerEU))
+k_gemm(KArgs p) {
+    using C = Cfg<WAVES, NF, (MODE == MODE_ROW128 || MODE == MODE_MX), WN>;
     constexpr int BM = C::BM, BN = C::BN;
     // per-row weight scales are copied by waves 0 .. ceil(BN / 64) - 1 in 64-row pieces
     static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || (BN + 63) / 64 <= WAVES,
@@ -234,7 +244,7 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = WN == 2 ? (wave & 1) : 0, wm = WN == 2 ? (wave >> 1) : wave;
     const int q = lane >> 4, r16 = lane & 15;
     const FragOff fo = frag_off(r16, q);
 
@@ -349,13 +359,13 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
         offA[j] = (uint32_t)((int64_t)arow(row) * p.lda + chunk * 16);
     }
     // Scale copies (4-byte lanes).  Activation scales: waves [0, BM/64) copy
-    // rows [64 w, +64).  Weight scales: BLOCK128 / P2 -> wave BM/64 copies the
+    // rows [64 w, +64).  Weight scales: BLOCK128 / P2 -> wave (BM/64) % WAVES copies the
     // two 128-row blocks of the tile; ROW128 / MX -> waves [0, ceil(BN/64))
     // copy rows [64 w, +64) (the last piece may pass the tile's rows: they
     // land in the padded scale region and read clamped rows of B's scales).
     const bool has_sa = MODE != MODE_KINV && wave < BM / 64;
     const bool has_sb = MODE != MODE_KINV &&
-                        ((MODE == MODE_BLOCK128 || MODE == MODE_P2) ? wave == BM / 64 : wave < (BN + 63) / 64);
+                        ((MODE == MODE_BLOCK128 || MODE == MODE_P2) ? wave == (BM / 64) % WAVES : wave < (BN + 63) / 64);
     uint32_t sa_off = 0, sb_off = 0;            // byte offsets without the slice term (< 4 GiB)
     if (has_sa) {
         const int m = arow(wave * 64 + lane);
@@ -597,10 +607,9 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
     // N % 128 == 0: with 256-row tiles each wave covers 128 aligned n, so a
     // wave's columns are all inside the matrix or all outside; other tiles
     // check each 16-column n-tile (wave-uniform).  Rows are checked per lane.
-    // One base address per m-tile, the n-tiles at constant offsets from it.
     const int nw0 = n0 + wn * 16 * NF;
-    if (nw0 >= p.N) return;
-    if (MODE == MODE_KINV) {
+    const bool wave_out = nw0 < p.N;
+    if (MODE == MODE_KINV && wave_out) {
         // scales constant along K: each output times sa(m) * sb(n), once
         const float* sa = reinterpret_cast<const float*>(p.sa);
         const float* sb = reinterpret_cast<const float*>(p.sb);
@@ -618,31 +627,59 @@ __global__ void __launch_bounds__((Cfg<WAVES, NF>::kThreads), 1) k_gemm(KArgs p)
                 }
         }
     }
+    // The outputs leave through LDS so that every store writes whole rows:
+    // a lane holds 4 consecutive columns of one row per 16 x 16 block, and
+    // storing those directly makes each store instruction write 32-byte
+    // pieces of 16 different rows.  Each wave stages its 64 x 16 NF block in
+    // passes of 32 rows (row pitch padded by 16 bytes to spread the banks)
+    // and reads it back in 16-byte pieces of consecutive columns.  The first
+    // barrier frees the operand buffers; afterwards each wave touches only
+    // its own staging region, whose LDS accesses complete in program order.
+    constexpr int EB = OUTF32 ? 4 : 2;                 // output bytes per element
+    constexpr int kRows = 32;                          // rows per pass
+    constexpr int kPitch = 16 * NF * EB + 16;          // staged row, bytes
+    constexpr int kChunks = 16 * NF * EB / 16;         // 16-byte pieces per row
+    static_assert(WAVES * kRows * kPitch <= C::kLdsBytes, "epilogue staging fits the operand buffers");
+    static_assert((kRows * kChunks) % 64 == 0, "whole store instructions per pass");
+    __syncthreads();
+    if (!wave_out) return;
+    const uint32_t wst = lds0 + (uint32_t)(wave * kRows * kPitch);
+    uint8_t* cbase = static_cast<uint8_t*>(p.c) + (int64_t)nw0 * EB;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int m = m_begin + wm * 64 + mt * 16 + r16;
-        if (m >= m_end) continue;
-        if (OUTF32) {
-            float* dst = static_cast<float*>(p.c) + (int64_t)m * p.ldc + nw0 + 4 * q;
+    for (int pass = 0; pass < 64 / kRows; ++pass) {
 #pragma unroll
-            for (int nt = 0; nt < NF; ++nt)
-                if (NF == 8 || nw0 + nt * 16 < p.N)
-                    *reinterpret_cast<float4*>(dst + nt * 16) =
-                    make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
-        } else {
-            uint16_t* dst = static_cast<uint16_t*>(p.c) + (int64_t)m * p.ldc + nw0 + 4 * q;
+        for (int h = 0; h < kRows / 16; ++h) {
+            const int mt = pass * (kRows / 16) + h;
+            const uint32_t rowa = wst + (uint32_t)((h * 16 + r16) * kPitch + 4 * q * EB);
 #pragma unroll
-            for (int nt = 0; nt < NF; ++nt)
-                if (NF == 8 || nw0 + nt * 16 < p.N)
-                    *reinterpret_cast<uint2*>(dst + nt * 16) =
-                        make_uint2(pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]), pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3]));
+            for (int nt = 0; nt < NF; ++nt) {
+                const uint32_t a = rowa + nt * 16 * EB;
+                if (OUTF32) {
+                    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>((uintptr_t)a) =
+                        f32x4{acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]};
+                } else {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)a) =
+                        u32x2{pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]), pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3])};
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < kRows * kChunks / 64; ++it) {
+            const int sidx = it * 64 + lane;
+            const int row = sidx / kChunks, ch = sidx % kChunks;
+            const u32x4 v = lds_read16(wst + (uint32_t)(row * kPitch + ch * 16));
+            const int m = m_begin + wm * 64 + pass * kRows + row;
+            const int col = ch * (16 / EB);
+            if (m < m_end && (NF == 8 || nw0 + col < p.N))
+                *reinterpret_cast<u32x4*>(cbase + ((int64_t)m * p.ldc) * EB + col * EB) = v;
         }
     }
 }
 
-template <int MODE, bool GROUPED, int WAVES, int NF>
+template <int MODE, bool GROUPED, int WAVES, int NF, int WN = 2>
 hipError_t launch(const KArgs& p, bool out_f32, hipStream_t st) {
-    using C = Cfg<WAVES, NF>;
+    using C = Cfg<WAVES, NF, false, WN>;
     dim3 grid;
     if (!GROUPED) {
         grid = dim3((unsigned)(((int64_t)(p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN)));
@@ -653,9 +690,9 @@ hipError_t launch(const KArgs& p, bool out_f32, hipStream_t st) {
         grid = dim3((unsigned)((items + 7) / 8 * 8));
     }
     if (out_f32)
-        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES, NF>), grid, dim3(C::kThreads), 0, st, p);
+        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES, NF, WN>), grid, dim3(C::kThreads), 0, st, p);
     else
-        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false, WAVES, NF>), grid, dim3(C::kThreads), 0, st, p);
+        hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false, WAVES, NF, WN>), grid, dim3(C::kThreads), 0, st, p);
     return hipGetLastError();
 }
 
@@ -672,28 +709,43 @@ int waves_for(int64_t rows, int64_t N, int64_t extra_tiles = 0) {
 
 // Dense BLOCK128 plans.  The output columns (weight rows) are cut into at
 // most two regions, each tiled with one configuration, so that the tiles
-// fill whole rounds over the compute units where the 256-row tile would
-// leave most of a round idle (N 2560 at M 4096: 160 tiles of 256 x 256 for
-// 256 CUs, against 256 tiles of 160 x 256).  The estimate per region is
-// rounds x (K slices x cycles per slice + cycles per tile), with the cycle
-// figures measured per configuration on the MLP shapes.
+// fill whole rounds over the compute units where a single tiling would
+// leave most of a round idle (N 2560 at M 4096: 320 tiles of 128 x 256 or
+// 160 of 256 x 256 for 256 CUs, against 256 tiles of 160 x 256).  The
+// estimate per region is rounds x (K slices x cycles per slice + cycles per
+// tile), with the cycle figures fitted to the MLP shapes (M 4096; N 9728,
+// K 2560; N 2560, K 9728; and M 9728, N 2560, K 4096).  For the 128 x 256
+// tile a round is two tiles per CU; a last round of at most one tile per CU
+// runs each tile at its lone speed, only about 12% faster per slice (a lone
+// 4-wave workgroup leaves each SIMD one wave, so pairs nearly double the
+// throughput).
 constexpr int kCUs = 256;
 struct TileCfg {
-    int waves, nf;
-    double slice_cycles, tile_cycles;
+    int waves, nf, wn;
+    double slice_cycles, tile_cycles;   // per round of tiles (wn = 1: two tiles per CU)
+    double lone_slice_cycles;           // wn = 1: one tile on the CU
 };
 constexpr TileCfg kDenseCfgs[] = {
-    {8, 8, 3440, 14000},   // 256 x 256
-    {4, 8, 2530, 10000},   // 256 x 128
-    {8, 5, 2520, 10000},   // 160 x 256
-    {4, 6, 2110, 8000},    // 192 x 128
+    {8, 8, 2, 3300, 9000, 0},       // 256 x 256
+    {4, 8, 2, 2450, 7000, 0},       // 256 x 128
+    {8, 5, 2, 2520, 8000, 0},       // 160 x 256
+    {4, 6, 2, 2400, 6000, 0},       // 192 x 128
+    {4, 8, 1, 3100, 8000, 2700},    // 128 x 256, two per CU
 };
-constexpr double kLaunchCycles = 5000;       // a second launch on the stream
+// A second launch on the stream: its ramp-up and the first region's tail.
+constexpr double kLaunchCycles = 15000;
+
+int64_t cfg_bn(const TileCfg& c) { return 16 * c.nf * c.wn; }
+int64_t cfg_bm(const TileCfg& c) { return 64 * c.waves / c.wn; }
 
 double region_cycles(const TileCfg& c, int64_t M, int64_t N, int64_t nk) {
-    const int64_t bm = 32 * c.waves, bn = 32 * c.nf;
+    const int64_t bm = cfg_bm(c), bn = cfg_bn(c);
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-    return (double)((tiles + kCUs - 1) / kCUs) * ((double)nk * c.slice_cycles + c.tile_cycles);
+    const double round = (double)nk * c.slice_cycles + c.tile_cycles;
+    if (c.wn != 1) return (double)((tiles + kCUs - 1) / kCUs) * round;
+    const int64_t full = tiles / (2 * kCUs), rest = tiles % (2 * kCUs);
+    const double last = rest == 0 ? 0.0 : rest <= kCUs ? (double)nk * c.lone_slice_cycles + c.tile_cycles : round;
+    return (double)full * round + last;
 }
 
 struct DensePlan {
@@ -710,7 +762,7 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K) {
         const double t = region_cycles(kDenseCfgs[i], M, N, nk);
         if (t < best_t) { best_t = t; best = DensePlan{i, -1, N}; }
         // region 1 in whole tiles of configuration i, on a 128-column boundary
-        const int64_t bn = 32 * kDenseCfgs[i].nf;
+        const int64_t bn = cfg_bn(kDenseCfgs[i]);
         for (int64_t split = bn; split < N; split += bn) {
             if (split % 128) continue;
             const double t1 = region_cycles(kDenseCfgs[i], M, split, nk);
@@ -730,7 +782,8 @@ hipError_t launch_dense(int ci, const KArgs& p, bool out_f32, hipStream_t st) {
         case 0: return launch<MODE, false, 8, 8>(p, out_f32, st);
         case 1: return launch<MODE, false, 4, 8>(p, out_f32, st);
         case 2: return launch<MODE, false, 8, 5>(p, out_f32, st);
-        default: return launch<MODE, false, 4, 6>(p, out_f32, st);
+        case 3: return launch<MODE, false, 4, 6>(p, out_f32, st);
+        default: return launch<MODE, false, 4, 8, 1>(p, out_f32, st);
     }
 }
 
@@ -774,9 +827,9 @@ hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st) {
 void plan_gemm_blockscaled(int64_t M, int64_t N, int64_t K, int32_t out[5]) {
     const DensePlan plan = plan_dense(M, N, K);
     out[0] = kDenseCfgs[plan.c1].waves;
-    out[1] = 32 * kDenseCfgs[plan.c1].nf;
+    out[1] = (int32_t)cfg_bn(kDenseCfgs[plan.c1]);
     out[2] = plan.c2 < 0 ? 0 : kDenseCfgs[plan.c2].waves;
-    out[3] = plan.c2 < 0 ? 0 : 32 * kDenseCfgs[plan.c2].nf;
+    out[3] = plan.c2 < 0 ? 0 : (int32_t)cfg_bn(kDenseCfgs[plan.c2]);
     out[4] = (int32_t)plan.split;
 }
 

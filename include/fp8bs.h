@@ -183,7 +183,9 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
  *                     output columns [0, plan[4]);
  *   plan[2], plan[3]  the same for columns [plan[4], N), or 0, 0 when one
  *                     tiling covers all columns (then plan[4] == N);
- *   a tile covers 32 * waves activation rows (m).
+ *   a tile covers 32 * waves activation rows (m), except the tile of 128
+ *   weight rows (4 waves, two workgroups per compute unit), which covers
+ *   256.
  * Requirements: M, N, K >= 0; K % 128 == 0; N % 128 == 0.
  * ------------------------------------------------------------------------ */
 fp8bs_status fp8_blockscaled_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t* plan);

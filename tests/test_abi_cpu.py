@@ -93,7 +93,7 @@ def test_dense_tile_plan(lib):
     every region's tiling is one the library builds, and the MLP shapes get
     tilings that fill whole rounds of 256 compute units."""
     from fp8_block_scaled_x128_amd import ops
-    tilings = {(8, 256), (4, 256), (8, 160), (4, 192)}
+    tilings = {(8, 256), (4, 256), (8, 160), (4, 192), (4, 128)}
     for M in (1, 130, 1000, 4096, 4100, 16384):
         for N in (128, 640, 1408, 2560, 4096, 9728):
             for K in (128, 2560, 9728):
@@ -104,9 +104,10 @@ def test_dense_tile_plan(lib):
                 else:
                     assert second in tilings and second != first
                     assert 0 < split < N and split % 128 == 0 and split % first[1] == 0
-    # down projection: 16 x 16 tiles of 160 x 256; up projection: two full
-    # rounds of 256 x 256 tiles, then one round of 192 x 128 tiles
+    # down projection: 16 x 16 tiles of 160 x 256; up projection and wgrad:
+    # 128 x 256 tiles, two per compute unit
     assert ops.fp8_blockscaled_gemm_plan(4096, 2560, 9728) == ((8, 160), None, 2560)
-    assert ops.fp8_blockscaled_gemm_plan(4096, 9728, 2560) == ((8, 256), (4, 192), 8192)
+    assert ops.fp8_blockscaled_gemm_plan(4096, 9728, 2560) == ((4, 128), None, 9728)
+    assert ops.fp8_blockscaled_gemm_plan(9728, 2560, 4096) == ((4, 128), None, 2560)
     assert lib.fp8_blockscaled_gemm_plan(128, 100, 128, ctypes.c_void_p(1 << 20)) == 2
     assert lib.fp8_blockscaled_gemm_plan(128, 128, 128, None) == 1

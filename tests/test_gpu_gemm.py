@@ -91,17 +91,18 @@ def _plan(M, N, K):
     return ((w1, n1), second, split)
 
 
-# Every dense tiling, each on a shape that the planner routes to it: M not a
+# Every tiling the dense planner chooses (the 256 x 256 tile serves grouped
+# problems only), each on a shape that the planner routes to it: M not a
 # multiple of the tile's rows, N not a multiple of its columns where the
-# tiling allows, and both two-region plans.
+# tiling allows, and the two-region plans.
 PLAN_CASES = [
-    ((4100, 2688, 512), ((8, 256), None, 2688)),
-    ((3000, 2560, 640), ((8, 160), None, 2560)),
-    ((4100, 4096, 512), ((8, 160), None, 4096)),
-    ((1000, 1408, 384), ((4, 192), None, 1408)),
-    ((130, 128, 128), ((4, 192), None, 128)),
-    ((4096, 9728, 512), ((8, 256), (4, 192), 8192)),
-    ((4100, 9728, 384), ((8, 256), (8, 160), 7424)),
+    ((1000, 10368, 384), ((4, 128), None, 10368)),
+    ((1000, 8448, 384), ((8, 160), None, 8448)),
+    ((1000, 6272, 384), ((4, 256), None, 6272)),
+    ((130, 128, 384), ((4, 192), None, 128)),
+    ((3200, 10112, 2048), ((4, 256), (4, 128), 5120)),
+    ((2816, 9344, 4096), ((4, 128), (8, 160), 5760)),
+    ((1664, 14464, 4096), ((8, 160), (4, 128), 5120)),
 ]
 
 
