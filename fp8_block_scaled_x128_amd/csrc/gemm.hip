@@ -240,7 +240,7 @@ k_gemm(KArgs p) {
     static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || (BN + 63) / 64 <= WAVES,
                   "one wave per 64 rows of per-row weight scales");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
-    __shared__ int s_tile[3];
+    __shared__ int s_tile[5];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,15 +287,41 @@ k_gemm(KArgs p) {
         const int ntn = (p.N + BN - 1) / BN;
         if (threadIdx.x == 0) s_tile[0] = -1;
         if (wave == 0) {
-            int total = 0;
-            for (int gb = 0; gb < p.G; gb += 128) {
+            // lane l looks at groups gb + 2l and gb + 2l + 1: their row
+            // bounds o0..o1, o1..o2 and row-tile counts c0, c1
+            int o0 = 0, o1 = 0, o2 = 0, c0 = 0, c1 = 0, incl = 0;
+            auto load = [&](int gb) {
                 const int g0 = gb + 2 * lane, g1 = g0 + 1;
-                int c = 0;
-                if (g0 < p.G) c += (p.offsets[g0 + 1] - p.offsets[g0] + BM - 1) / BM;
-                if (g1 < p.G) c += (p.offsets[g1 + 1] - p.offsets[g1] + BM - 1) / BM;
+                o0 = g0 < p.G ? p.offsets[g0] : 0;
+                o1 = g0 < p.G ? p.offsets[g0 + 1] : 0;
+                o2 = g1 < p.G ? p.offsets[g1 + 1] : 0;
+                c0 = g0 < p.G ? (o1 - o0 + BM - 1) / BM : 0;
+                c1 = g1 < p.G ? (o2 - o1 + BM - 1) / BM : 0;
+            };
+            auto scan = [&]() {
+                incl = c0 + c1;
 #pragma unroll
-                for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
-                total += c;
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int v = __shfl_up(incl, d, 64);
+                    if (lane >= d) incl += v;
+                }
+            };
+            // up to 128 groups: one load of the offsets serves both the
+            // total and the prefix sums
+            const bool one_pass = p.G <= 128;
+            int total = 0;
+            if (one_pass) {
+                load(0);
+                scan();
+                total = __shfl(incl, 63, 64);
+            } else {
+                for (int gb = 0; gb < p.G; gb += 128) {
+                    load(gb);
+                    int c = c0 + c1;
+#pragma unroll
+                    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+                    total += c;
+                }
             }
             const int items = total * ntn;
             const int per = (items + 7) / 8;
@@ -303,32 +329,36 @@ k_gemm(KArgs p) {
             const int item = bid / 8 < per ? (bid % 8) * per + bid / 8 : items;
             const int t = item < items ? item / ntn : -1;   // row tile, -1: no work
             if (lane == 0) s_tile[2] = item - (item / ntn) * ntn;
-            int carry = 0;
-            for (int gb = 0; gb < p.G; gb += 128) {
-                const int g0 = gb + 2 * lane, g1 = g0 + 1;
-                const int o0 = g0 < p.G ? p.offsets[g0] : 0, o1 = g0 < p.G ? p.offsets[g0 + 1] : 0;
-                const int o2 = g1 < p.G ? p.offsets[g1 + 1] : 0;
-                const int c0 = g0 < p.G ? (o1 - o0 + BM - 1) / BM : 0;
-                const int c1 = g1 < p.G ? (o2 - o1 + BM - 1) / BM : 0;
-                int incl = c0 + c1;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int v = __shfl_up(incl, d, 64);
-                    if (lane >= d) incl += v;
-                }
+            // the lane whose group holds row tile t publishes the group, the
+            // tile's index in it and the group's row bounds
+            auto place = [&](int gb, int carry) {
                 const int start0 = carry + incl - (c0 + c1);
                 const int start1 = start0 + c0;
-                if (t >= start0 && t < start0 + c0) { s_tile[0] = g0; s_tile[1] = t - start0; }
-                if (t >= start1 && t < start1 + c1) { s_tile[0] = g1; s_tile[1] = t - start1; }
-                carry += __shfl(incl, 63, 64);
+                if (t >= start0 && t < start0 + c0) {
+                    s_tile[0] = gb + 2 * lane; s_tile[1] = t - start0; s_tile[3] = o0; s_tile[4] = o1;
+                }
+                if (t >= start1 && t < start1 + c1) {
+                    s_tile[0] = gb + 2 * lane + 1; s_tile[1] = t - start1; s_tile[3] = o1; s_tile[4] = o2;
+                }
+            };
+            if (one_pass) {
+                place(0, 0);
+            } else {
+                int carry = 0;
+                for (int gb = 0; gb < p.G; gb += 128) {
+                    load(gb);
+                    scan();
+                    place(gb, carry);
+                    carry += __shfl(incl, 63, 64);
+                }
             }
         }
         __syncthreads();
         const int g = s_tile[0];
         if (g < 0) return;                         // uniform: no tile for this work item
         const int lt = s_tile[1];
-        m_begin = p.offsets[g] + lt * BM;
-        m_end = min(p.offsets[g + 1], m_begin + BM);
+        m_begin = s_tile[3] + lt * BM;
+        m_end = min(s_tile[4], m_begin + BM);
         n0 = s_tile[2] * BN;
         bptr += (int64_t)g * p.b_sg;
         sbp += (int64_t)g * p.sb_sg * ((MODE == MODE_MX || MODE == MODE_P2) ? 1 : 4);

@@ -291,6 +291,31 @@ def test_grouped_exact_integer_case():
     assert np.array_equal(host(c).astype(np.float64), yref)
 
 
+def test_grouped_exact_integer_case_many_groups():
+    """More than 128 groups (the work-item lookup then walks the offsets in
+    chunks of 128 groups), many of them empty: bit-exact."""
+    rng = np.random.default_rng(12)
+    G, N, K = 300, 256, 256
+    counts = np.where(rng.random(G) < 0.3, 0, rng.integers(1, 300, G))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    qa, sa, _, _ = _exact_case(rows, 128, K, 13)
+    qbs, sbs = [], []
+    for g in range(G):
+        _, _, qb, sb = _exact_case(128, N, K, 1000 + g)
+        qbs.append(qb)
+        sbs.append(sb)
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    yref, _ = oracle.grouped_gemm_blockscaled(qa, sa, offsets, qb, sb)
+    _say("grouped, %d groups, %d rows" % (G, rows))
+    c = torch.zeros((rows, N), dtype=torch.float32, device="cuda")
+    dsa, dqb, dsb = dev(sa), dev(qb), dev(sb)
+    ops.fp8_grouped_gemm(rows, N, K, G, dev(offsets), None, rows, dev(qa), K, dsa, dsa.stride(0), dsa.stride(1),
+                         dqb, K, N * K, dsb, dsb.stride(0), dsb.stride(1), dsb.stride(2), c, N, ops.OUT_FP32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c).astype(np.float64), yref)
+
+
 def _group_samples(offsets, N, seed, per_group=20):
     """Per non-empty group: its first and last 3 rows and `per_group` random
     rows, every column; returns {g: (local rows, local cols)}."""
