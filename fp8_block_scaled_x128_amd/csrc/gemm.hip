@@ -171,7 +171,9 @@ __device__ __forceinline__ int lds_readu8(uint32_t addr) {
 // current stage, which serializes the pipeline.  Ordering is explicit
 // instead: s_waitcnt vmcnt(n) on the issuing wave, then s_barrier, before any
 // wave reads a stage.  Copies use the scalar-base form: wave-uniform 64-bit
-// base in SGPRs plus a per-lane 32-bit byte offset (one VGPR per copy).
+// base in SGPRs plus a per-lane 32-bit byte offset (one VGPR per copy).  The
+// K slice advances the scalar base, so the per-lane offsets stay fixed and a
+// copy costs no vector instruction for its address.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_dst) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
@@ -354,12 +356,14 @@ k_gemm(KArgs p) {
             }
         }
         __syncthreads();
-        const int g = s_tile[0];
+        // the lookup results are workgroup-uniform: kept in scalar registers,
+        // so the copies' base addresses need no per-lane arithmetic
+        const int g = __builtin_amdgcn_readfirstlane(s_tile[0]);
         if (g < 0) return;                         // uniform: no tile for this work item
-        const int lt = s_tile[1];
-        m_begin = s_tile[3] + lt * BM;
-        m_end = min(s_tile[4], m_begin + BM);
-        n0 = s_tile[2] * BN;
+        const int lt = __builtin_amdgcn_readfirstlane(s_tile[1]);
+        m_begin = __builtin_amdgcn_readfirstlane(s_tile[3]) + lt * BM;
+        m_end = min(__builtin_amdgcn_readfirstlane(s_tile[4]), m_begin + BM);
+        n0 = __builtin_amdgcn_readfirstlane(s_tile[2]) * BN;
         bptr += (int64_t)g * p.b_sg;
         sbp += (int64_t)g * p.sb_sg * ((MODE == MODE_MX || MODE == MODE_P2) ? 1 : 4);
     }
@@ -423,23 +427,23 @@ k_gemm(KArgs p) {
     auto copy_sb = [&](int kb, int stage) {
         if (!has_sb) return;
         const uint32_t st = bstage(stage) + BN * BK;
-        if (MODE == MODE_MX) dma4(sbp, sb_off + (uint32_t)(kb * 4), st + wave * 64 * 4);
-        else if (MODE == MODE_P2) dma4(sbp, sb_off + (uint32_t)((kb >> 2) * 4), st);   // slices 4(kb/4) .. +3
-        else if (MODE == MODE_BLOCK128) dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st);
-        else dma4(sbp, sb_off + (uint32_t)(kb * p.sb_sk * 4), st + wave * 64 * 4);
+        if (MODE == MODE_MX) dma4(sbp + kb * 4, sb_off, st + wave * 64 * 4);
+        else if (MODE == MODE_P2) dma4(sbp + (kb >> 2) * 4, sb_off, st);   // slices 4(kb/4) .. +3
+        else if (MODE == MODE_BLOCK128) dma4(sbp + kb * p.sb_sk * 4, sb_off, st);
+        else dma4(sbp + kb * p.sb_sk * 4, sb_off, st + wave * 64 * 4);
     };
     auto copy_sa = [&](int kb, int buf) {
         if (!has_sa) return;
         const uint32_t st = abuf(buf) + BM * BK + wave * 64 * 4;
-        if (MODE == MODE_MX) dma4(p.sa, sa_off + (uint32_t)(kb * 4), st);
-        else if (MODE == MODE_P2) dma4(p.sa, sa_off + (uint32_t)((kb >> 2) * 4), st);
-        else dma4(p.sa, sa_off + (uint32_t)(kb * p.sa_sk * 4), st);
+        if (MODE == MODE_MX) dma4(p.sa + kb * 4, sa_off, st);
+        else if (MODE == MODE_P2) dma4(p.sa + (kb >> 2) * 4, sa_off, st);
+        else dma4(p.sa + kb * p.sa_sk * 4, sa_off, st);
     };
     auto copy_a = [&](int kb, int buf, int t) {
-        dma16(p.a, offA[t] + (uint32_t)kb * BK, abuf(buf) + (wave * C::kDmaA + t) * 8 * BK);
+        dma16(p.a + kb * BK, offA[t], abuf(buf) + (wave * C::kDmaA + t) * 8 * BK);
     };
     auto copy_b = [&](int kb, int stage, int t) {
-        dma16(bptr, offB[t] + (uint32_t)kb * BK, bstage(stage) + bcopy(t) * 8 * BK);
+        dma16(bptr + kb * BK, offB[t], bstage(stage) + bcopy(t) * 8 * BK);
     };
 
     v4f acc[NF][4];
