@@ -153,7 +153,7 @@ def test_row_scale_modes_exact_every_tiling(shape, plan):
     assert np.array_equal(host(y_mx)[mi, ni].astype(np.float64), yref)
 
 
-@pytest.mark.parametrize("M,N,K", [(3000, 2560, 640), (1000, 1408, 384)])
+@pytest.mark.parametrize("M,N,K", [(3000, 2688, 384), (1000, 1408, 384)])
 def test_other_tilings_real_data(M, N, K):
     """Quantized N(0,1) activations with outliers and N(0, 0.02) weights on the
     160- and 192-row tilings: every output within tolerance."""

@@ -85,11 +85,12 @@ def test_gemm_pow2_small(M, N, K):
     _check(*_operands(M, N, K, M + N + K))
 
 
-@pytest.mark.parametrize("M,N,K", [(4096, 9728, 2560), (4100, 9728, 384), (4096, 2560, 9728)])
+@pytest.mark.parametrize("M,N,K", [(4096, 9728, 2560), (4100, 9728, 384), (4096, 2560, 9728), (3200, 10112, 2048)])
 def test_gemm_pow2_planned_tilings(M, N, K):
-    """The MLP shapes and a ragged one: the planner's tilings (160-, 192- and
-    256-row weight tiles, two column regions); sampled outputs, tile corners
-    and the columns around the region boundary."""
+    """The MLP shapes, a ragged one and one the planner splits: its tilings
+    (128-row weight tiles two per compute unit, 160-row tiles, and a 256 x 128
+    region beside a 128 x 256 one); sampled outputs, tile corners and the
+    columns around the region boundary."""
     split = ops.fp8_blockscaled_gemm_plan(M, N, K)[2]
     _say("pow2 gemm", M, N, K, "split", split)
     opnds = _operands(M, N, K, 9)
