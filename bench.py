@@ -2,9 +2,10 @@
 
 Headline step: the Qwen3-4B MLP forward with the block-wise FP8 recipe,
 every part on the GPU through the C ABI:
-    quantize X_up [4096 x 2560] per token (1x128), quantize W_up [9728 x 2560]
-    in 128x128 blocks, GEMM up (bf16 out), quantize X_down [4096 x 9728],
-    quantize W_down [2560 x 9728], GEMM down (bf16 out).
+    quantize X_up [4096 x 2560] per token (1x128) and W_up [9728 x 2560] in
+    128x128 blocks (one fp8_quant_linear launch), GEMM up (bf16 out),
+    quantize X_down [4096 x 9728] and W_down [2560 x 9728] (one launch),
+    GEMM down (bf16 out).
 Inputs are seeded synthetic tensors (see fp8_block_scaled_x128_amd.inputs),
 resident in HBM before timing; activations rotate over several copies so
 that the 256 MB last-level cache cannot serve them.
@@ -427,31 +428,29 @@ def main():
     qw_dn, sw_dn = u8(HID, INTER), f32(HID // 128, INTER // 128)
     y_dn = torch.empty((M_TOK, HID), dtype=torch.bfloat16, device=dev)
 
-    names = ["quant_x_up", "quant_w_up", "gemm_up", "quant_x_down", "quant_w_down", "gemm_down"]
-    # each launch takes (activation copy index, raw HIP stream handle)
+    names = ["quant_up", "gemm_up", "quant_down", "gemm_down"]
+    # each launch takes (activation copy index, raw HIP stream handle); each
+    # projection's activation (1x128) and weight (128x128) are quantized by
+    # one fp8_quant_linear launch
     launches = [
-        lambda i, st: ops.fp8_quant_rowblock(xs_up[i], M_TOK, HID, HID, ops.AXIS_ROW, qx_up, HID, sx_up, 1, M_TOK,
-                                             stream=st),
-        lambda i, st: ops.fp8_quant_block2d(w_up, 1, INTER, HID, HID, qw_up, HID, None, 0, sw_up, stream=st),
+        lambda i, st: ops.fp8_quant_linear(xs_up[i], M_TOK, HID, HID, qx_up, HID, sx_up, 1, M_TOK,
+                                           w_up, INTER, HID, qw_up, HID, sw_up, stream=st),
         lambda i, st: ops.fp8_blockscaled_gemm(M_TOK, INTER, HID, qx_up, HID, sx_up, 1, M_TOK, qw_up, HID, sw_up,
                                                HID // 128, 1, ops.BSCALE_BLOCK128, y_up, INTER, ops.OUT_BF16,
                                                stream=st),
-        lambda i, st: ops.fp8_quant_rowblock(xs_dn[i], M_TOK, INTER, INTER, ops.AXIS_ROW, qx_dn, INTER, sx_dn, 1,
-                                             M_TOK, stream=st),
-        lambda i, st: ops.fp8_quant_block2d(w_dn, 1, HID, INTER, INTER, qw_dn, INTER, None, 0, sw_dn, stream=st),
+        lambda i, st: ops.fp8_quant_linear(xs_dn[i], M_TOK, INTER, INTER, qx_dn, INTER, sx_dn, 1, M_TOK,
+                                           w_dn, HID, INTER, qw_dn, INTER, sw_dn, stream=st),
         lambda i, st: ops.fp8_blockscaled_gemm(M_TOK, HID, INTER, qx_dn, INTER, sx_dn, 1, M_TOK, qw_dn, INTER, sw_dn,
                                                INTER // 128, 1, ops.BSCALE_BLOCK128, y_dn, HID, ops.OUT_BF16,
                                                stream=st),
     ]
     gemm_flops = 2.0 * M_TOK * INTER * HID
-    work = {"quant_x_up": ("GB/s", qbytes_row(M_TOK, HID)),
-            "quant_w_up": ("GB/s", qbytes_block2d(1, INTER, HID)),
+    work = {"quant_up": ("GB/s", qbytes_row(M_TOK, HID) + qbytes_block2d(1, INTER, HID)),
             "gemm_up": ("TFLOP/s", gemm_flops),
-            "quant_x_down": ("GB/s", qbytes_row(M_TOK, INTER)),
-            "quant_w_down": ("GB/s", qbytes_block2d(1, HID, INTER)),
+            "quant_down": ("GB/s", qbytes_row(M_TOK, INTER) + qbytes_block2d(1, HID, INTER)),
             "gemm_down": ("TFLOP/s", gemm_flops)}
 
-    # The six launches in order on one stream.  The timed loop records no
+    # The four launches in order on one stream.  The timed loop records no
     # per-kernel events (their host cost paced the GPU: 0.36 instead of 0.29
     # ms per step); the per-kernel times come from a second pass.  Running
     # each weight quantization on a second stream next to the activation

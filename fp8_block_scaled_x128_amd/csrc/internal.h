@@ -11,6 +11,10 @@ hipError_t launch_quant_1x128(const uint16_t* x, int64_t rows, int64_t cols, int
                               int64_t ld_q, float* s, int64_t ssr, int64_t ssg, hipStream_t st);
 hipError_t launch_quant_128x1_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt,
                                 int64_t ld_qt, float* s, int64_t ssr, int64_t ssg, hipStream_t st);
+// X in 1x128 groups and W (rows w_rows, same cols) in 128x128 blocks, one launch.
+hipError_t launch_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx, int64_t ld_qx,
+                               float* sx, int64_t ssr, int64_t ssg, const uint16_t* w, int64_t w_rows, int64_t ld_w,
+                               uint8_t* qw, int64_t ld_qw, float* sw, hipStream_t st);
 hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, int64_t cols, int64_t ld_w,
                                 uint8_t* q, int64_t ld_q, uint8_t* qt, int64_t ld_qt, float* s, hipStream_t st);
 hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,

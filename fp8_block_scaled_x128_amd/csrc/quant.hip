@@ -102,11 +102,13 @@ struct RowArgs {
 
 // P2: 128-element groups with power-of-two scales (the MX exponent rule on
 // the group's amax, a UE8M0 byte per group, codes E4M3(x * 2^-e)).
+// The body takes its workgroup index and count as arguments so that the
+// fused linear-operand kernel below can run it on part of its grid.
 template <bool SILU, bool MX, bool ROW_FAST, int U, bool NTQ, bool P2>
-__global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
+__device__ __forceinline__ void rowgroup_body(const RowArgs& p, int32_t block, int32_t nblocks) {
     const int sub = threadIdx.x & 15;
-    const int32_t rid = (int32_t)blockIdx.x * (kThreads / 16) + (int32_t)(threadIdx.x >> 4);
-    const int32_t nr = (int32_t)gridDim.x * (kThreads / 16);
+    const int32_t rid = block * (kThreads / 16) + (int32_t)(threadIdx.x >> 4);
+    const int32_t nr = nblocks * (kThreads / 16);
     for (int32_t base = rid; base < p.total_runs; base += nr * U) {
         uint4 raw[U], raw_u[U];
         int32_t rr[U], gg[U];
@@ -189,6 +191,11 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
             }
         }
     }
+}
+
+template <bool SILU, bool MX, bool ROW_FAST, int U, bool NTQ, bool P2>
+__global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
+    rowgroup_body<SILU, MX, ROW_FAST, U, NTQ, P2>(p, (int32_t)blockIdx.x, (int32_t)gridDim.x);
 }
 
 template <bool SILU, bool MX, bool P2 = false>
@@ -312,20 +319,21 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
 
 // P2: power-of-two scale (MX exponent rule on the block's amax) stored as a
 // UE8M0 byte, codes E4M3(x * 2^-e); s is then uint8 with row stride lds.
+// Block (bx, by) of matrix bz; the body takes the block coordinates as
+// arguments so that the fused linear-operand kernel can run it.
 template <bool TRANS, bool NT, bool P2>
-__global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __restrict__ w, int32_t rows, int32_t cols,
-                                                            int64_t ld_w, uint8_t* __restrict__ q, int64_t ld_q,
-                                                            uint8_t* __restrict__ qt, int64_t ld_qt,
-                                                            void* __restrict__ s, int32_t nbr, int32_t lds) {
+__device__ __forceinline__ void block2d_body(const uint16_t* __restrict__ w, int32_t rows, int32_t cols, int64_t ld_w,
+                                             uint8_t* __restrict__ q, int64_t ld_q, uint8_t* __restrict__ qt,
+                                             int64_t ld_qt, void* __restrict__ s, int32_t nbr, int32_t lds, int32_t bx,
+                                             int32_t by, int32_t bz) {
     __shared__ float red[kThreads / 64];
     __shared__ __attribute__((aligned(16))) uint32_t ctile[TRANS ? 128 : 1][33];
     const int t = threadIdx.x;
-    const int64_t bz = blockIdx.z;
     w += bz * (int64_t)rows * ld_w;
     q += bz * (int64_t)rows * ld_q;
     if (TRANS) qt += bz * (int64_t)cols * ld_qt;
-    const int64_t s_idx = bz * (int64_t)nbr * lds + (int64_t)blockIdx.y * lds + blockIdx.x;
-    const int32_t r0 = (int32_t)blockIdx.y * 128, c0 = (int32_t)blockIdx.x * 128;
+    const int64_t s_idx = bz * (int64_t)nbr * lds + (int64_t)by * lds + bx;
+    const int32_t r0 = by * 128, c0 = bx * 128;
     const int cc = t & 15;
     uint4 raw[8];
 #pragma unroll
@@ -406,6 +414,38 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
             }
         }
     }
+}
+
+template <bool TRANS, bool NT, bool P2>
+__global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __restrict__ w, int32_t rows, int32_t cols,
+                                                            int64_t ld_w, uint8_t* __restrict__ q, int64_t ld_q,
+                                                            uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                            void* __restrict__ s, int32_t nbr, int32_t lds) {
+    block2d_body<TRANS, NT, P2>(w, rows, cols, ld_w, q, ld_q, qt, ld_qt, s, nbr, lds, (int32_t)blockIdx.x,
+                                (int32_t)blockIdx.y, (int32_t)blockIdx.z);
+}
+
+// The two operands of one linear layer in one launch: workgroups [0, w_blocks)
+// quantize 128 x 128 blocks of the weight W (row-major block order), the rest
+// run the 1x128 row-group quantizer over the activation X.  Both parts are
+// HBM-bound; in one grid their loads are in flight together, and the step
+// saves a launch, its ramp-up and its tail.
+struct LinearArgs {
+    RowArgs x;
+    int32_t x_blocks;
+    const uint16_t* w; int32_t w_rows, cols; int64_t ld_w;
+    uint8_t* qw; int64_t ld_qw; float* sw;
+    int32_t nbr, nbc, w_blocks;
+};
+
+template <bool ROW_FAST>
+__global__ void __launch_bounds__(kThreads) k_quant_linear(LinearArgs a) {
+    const int32_t b = (int32_t)blockIdx.x;
+    if (b < a.w_blocks)
+        block2d_body<false, false, false>(a.w, a.w_rows, a.cols, a.ld_w, a.qw, a.ld_qw, nullptr, 0, a.sw, a.nbr, a.nbc,
+                                          b % a.nbc, b / a.nbc, 0);
+    else
+        rowgroup_body<false, false, ROW_FAST, 4, false, false>(a.x, b - a.w_blocks, a.x_blocks);
 }
 
 __global__ void __launch_bounds__(kThreads) k_e4m3_encode(const float* __restrict__ in, uint8_t* __restrict__ out,
@@ -574,6 +614,41 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, 
         if (nt) go(std::false_type{}, std::true_type{});
         else go(std::false_type{}, std::false_type{});
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx, int64_t ld_qx,
+                               float* sx, int64_t ssr, int64_t ssg, const uint16_t* w, int64_t w_rows, int64_t ld_w,
+                               uint8_t* qw, int64_t ld_qw, float* sw, hipStream_t st) {
+    // Tensors past the 256 MB last-level cache take the streaming policies of
+    // the separate kernels; the fused kernel serves the cached sizes.
+    const bool big = rows * cols > ((int64_t)256 << 20) || w_rows * cols * 2 > ((int64_t)256 << 20);
+    if (big || rows == 0 || w_rows == 0 || cols == 0) {
+        hipError_t e = launch_quant_128x128(w, 1, w_rows, cols, ld_w, qw, ld_qw, nullptr, 0, sw, st);
+        if (e != hipSuccess) return e;
+        return launch_quant_1x128(x, rows, cols, ld_x, qx, ld_qx, sx, ssr, ssg, st);
+    }
+    LinearArgs a{};
+    RowArgs& p = a.x;
+    p.x = x; p.ld_x = ld_x; p.rows = (int32_t)rows; p.cols = (int32_t)cols; p.up_off = 0;
+    p.q = qx; p.ld_q = ld_qx; p.s = sx; p.ssr = ssr; p.ssg = ssg; p.h = nullptr; p.ld_h = 0;
+    p.runs_per_row = (int32_t)((cols + 127) / 128);
+    p.total_runs = (int32_t)(rows * p.runs_per_row);
+    constexpr int U = 4;                     // as the row-group launch: one trip per 16-lane row
+    const int64_t rows16 = ((int64_t)p.total_runs + U - 1) / U;
+    int64_t xb = (rows16 + (kThreads / 16) - 1) / (kThreads / 16);
+    if (xb > 256 * 256) xb = 256 * 256;
+    a.x_blocks = (int32_t)xb;
+    a.w = w; a.w_rows = (int32_t)w_rows; a.cols = (int32_t)cols; a.ld_w = ld_w;
+    a.qw = qw; a.ld_qw = ld_qw; a.sw = sw;
+    a.nbr = (int32_t)((w_rows + 127) / 128);
+    a.nbc = (int32_t)((cols + 127) / 128);
+    a.w_blocks = a.nbr * a.nbc;
+    const dim3 grid((unsigned)(a.w_blocks + a.x_blocks));
+    if (ssr == 1 && ssg != 1)
+        hipLaunchKernelGGL(k_quant_linear<true>, grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_quant_linear<false>, grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ AXIS_ROW, AXIS_COL = 0, 1
 OUT_BF16, OUT_FP32 = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
-EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
+EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_linear", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
            "fp8_grouped_gemm",
            "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
            "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
@@ -56,6 +56,7 @@ def load():
         sig = {
             "fp8_quant_rowblock": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P],
             "fp8_quant_block2d": [P, I64, I64, I64, I64, P, I64, P, I64, P, P],
+            "fp8_quant_linear": [P, I64, I64, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, P, P],
             "fp8_quant_rowwise": [P, I64, I64, I64, P, I64, P, P],
             "fp8_quant_tensorwise": [P, I64, I64, I64, P, I64, P, P],
             "fp8_blockscaled_gemm": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P, I64, INT, P],
@@ -118,6 +119,13 @@ def fp8_quant_block2d(w, batch, rows, cols, ld_w, q, ld_q, q_t, ld_qt, s, stream
     st = load().fp8_quant_block2d(_p(w), batch, rows, cols, ld_w, _p(q), ld_q, _p(q_t), ld_qt, _p(s),
                                   _stream(stream))
     return _check("fp8_quant_block2d", st, raise_on_error)
+
+
+def fp8_quant_linear(x, rows, cols, ld_x, qx, ld_qx, sx, sx_stride_row, sx_stride_group, w, w_rows, ld_w, qw, ld_qw,
+                     sw, stream=None, raise_on_error=True):
+    st = load().fp8_quant_linear(_p(x), rows, cols, ld_x, _p(qx), ld_qx, _p(sx), sx_stride_row, sx_stride_group,
+                                 _p(w), w_rows, ld_w, _p(qw), ld_qw, _p(sw), _stream(stream))
+    return _check("fp8_quant_linear", st, raise_on_error)
 
 
 def fp8_quant_rowwise(x, rows, cols, ld_x, q, ld_q, s, stream=None, raise_on_error=True):
@@ -233,6 +241,22 @@ def quant_rowblock(x: torch.Tensor, axis: int = AXIS_ROW, scale_layout: str = "m
         ssr, ssg = ng, 1
     fp8_quant_rowblock(x, rows, cols, x.stride(0), axis, q, ld_q, s, ssr, ssg)
     return q, s
+
+
+def quant_linear(x: torch.Tensor, w: torch.Tensor):
+    """Both operands of a linear layer in one launch: X [rows, cols] in 1x128
+    groups (M-major scales, returned as a [rows, groups] view) and W
+    [w_rows, cols] in 128x128 blocks.  Returns (qx, sx, qw, sw)."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.is_contiguous() and w.shape[1] == x.shape[1]
+    rows, cols = x.shape
+    w_rows = w.shape[0]
+    ng = (cols + 127) // 128
+    qx, qw = _u8((rows, cols), x.device), _u8((w_rows, cols), x.device)
+    sbuf = torch.empty((ng, rows), dtype=torch.float32, device=x.device)
+    sw = torch.empty(((w_rows + 127) // 128, ng), dtype=torch.float32, device=x.device)
+    fp8_quant_linear(x, rows, cols, cols, qx, cols, sbuf, 1, rows, w, w_rows, cols, qw, cols, sw)
+    return qx, sbuf.t(), qw, sw
 
 
 def quant_block2d(w: torch.Tensor, transposed: bool = False):

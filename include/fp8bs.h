@@ -142,6 +142,32 @@ fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, i
                                float* s, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_quant_linear -- both operands of one block-wise FP8 linear layer in
+ * one launch: the activation X [rows][cols] in 1x128 per-token groups and
+ * the weight W [w_rows][cols] in 128x128 blocks, each with the scale
+ * S = max|x| / 448 of its group and codes E4M3(x / S) ("Unified FP8: Beyond
+ * Mixed Precision...", section "FP8 Quantization"; groupings of "Low
+ * Precision RL", table "Choose a precision").  The results are identical
+ * to fp8_quant_rowblock(x, ..., FP8BS_AXIS_ROW, qx, ld_qx, sx, ...) followed
+ * by fp8_quant_block2d(w, 1, w_rows, cols, ...) without a transposed copy;
+ * one grid carries both, so their memory traffic overlaps and the pair
+ * costs one launch.
+ *
+ * x, qx, sx : as x, q, s of fp8_quant_rowblock with FP8BS_AXIS_ROW
+ *             (scale of row r, group g at sx[r * sx_stride_row +
+ *             g * sx_stride_group]).
+ * w, qw, sw : as w, q, s of fp8_quant_block2d with batch 1 (sw is
+ *             [ceil(w_rows/128)][ceil(cols/128)], contiguous).
+ * Either operand may be empty (rows == 0 or w_rows == 0; its pointers are
+ * then not read).  Requirements: as the two calls above; the buffers of
+ * the two operands must not overlap.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t* qx, int64_t ld_qx, float* sx, int64_t sx_stride_row, int64_t sx_stride_group,
+                              const uint16_t* w, int64_t w_rows, int64_t ld_w,
+                              uint8_t* qw, int64_t ld_qw, float* sw, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_blockscaled_gemm -- C = A B^T with block scales, FP32 accumulation.
  *
  *   C[m, n] = sum_kb (sa(m, kb) * sb(n, kb)) * sum_{k in kb} dec(a[m, k]) dec(b[n, k])

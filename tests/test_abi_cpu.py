@@ -86,6 +86,20 @@ def test_host_validation_rejects_before_launch(lib):
     # empty inputs are a successful no-op
     assert ops.fp8_quant_rowblock(None, 0, 128, 128, 0, None, 128, None, 1, 1, stream=0,
                                   raise_on_error=False) == 0
+    # both operands of a linear layer in one launch: each operand checked as
+    # its own call would check it; an empty operand's pointers are not read
+    lin = lambda x, rows, cols, ld_x, w, w_rows, ld_w, sx=fake, sw=fake: ops.fp8_quant_linear(
+        x, rows, cols, ld_x, fake, cols, sx, 1, max(rows, 1), w, w_rows, ld_w, fake, cols, sw, stream=0,
+        raise_on_error=False)
+    assert lin(fake, 4, 100, 100, fake, 128, 100) == 2          # cols % 8
+    assert lin(fake, 4, 128, 64, fake, 128, 128) == 3           # ld_x < cols
+    assert lin(fake, 4, 128, 128, fake, 128, 64) == 3           # ld_w < cols
+    assert lin(fake + 2, 4, 128, 128, fake, 128, 128) == 4      # misaligned x
+    assert lin(fake, 4, 128, 128, fake + 2, 128, 128) == 4      # misaligned w
+    assert lin(None, 4, 128, 128, fake, 128, 128) == 1          # NULL x
+    assert lin(fake, 4, 128, 128, fake, 128, 128, sw=None) == 1  # NULL weight scales
+    assert lin(fake, -1, 128, 128, fake, 128, 128) == 2
+    assert lin(None, 0, 128, 128, None, 0, 128, sx=None, sw=None) == 0
 
 
 def test_dense_tile_plan(lib):

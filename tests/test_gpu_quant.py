@@ -172,6 +172,68 @@ def test_block2d_qwen3_4b_weight_full():
     _assert_same_codes(qt, np.ascontiguousarray(qr.T))
 
 
+# ------------------------------------------- both operands in one launch
+def _linear_check(x, w, qx, sx, qw, sw):
+    qr, sr = oracle.quant_1x128(x)
+    _assert_same_codes(qx, qr)
+    _assert_same_scales(sx, sr)
+    qr, sr = oracle.quant_128x128(w)
+    _assert_same_codes(qw, qr)
+    _assert_same_scales(sw, sr)
+
+
+@pytest.mark.parametrize("rows,w_rows,cols", [(300, 200, 1000), (256, 512, 512), (7, 130, 264), (1, 8, 8)])
+def test_quant_linear_small(rows, w_rows, cols):
+    """X in 1x128 groups and W in 128x128 blocks from one launch: codes and
+    scales bit-identical to the oracle (ragged rows, columns and blocks)."""
+    _say("quant_linear", rows, w_rows, cols)
+    x = _bits((rows, cols), 40 + rows)
+    w = _bits((w_rows, cols), 41 + w_rows, 0.02, 0.0, 1.0)
+    qx, sx, qw, sw = ops.quant_linear(dev_bf16(x), dev_bf16(w))
+    torch.cuda.synchronize()
+    _linear_check(x, w, qx, sx, qw, sw)
+
+
+@pytest.mark.parametrize("part", ["up", "down"])
+def test_quant_linear_qwen3_4b_full(part):
+    """The MLP step's operand pairs at full size: X_up [4096 x 2560] with
+    W_up [9728 x 2560], X_down [4096 x 9728] with W_down [2560 x 9728]."""
+    d = inputs.qwen3_4b_mlp(1, parts=(part,))
+    x, w = d["x_" + part], d["w_" + part]
+    _say("quant_linear full", part, x.shape, w.shape)
+    qx, sx, qw, sw = ops.quant_linear(dev_bf16(x), dev_bf16(w))
+    torch.cuda.synchronize()
+    _linear_check(x, w, qx, sx, qw, sw)
+
+
+def test_quant_linear_layouts_and_empty_operands():
+    """Row-major activation scales, and one operand empty: the results equal
+    the separate fp8_quant_rowblock / fp8_quant_block2d calls byte for byte."""
+    rows, w_rows, cols = 260, 384, 640
+    x = dev_bf16(_bits((rows, cols), 44))
+    w = dev_bf16(_bits((w_rows, cols), 45, 0.02, 0.0, 1.0))
+    ng = cols // 128
+    u8 = lambda *sh: torch.full(sh, 0xAA, dtype=torch.uint8, device="cuda")
+    f32 = lambda *sh: torch.full(sh, -1.0, dtype=torch.float32, device="cuda")
+    # reference: the two separate calls, row-major activation scales
+    qx0, sx0, qw0, sw0 = u8(rows, cols), f32(rows, ng), u8(w_rows, cols), f32(w_rows // 128, ng)
+    ops.fp8_quant_rowblock(x, rows, cols, cols, ops.AXIS_ROW, qx0, cols, sx0, ng, 1)
+    ops.fp8_quant_block2d(w, 1, w_rows, cols, cols, qw0, cols, None, 0, sw0)
+    for rx, rw in ((rows, w_rows), (0, w_rows), (rows, 0)):
+        qx, sx, qw, sw = u8(rows, cols), f32(rows, ng), u8(w_rows, cols), f32(w_rows // 128, ng)
+        ops.fp8_quant_linear(x, rx, cols, cols, qx, cols, sx, ng, 1, w, rw, cols, qw, cols, sw)
+        torch.cuda.synchronize()
+        _say("quant_linear rows", rx, "w_rows", rw)
+        if rx:
+            assert torch.equal(qx, qx0) and torch.equal(sx.view(torch.int32), sx0.view(torch.int32))
+        else:   # untouched
+            assert bool((qx == 0xAA).all()) and bool((sx == -1.0).all())
+        if rw:
+            assert torch.equal(qw, qw0) and torch.equal(sw.view(torch.int32), sw0.view(torch.int32))
+        else:
+            assert bool((qw == 0xAA).all()) and bool((sw == -1.0).all())
+
+
 # ---------------------------------------------------------------------- MX
 @pytest.mark.parametrize("shape", [(64, 256), (5, 96), (300, 2048)])
 def test_mx_small(shape):
