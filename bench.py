@@ -18,7 +18,9 @@ repetitions, each kernel bracketed by HIP events on the launch stream):
                      GEMMs (fp32 out)
     moe_blockwise    Qwen3-30B-A3B MoE layer (16384 tokens, 128 experts, top 8):
                      X 1x128, W_gu / W_d 128x128, grouped gate_up GEMM, SiLU*mul
-                     + 1x128 requantization, grouped down GEMM
+                     + 1x128 requantization, grouped down GEMM, combine
+    moe_blockwise_fused  the same layer with SiLU*mul and the requantization
+                     in the gate_up GEMM's epilogue
     moe_mxfp8        the same layer with 1x32 UE8M0 scales (MXFP8)
 
 Prints ONE JSON line: value = GEMM FLOPs of the headline step / step time
@@ -43,7 +45,8 @@ PEAK_FP8_TFLOPS = 5030.0     # 256 CUs x 2.4 GHz x 8192 dense FP8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 M_TOK, HID, INTER = 4096, 2560, 9728
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
-WORKLOADS = ("tiny_linear", "mlp_backward", "mlp_backward_mxfp8", "moe_blockwise", "moe_mxfp8", "up_proj_rowwise",
+WORKLOADS = ("tiny_linear", "mlp_backward", "mlp_backward_mxfp8", "moe_blockwise", "moe_blockwise_fused", "moe_mxfp8",
+             "up_proj_rowwise",
              "up_proj_pow2")
 
 
@@ -267,7 +270,11 @@ def _moe_inputs(inputs, cache={}):
     return cache["d"]
 
 
-def wl_moe_blockwise(torch, ops, inputs, to_dev, R):
+def wl_moe_blockwise(torch, ops, inputs, to_dev, R, fused=False):
+    """The Qwen3-30B-A3B MoE layer with the block-wise recipe.  fused: the
+    gate/up GEMM forms h = SiLU(gate) * up and its 1x128 codes in its
+    epilogue (fp8_grouped_gemm_swiglu_quant) instead of writing bf16 gate/up
+    for the separate SiLU*mul kernel."""
     d = _moe_inputs(inputs)
     r = d["routing"]
     T, H = d["x"].shape
@@ -283,7 +290,7 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R):
     qx, sx = u8(T, H), f32(H // 128, T)
     qgu, sgu = u8(E, N2, H), f32(E, N2 // 128, H // 128)
     qd, qdt, sd = u8(E, I, H), u8(E, H, I), f32(E, I // 128, H // 128)
-    gu = torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
+    gu = None if fused else torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
     qh, sh = u8(rows, I), f32(I // 128, rows)
     y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
     pos, wts = torch.from_numpy(r.token_rows).cuda(), torch.from_numpy(r.weights).cuda()
@@ -291,6 +298,19 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R):
     k = r.token_rows.shape[1]
     n_gu = 2.0 * rows * N2 * H
     n_dn = 2.0 * rows * H * I
+    gate_up_steps = [
+        ("grouped_gemm_gate_up", lambda i: ops.fp8_grouped_gemm(
+            rows, N2, H, G, offs, a_rows, T, qx, H, sx, 1, T, qgu, H, N2 * H, sgu, (N2 // 128) * (H // 128),
+            H // 128, 1, gu, N2, ops.OUT_BF16), ("TFLOP/s", n_gu)),
+        ("silu_mul_quant_1x128", lambda i: ops.fp8_silu_mul_quant(gu, rows, I, N2, 0, qh, I, sh, 1, rows, None, 0),
+         ("GB/s", rows * N2 * 2 + rows * I + rows * (I // 128) * 4)),
+    ]
+    if fused:
+        gate_up_steps = [
+            ("grouped_gemm_gate_up_swiglu_quant", lambda i: ops.fp8_grouped_gemm_swiglu_quant(
+                rows, I, H, G, offs, a_rows, T, qx, H, sx, 1, T, qgu, H, N2 * H, sgu, (N2 // 128) * (H // 128),
+                H // 128, 1, qh, I, sh, 1, rows), ("TFLOP/s", n_gu)),
+        ]
     return [
         ("quant_x_1x128", lambda i: ops.fp8_quant_rowblock(xs[i % R], T, H, H, ops.AXIS_ROW, qx, H, sx, 1, T),
          ("GB/s", qbytes_row(T, H))),
@@ -298,18 +318,15 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R):
          ("GB/s", qbytes_block2d(E, N2, H))),
         ("quant_w_down_128x128_with_transpose", lambda i: ops.fp8_quant_block2d(wd, E, I, H, H, qd, H, qdt, I, sd),
          ("GB/s", qbytes_block2d(E, I, H, transposed=True))),
-        ("grouped_gemm_gate_up", lambda i: ops.fp8_grouped_gemm(
-            rows, N2, H, G, offs, a_rows, T, qx, H, sx, 1, T, qgu, H, N2 * H, sgu, (N2 // 128) * (H // 128),
-            H // 128, 1, gu, N2, ops.OUT_BF16), ("TFLOP/s", n_gu)),
-        ("silu_mul_quant_1x128", lambda i: ops.fp8_silu_mul_quant(gu, rows, I, N2, 0, qh, I, sh, 1, rows, None, 0),
-         ("GB/s", rows * N2 * 2 + rows * I + rows * (I // 128) * 4)),
+    ] + gate_up_steps + [
         # B[n = hidden, k = inter] = W_d[e]^T codes; scales sd[e][k/128][n/128] read transposed
         ("grouped_gemm_down", lambda i: ops.fp8_grouped_gemm(
             rows, H, I, G, offs, None, rows, qh, I, sh, 1, rows, qdt, I, H * I, sd, (I // 128) * (H // 128),
             1, H // 128, y, H, ops.OUT_BF16), ("TFLOP/s", n_dn)),
         ("combine", lambda i: ops.fp8_moe_combine(y, rows, H, H, pos, wts, T, k, out, H, ops.OUT_BF16),
          ("GB/s", combine_bytes(rows, H, T, k))),
-    ], {"workload": "moe_blockwise", "tokens": T, "hidden": H, "experts": E, "intermediate": I, "top_k": 8,
+    ], {"workload": "moe_blockwise_fused" if fused else "moe_blockwise", "tokens": T, "hidden": H, "experts": E,
+        "intermediate": I, "top_k": 8,
         "grouped_rows": rows, "seed": 3}
 
 
@@ -530,7 +547,8 @@ def main():
     wanted = [w for w in args.workloads.split(",") if w and w != "none"]
     table = {"tiny_linear": wl_tiny_linear, "mlp_backward": wl_mlp_backward,
              "mlp_backward_mxfp8": wl_mlp_backward_mxfp8, "up_proj_pow2": wl_up_proj_pow2,
-             "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8, "up_proj_rowwise": wl_up_proj_rowwise}
+             "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8, "up_proj_rowwise": wl_up_proj_rowwise,
+             "moe_blockwise_fused": lambda *a: wl_moe_blockwise(*a, fused=True)}
     others = {}
     for wname in wanted:
         if wname not in table:

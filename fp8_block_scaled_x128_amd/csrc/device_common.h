@@ -120,4 +120,64 @@ __device__ __forceinline__ float pow2_neg(int e) {
     return be >= 1 ? __uint_as_float((uint32_t)be << 23) : __uint_as_float(1u << (22 + be));
 }
 
+// Codes of 8 values of one group given its scale s (S == 0 -> all 0x00).
+__device__ __forceinline__ void encode8(const float v[8], float s, uint32_t& w0, uint32_t& w1) {
+    float qv[8];
+    if (s >= kFastDivMinScale) {
+        const float y = 1.0f / s;                 // IEEE division: y = RN(1/s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = div_by_scale(v[i], s, y);
+    } else if (s > 0.0f) {                        // subnormal-range scales: plain IEEE division
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = v[i] / s;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = 0.0f;
+    }
+    w0 = enc4(qv[0], qv[1], qv[2], qv[3]);
+    w1 = enc4(qv[4], qv[5], qv[6], qv[7]);
+}
+
+__device__ __forceinline__ void unpack8(const uint4 raw, float v[8]) {
+    v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x);
+    v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
+    v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z);
+    v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+}
+
+__device__ __forceinline__ float absmax8(const float v[8]) {
+    float m = fabsf(v[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    return m;
+}
+
+// silu(g) * u rounded to bf16 and widened back (the value the next GEMM consumes).
+// silu(g) = g * sigmoid(g), with sigmoid(g) = 1 / (1 + t) for g >= 0 and
+// t / (1 + t) for g < 0, t = exp(-|g|) in (0, 1]: no overflow, and 1 + t in
+// [1, 2] for the hardware reciprocal.  t = 2^a with a = -|g| log2(e) split
+// into a rounded part for the hardware exp2 and its exact residual applied to
+// first order, so t is good to about one fp32 ulp.  Where t would be an fp32
+// denormal (a < -64, that is |g| above about 44.4) it is formed scaled by 2^64
+// and the scale is removed from the final product.  The accurate expf and IEEE
+// division cost about 25 more instructions per element, enough to make this
+// kernel VALU bound.  The product is rounded once to bf16: the result stays
+// within one bf16 ulp of the exactly rounded value, and differs from it only
+// where the exact value lies a few fp32 ulp from a bf16 rounding midpoint.
+__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+    constexpr float kLog2e = 1.4426950216293335f;       // log2(e) rounded to fp32
+    constexpr float kLog2eLo = 1.925963033500011e-08f;  // log2(e) - kLog2e
+    constexpr float kLn2 = 0.6931471824645996f;
+    const float ng = -fabsf(g);
+    const float a_hi = ng * kLog2e;
+    const float a_lo = __builtin_fmaf(ng, kLog2e, -a_hi) + ng * kLog2eLo;
+    const bool tiny = a_hi < -64.0f;
+    const float t = __builtin_amdgcn_exp2f(tiny ? a_hi + 64.0f : a_hi) * __builtin_fmaf(a_lo, kLn2, 1.0f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + (tiny ? 0.0f : t));
+    const float sig = g >= 0.0f ? r : t * r;
+    float h = (g * sig) * u;
+    if (tiny && g < 0.0f) h *= 0x1p-64f;
+    return f32_to_bf16_rne(h);
+}
+
 }  // namespace fp8bs

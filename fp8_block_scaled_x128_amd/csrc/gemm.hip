@@ -139,6 +139,12 @@ struct KArgs {
     void* c; int64_t ldc;
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
     int32_t kinv_row;                          // MODE_KINV: sb indexed by n (1) or n / 128 (0)
+    // SWIGLU (grouped gate/up GEMM with SiLU*mul and 1x128 quantization in
+    // the epilogue): B rows [0, swi) are gate rows, [swi, 2 swi) up rows;
+    // h codes hq [rows][ld_hq], h scales hs[m * hs_sm + (j / 128) * hs_sg]
+    int32_t swi;
+    uint8_t* hq; int64_t ld_hq;
+    float* hs; int64_t hs_sm, hs_sg;
 };
 
 __device__ __forceinline__ int swz(int r) { return r & 7; }
@@ -233,10 +239,14 @@ __device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
 }
 
-template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF, int WN>
+template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF, int WN, bool SWIGLU = false>
 __global__ void __launch_bounds__((Cfg<WAVES, NF, false, WN>::kThreads), (Cfg<WAVES, NF, false, WN>::kMinWavesPerEU))
 k_gemm(KArgs p) {
     using C = Cfg<WAVES, NF, (MODE == MODE_ROW128 || MODE == MODE_MX), WN>;
+    // SWIGLU tiles: 256 weight rows = 128 gate rows (wave column 0) and the
+    // matching 128 up rows (wave column 1) for 128 columns of h
+    static_assert(!SWIGLU || (GROUPED && MODE == MODE_BLOCK128 && !OUTF32 && WAVES == 8 && NF == 8 && WN == 2),
+                  "SiLU*mul epilogue: grouped BLOCK128 GEMM, 256 x 256 tiles, bf16 rounding of gate and up");
     constexpr int BM = C::BM, BN = C::BN;
     // per-row weight scales are copied by waves 0 .. ceil(BN / 64) - 1 in 64-row pieces
     static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || (BN + 63) / 64 <= WAVES,
@@ -286,7 +296,7 @@ k_gemm(KArgs p) {
         // 4.8 times from HBM).  Wave 0 counts all row tiles (pass 1), maps
         // the workgroup to its work item, then finds the group of the item's
         // row tile with a prefix scan of the per-group counts (pass 2).
-        const int ntn = (p.N + BN - 1) / BN;
+        const int ntn = SWIGLU ? p.swi / 128 : (p.N + BN - 1) / BN;
         if (threadIdx.x == 0) s_tile[0] = -1;
         if (wave == 0) {
             // lane l looks at groups gb + 2l and gb + 2l + 1: their row
@@ -363,7 +373,7 @@ k_gemm(KArgs p) {
         const int lt = __builtin_amdgcn_readfirstlane(s_tile[1]);
         m_begin = __builtin_amdgcn_readfirstlane(s_tile[3]) + lt * BM;
         m_end = min(__builtin_amdgcn_readfirstlane(s_tile[4]), m_begin + BM);
-        n0 = __builtin_amdgcn_readfirstlane(s_tile[2]) * BN;
+        n0 = __builtin_amdgcn_readfirstlane(s_tile[2]) * (SWIGLU ? 128 : BN);   // SWIGLU: first h column
         bptr += (int64_t)g * p.b_sg;
         sbp += (int64_t)g * p.sb_sg * ((MODE == MODE_MX || MODE == MODE_P2) ? 1 : 4);
     }
@@ -384,7 +394,8 @@ k_gemm(KArgs p) {
     for (int j = 0; j < C::kDmaB; ++j) {
         const int row = bcopy(j) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz(row);
-        offB[j] = (uint32_t)((int64_t)min(n0 + row, p.N - 1) * p.ldb + chunk * 16);
+        const int brow = !SWIGLU ? min(n0 + row, p.N - 1) : row < 128 ? n0 + row : p.swi + n0 + row - 128;
+        offB[j] = (uint32_t)((int64_t)brow * p.ldb + chunk * 16);
     }
 #pragma unroll
     for (int j = 0; j < C::kDmaA; ++j) {
@@ -406,7 +417,8 @@ k_gemm(KArgs p) {
         sa_off = (uint32_t)((MODE == MODE_MX || MODE == MODE_P2) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4);
     }
     if (MODE == MODE_BLOCK128 || MODE == MODE_P2) {
-        const int nb = min(n0 / 128 + (lane & 1), (p.N - 1) / 128);
+        const int nb = !SWIGLU ? min(n0 / 128 + (lane & 1), (p.N - 1) / 128)
+                               : ((lane & 1) ? (p.swi + n0) / 128 : n0 / 128);   // gate block, up block
         sb_off = (uint32_t)((int64_t)nb * p.sb_sn * (MODE == MODE_P2 ? 1 : 4));
     } else if (MODE != MODE_KINV) {
         const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
@@ -698,15 +710,50 @@ k_gemm(KArgs p) {
                 }
             }
         }
+        if constexpr (SWIGLU) {
+            // h = bf16(silu(gate) * up) for the pass's rows of all four wave
+            // rows, then each row's 128 h values form one 1x128 group.  The
+            // gate half of wave row wr is staged by wave 2 wr, its up half by
+            // wave 2 wr + 1, so every wave must have staged first.  Gate and
+            // up are the bf16-rounded GEMM outputs and h uses the SiLU of the
+            // separate SiLU*mul kernel, so codes and scales equal those of
+            // the bf16 GEMM followed by fp8_silu_mul_quant.
+            __syncthreads();
+            const int sub = lane & 15;
 #pragma unroll
-        for (int it = 0; it < kRows * kChunks / 64; ++it) {
-            const int sidx = it * 64 + lane;
-            const int row = sidx / kChunks, ch = sidx % kChunks;
-            const u32x4 v = lds_read16(wst + (uint32_t)(row * kPitch + ch * 16));
-            const int m = m_begin + wm * 64 + pass * kRows + row;
-            const int col = ch * (16 / EB);
-            if (m < m_end && (NF == 8 || nw0 + col < p.N))
-                *reinterpret_cast<u32x4*>(cbase + ((int64_t)m * p.ldc) * EB + col * EB) = v;
+            for (int it = 0; it < 4; ++it) {
+                const int R = wave * 16 + it * 4 + (lane >> 4);      // row of the pass, 0..127
+                const int wr = R >> 5, rr = R & 31;
+                const uint32_t ga = lds0 + (uint32_t)(2 * wr * kRows * kPitch + rr * kPitch + sub * 16);
+                const u32x4 gv = lds_read16(ga);
+                const u32x4 uv = lds_read16(ga + kRows * kPitch);
+                float g[8], u[8], v[8];
+                unpack8(make_uint4(gv.x, gv.y, gv.z, gv.w), g);
+                unpack8(make_uint4(uv.x, uv.y, uv.z, uv.w), u);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(silu_mul_bf16(g[i], u[i]) << 16);
+                const float amax = group16_max(absmax8(v));
+                const float sc = amax / kE4M3Max;
+                uint32_t w0, w1;
+                encode8(v, sc, w0, w1);
+                const int m = m_begin + wr * 64 + pass * kRows + rr;
+                if (m < m_end) {
+                    *reinterpret_cast<uint2*>(p.hq + (int64_t)m * p.ld_hq + n0 + sub * 8) = make_uint2(w0, w1);
+                    if (sub == 0) p.hs[(int64_t)m * p.hs_sm + (int64_t)(n0 / 128) * p.hs_sg] = sc;
+                }
+            }
+            __syncthreads();     // the next pass overwrites the staging regions
+        } else {
+#pragma unroll
+            for (int it = 0; it < kRows * kChunks / 64; ++it) {
+                const int sidx = it * 64 + lane;
+                const int row = sidx / kChunks, ch = sidx % kChunks;
+                const u32x4 v = lds_read16(wst + (uint32_t)(row * kPitch + ch * 16));
+                const int m = m_begin + wm * 64 + pass * kRows + row;
+                const int col = ch * (16 / EB);
+                if (m < m_end && (NF == 8 || nw0 + col < p.N))
+                    *reinterpret_cast<u32x4*>(cbase + ((int64_t)m * p.ldc) * EB + col * EB) = v;
+            }
         }
     }
 }
@@ -874,6 +921,22 @@ hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st) {
     p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
     return waves_for(g.M, g.N, g.G / 2) == 8 ? launch<MODE_BLOCK128, true, 8, 8>(p, g.out_f32, st)
                                               : launch<MODE_BLOCK128, true, 4, 8>(p, g.out_f32, st);
+}
+
+hipError_t launch_gemm_grouped_swiglu(const GemmArgs& g, int64_t I, uint8_t* hq, int64_t ld_hq, float* hs,
+                                      int64_t hs_sm, int64_t hs_sg, hipStream_t st) {
+    if (g.M == 0 || I == 0) return hipSuccess;
+    KArgs p = base_args(g.M, 2 * I, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, nullptr, 0);
+    p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
+    p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
+    p.swi = (int32_t)I; p.hq = hq; p.ld_hq = ld_hq; p.hs = hs; p.hs_sm = hs_sm; p.hs_sg = hs_sg;
+    using C = Cfg<8, 8>;
+    // upper bound on the work items (row tiles x 128-column blocks of h),
+    // rounded up to a multiple of the 8 XCDs
+    const int64_t items = ((int64_t)(g.M + C::BM - 1) / C::BM + g.G) * (I / 128);
+    const dim3 grid((unsigned)((items + 7) / 8 * 8));
+    hipLaunchKernelGGL((k_gemm<MODE_BLOCK128, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_pow2(const Pow2GemmArgs& g, hipStream_t st) {

@@ -53,6 +53,11 @@ hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st);
 // two column regions, and the first column of the second (N if one region).
 void plan_gemm_blockscaled(int64_t M, int64_t N, int64_t K, int32_t out[5]);
 hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st);
+// Grouped gate/up GEMM (B = [G][2I][K], gate rows then up rows) whose epilogue
+// forms h = bf16(silu(gate) * up) from the bf16-rounded outputs and writes
+// h's 1x128 FP8 codes hq [M][ld_hq] and scales hs[m * hs_sm + g * hs_sg].
+hipError_t launch_gemm_grouped_swiglu(const GemmArgs& g, int64_t I, uint8_t* hq, int64_t ld_hq, float* hs,
+                                      int64_t hs_sm, int64_t hs_sg, hipStream_t st);
 
 struct MxGemmArgs {
     int64_t M, N, K;

@@ -246,6 +246,37 @@ fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t 
                               void* c, int64_t ldc, fp8bs_out out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_grouped_gemm_swiglu_quant -- the MoE expert gate/up GEMM
+ * (fp8_grouped_gemm) with the step that follows it, SiLU*mul and the 1x128
+ * re-quantization of h (fp8_silu_mul_quant, mx == 0), in the GEMM's
+ * epilogue: for callers who need only h's codes and scales (the operand of
+ * the down GEMM).
+ *
+ * Per expert g and row m of its group, with GU = the block-scaled product of
+ * fp8_grouped_gemm rounded to bf16 (N = 2 I, B = [G][2I][K], rows [0, I) of
+ * each expert gate, rows [I, 2I) up):
+ *   h[m, j] = bf16(silu(GU[m, j]) * GU[m, I + j]),  j < I,
+ * and h is quantized in 1x128 groups: hs = max|h| / 448 per group, codes
+ * E4M3(h / hs).  The codes and scales equal those of fp8_grouped_gemm (bf16
+ * out) followed by fp8_silu_mul_quant(mx = 0); the bf16 gate/up output and h
+ * are never written to memory.
+ *
+ * a .. sb_stride_k : as fp8_grouped_gemm with N = 2 I.
+ * hq : [total_rows][ld_hq] h codes.   hs(m, j/128) = hs[m * hs_stride_row +
+ *      (j / 128) * hs_stride_group] (pass 1 and total_rows for the M-major
+ *      layout the down GEMM reads).
+ * Requirements: as fp8_grouped_gemm; I % 128 == 0; ld_hq >= I, ld_hq % 8 ==
+ * 0, hq 8-byte aligned; hs 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int64_t K, int32_t G, const int32_t* offsets,
+                                           const int32_t* a_rows, int64_t a_count, const uint8_t* a, int64_t lda,
+                                           const float* sa, int64_t sa_stride_m, int64_t sa_stride_k,
+                                           const uint8_t* b, int64_t ldb, int64_t b_stride_g, const float* sb,
+                                           int64_t sb_stride_g, int64_t sb_stride_n, int64_t sb_stride_k, uint8_t* hq,
+                                           int64_t ld_hq, float* hs, int64_t hs_stride_row, int64_t hs_stride_group,
+                                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_silu_mul_quant -- the step between the MoE gate/up and down GEMMs:
  * h = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)) in fp32, then
  * quantization of h, 1x128 with FP32 scales (mx == 0) or 1x32 with UE8M0

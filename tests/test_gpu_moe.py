@@ -190,6 +190,7 @@ def _blockwise_chain(d, routing, seed, check_down=True, weights=None):
     ops.fp8_silu_mul_quant(gu16, rows, INTER, 2 * INTER, 0, qh, INTER, sh, 1, rows, h, INTER)
     torch.cuda.synchronize()
     _check_h(gu16, h, qh, sh, np.random.default_rng(seed + 2).integers(0, rows, 256), mx=False)
+    _fused_gate_up_matches(rows, G, offs, a_rows, x.shape[0], qx, sx, qgu, sgu, qh, shb)
     _say("down")
     dn16 = _grouped(rows, HID, INTER, G, offs, None, rows, qh, sh, qdt, sdt, torch.bfloat16)
     dn32 = _grouped(rows, HID, INTER, G, offs, None, rows, qh, sh, qdt, sdt, torch.float32)
@@ -210,6 +211,49 @@ def _blockwise_chain(d, routing, seed, check_down=True, weights=None):
     local = np.arange(pos.size, dtype=np.int32).reshape(pos.shape)
     tidx = torch.from_numpy(toks).cuda()
     _check_combine(yrows, local, r.weights[toks], host(out32[tidx]), host(out16[tidx]))
+
+
+def _fused_gate_up_matches(rows, G, offs, a_rows, a_count, qx, sx, qgu, sgu, qh, shb):
+    """The gate/up GEMM with SiLU*mul and the 1x128 quantization of h in its
+    epilogue: codes and (M-major) scales byte-identical to the bf16 grouped
+    GEMM followed by fp8_silu_mul_quant; every row, including the last rows
+    of every group."""
+    I, K = qgu.shape[1] // 2, qgu.shape[2]
+    _say("gate_up with SiLU*mul and 1x128 quantization in the epilogue: %d rows, G=%d" % (rows, G))
+    qhf = torch.full((rows, I), 0xAA, dtype=torch.uint8, device="cuda")
+    shf = torch.full((I // 128, rows), -1.0, dtype=torch.float32, device="cuda")
+    ops.fp8_grouped_gemm_swiglu_quant(rows, I, K, G, offs, a_rows, a_count, qx, qx.stride(0), sx, sx.stride(0),
+                                      sx.stride(1), qgu, qgu.stride(1), qgu.stride(0), sgu, sgu.stride(0),
+                                      sgu.stride(1), sgu.stride(2), qhf, I, shf, 1, rows)
+    torch.cuda.synchronize()
+    bad = torch.nonzero(qhf != qh)
+    assert bad.numel() == 0, "fused h codes differ at %s" % bad[:5].tolist()
+    assert torch.equal(shf.view(torch.int32), shb.view(torch.int32)), "fused h scales differ"
+
+
+@pytest.mark.parametrize("gather", [True, False])
+def test_gate_up_swiglu_quant_small_moe(gather):
+    """The fused gate/up epilogue on the scaled-down MoE layer with empty
+    experts, with the dispatch gather of X rows and with pre-gathered rows."""
+    d = inputs.small_moe()
+    r = d["routing"]
+    rows, G = r.row_token.size, r.offsets.size - 1
+    assert np.any(np.diff(r.offsets) == 0)
+    qx, sx = ops.quant_rowblock(dev_bf16(d["x"]), ops.AXIS_ROW, "m_major")
+    qgu, sgu, _ = ops.quant_block2d(dev_bf16(d["w_gu"]))
+    offs = dev(r.offsets)
+    I = qgu.shape[1] // 2
+    if gather:
+        a, sa, a_rows, a_count = qx, sx, dev(r.row_token), qx.shape[0]
+    else:
+        idx = torch.from_numpy(r.row_token.astype(np.int64)).cuda()
+        a, sa, a_rows, a_count = qx[idx].contiguous(), sx[idx].t().contiguous().t(), None, rows
+    gu16 = _grouped(rows, 2 * I, qgu.shape[2], G, offs, a_rows, a_count, a, sa, qgu, sgu, torch.bfloat16)
+    qh = torch.empty((rows, I), dtype=torch.uint8, device="cuda")
+    shb = torch.empty((I // 128, rows), dtype=torch.float32, device="cuda")
+    ops.fp8_silu_mul_quant(gu16, rows, I, 2 * I, 0, qh, I, shb.t(), 1, rows, None, 0)
+    torch.cuda.synchronize()
+    _fused_gate_up_matches(rows, G, offs, a_rows, a_count, a, sa, qgu, sgu, qh, shb)
 
 
 @pytest.fixture(scope="module")
