@@ -100,6 +100,19 @@ def test_host_validation_rejects_before_launch(lib):
     assert lin(fake, 4, 128, 128, fake, 128, 128, sw=None) == 1  # NULL weight scales
     assert lin(fake, -1, 128, 128, fake, 128, 128) == 2
     assert lin(None, 0, 128, 128, None, 0, 128, sx=None, sw=None) == 0
+    # grouped gate/up GEMM with SiLU*mul and 1x128 quantization of h
+    swi = lambda rows, I, K, G=2, hq=fake, ld_hq=None, hs=fake, ldb=None: ops.fp8_grouped_gemm_swiglu_quant(
+        rows, I, K, G, fake, None, rows, fake, K, fake, 1, 1, fake, K if ldb is None else ldb, 2 * I * K, fake, 1,
+        1, 1, hq, I if ld_hq is None else ld_hq, hs, 1, max(rows, 1), stream=0, raise_on_error=False)
+    assert swi(256, 96, 256) == 2                 # I % 128
+    assert swi(256, 128, 200) == 2                # K % 128
+    assert swi(256, 128, 256, G=0) == 2           # G < 1
+    assert swi(256, 128, 256, hq=None) == 1       # NULL h codes
+    assert swi(256, 128, 256, hs=None) == 1       # NULL h scales
+    assert swi(256, 128, 256, ld_hq=64) == 3      # ld_hq < I
+    assert swi(256, 128, 256, hq=fake + 4) == 4   # h codes not 8-byte aligned
+    assert swi(256, 128, 256, ldb=64) == 3        # ldb < K
+    assert swi(0, 128, 256) == 0                  # no rows: a successful no-op
 
 
 def test_dense_tile_plan(lib):
