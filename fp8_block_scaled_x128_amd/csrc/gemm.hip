@@ -34,6 +34,7 @@
 //    that the promotion overlaps the next n-tile's matrix work.
 //  - MX mode: the instruction accumulates in place with the per-lane UE8M0
 //    scale bytes of its row and 32-wide K block.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -47,6 +48,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;                         // K bytes per slice
 constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
+constexpr int kCUs = 256;                       // MI355X compute units
 
 // Tile configurations.  Every wave computes NF 16-row weight tiles (16 NF
 // weight rows) x 64 activation rows; waves are arranged 2 (n) x WAVES/2 (m),
@@ -229,6 +231,13 @@ __device__ __forceinline__ v8i read_frag(const FragOff& b, uint32_t offset) {
     r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
     return r;
 }
+// Barrier that orders LDS only: this wave's LDS accesses complete, then all
+// waves meet.  (__syncthreads would also wait for every global access in
+// flight, such as the copies of the next work item.)
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm volatile("" : "+v"(v));
     return v;
@@ -252,7 +261,12 @@ k_gemm(KArgs p) {
     static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || (BN + 63) / 64 <= WAVES,
                   "one wave per 64 rows of per-row weight scales");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLdsBytes];
-    __shared__ int s_tile[5];
+    // grouped: two slots for the published work item (the next item is
+    // published while the current one may still be read), the workgroup's
+    // item range, and wave 0's per-lane group table (up to 128 groups)
+    __shared__ int s_tile[2][5];
+    __shared__ int s_range[3];
+    __shared__ int s_lk[6][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -261,11 +275,89 @@ k_gemm(KArgs p) {
     const FragOff fo = frag_off(r16, q);
 
     // ---------------------------------------------------------------- tile
-    int32_t m_begin, m_end, n0;
+    int32_t m_begin = 0, m_end = 0, n0 = 0;
     const uint8_t* bptr = p.b;
     const uint8_t* sbp = p.sb;
+    // Grouped work items are (row tile, n-tile) pairs, row-tile major, over
+    // the list of all groups' BM-row tiles.  Workgroups are dealt round-robin
+    // to the 8 XCDs, and each XCD takes one contiguous range of work items:
+    // the n-tiles of a row tile and the row tiles of one expert then run on
+    // the same XCD and share their operand panels in its L2 (dealing n-tiles
+    // across XCDs fetched the grouped gate/up operands 4.8 times from HBM).
+    // The grid holds at most one workgroup per CU, and each workgroup walks
+    // its XCD's items in turn: the copies of its next item go out before the
+    // epilogue of the current one, so the first slices' latency overlaps the
+    // output stores.  Wave 0 finds an item's group and row tile with a prefix
+    // scan of the per-group row-tile counts; lane l keeps groups gb + 2l and
+    // gb + 2l + 1 (row bounds o0..o1, o1..o2, tile counts c0, c1).
+    const int ntn = SWIGLU ? p.swi / 128 : (p.N + BN - 1) / BN;
+    int lk_o0 = 0, lk_o1 = 0, lk_o2 = 0, lk_c0 = 0, lk_c1 = 0, lk_incl = 0;
+    int it_item = 0, it_end = 0, it_items = 0, it_slot = 0;
+    auto lk_load = [&](int gb) {
+        const int g0 = gb + 2 * lane, g1 = g0 + 1;
+        lk_o0 = g0 < p.G ? p.offsets[g0] : 0;
+        lk_o1 = g0 < p.G ? p.offsets[g0 + 1] : 0;
+        lk_o2 = g1 < p.G ? p.offsets[g1 + 1] : 0;
+        lk_c0 = g0 < p.G ? (lk_o1 - lk_o0 + BM - 1) / BM : 0;
+        lk_c1 = g1 < p.G ? (lk_o2 - lk_o1 + BM - 1) / BM : 0;
+    };
+    auto lk_scan = [&]() {
+        lk_incl = lk_c0 + lk_c1;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(lk_incl, d, 64);
+            if (lane >= d) lk_incl += v;
+        }
+    };
+    // the lane whose group holds row tile t publishes the group, the tile's
+    // index in it and the group's row bounds
+    auto lk_place = [&](int* st, int t, int gb, int carry) {
+        const int start0 = carry + lk_incl - (lk_c0 + lk_c1);
+        const int start1 = start0 + lk_c0;
+        if (t >= start0 && t < start0 + lk_c0) {
+            st[0] = gb + 2 * lane; st[1] = t - start0; st[3] = lk_o0; st[4] = lk_o1;
+        }
+        if (t >= start1 && t < start1 + lk_c1) {
+            st[0] = gb + 2 * lane + 1; st[1] = t - start1; st[3] = lk_o1; st[4] = lk_o2;
+        }
+    };
+    // wave 0: publish work item `item` in slot `slot` (group -1 if item >=
+    // items).  Up to 128 groups the per-lane table comes back from LDS.
+    auto lookup = [&](int item, int items, int slot) {
+        int* st = s_tile[slot];
+        const int t = item < items ? item / ntn : -1;
+        if (lane == 0) { st[0] = -1; st[2] = item - (item / ntn) * ntn; }
+        if (p.G <= 128) {
+            lk_o0 = s_lk[0][lane]; lk_o1 = s_lk[1][lane]; lk_o2 = s_lk[2][lane];
+            lk_c0 = s_lk[3][lane]; lk_c1 = s_lk[4][lane]; lk_incl = s_lk[5][lane];
+            lk_place(st, t, 0, 0);
+        } else {
+            int carry = 0;
+            for (int gb = 0; gb < p.G; gb += 128) {
+                lk_load(gb);
+                lk_scan();
+                lk_place(st, t, gb, carry);
+                carry += __shfl(lk_incl, 63, 64);
+            }
+        }
+    };
+    // read the published item (after a barrier); false if there is none.
+    // The results are workgroup-uniform: kept in scalar registers, so the
+    // copies' base addresses need no per-lane arithmetic.
+    auto take_tile = [&](int slot) {
+        const int* st = s_tile[slot];
+        const int g = __builtin_amdgcn_readfirstlane(st[0]);
+        if (g < 0) return false;
+        const int lt = __builtin_amdgcn_readfirstlane(st[1]);
+        m_begin = __builtin_amdgcn_readfirstlane(st[3]) + lt * BM;
+        m_end = min(__builtin_amdgcn_readfirstlane(st[4]), m_begin + BM);
+        n0 = __builtin_amdgcn_readfirstlane(st[2]) * (SWIGLU ? 128 : BN);   // SWIGLU: first h column
+        bptr = p.b + (int64_t)g * p.b_sg;
+        sbp = p.sb + (int64_t)g * p.sb_sg * ((MODE == MODE_MX || MODE == MODE_P2) ? 1 : 4);
+        return true;
+    };
     if (!GROUPED) {
-        const int ntn = (p.N + BN - 1) / BN, ntm = (p.M + BM - 1) / BM;
+        const int ntm = (p.M + BM - 1) / BM;
         const int nblk = ntn * ntm;
         const int bid = blockIdx.x;
         // consecutive tile ids on one XCD (workgroups are dealt round-robin to the 8 XCDs)
@@ -287,95 +379,40 @@ k_gemm(KArgs p) {
         m_end = min(p.M, m_begin + BM);
         n0 = tn * BN;
     } else {
-        // Work items are (row tile, n-tile) pairs, row-tile major, over the
-        // list of all groups' BM-row tiles.  Workgroups are dealt round-robin
-        // to the 8 XCDs, and each XCD takes one contiguous range of work
-        // items: the n-tiles of a row tile and the row tiles of one expert
-        // then run on the same XCD and share their operand panels in its L2
-        // (dealing n-tiles across XCDs fetched the grouped gate/up operands
-        // 4.8 times from HBM).  Wave 0 counts all row tiles (pass 1), maps
-        // the workgroup to its work item, then finds the group of the item's
-        // row tile with a prefix scan of the per-group counts (pass 2).
-        const int ntn = SWIGLU ? p.swi / 128 : (p.N + BN - 1) / BN;
-        if (threadIdx.x == 0) s_tile[0] = -1;
         if (wave == 0) {
-            // lane l looks at groups gb + 2l and gb + 2l + 1: their row
-            // bounds o0..o1, o1..o2 and row-tile counts c0, c1
-            int o0 = 0, o1 = 0, o2 = 0, c0 = 0, c1 = 0, incl = 0;
-            auto load = [&](int gb) {
-                const int g0 = gb + 2 * lane, g1 = g0 + 1;
-                o0 = g0 < p.G ? p.offsets[g0] : 0;
-                o1 = g0 < p.G ? p.offsets[g0 + 1] : 0;
-                o2 = g1 < p.G ? p.offsets[g1 + 1] : 0;
-                c0 = g0 < p.G ? (o1 - o0 + BM - 1) / BM : 0;
-                c1 = g1 < p.G ? (o2 - o1 + BM - 1) / BM : 0;
-            };
-            auto scan = [&]() {
-                incl = c0 + c1;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int v = __shfl_up(incl, d, 64);
-                    if (lane >= d) incl += v;
-                }
-            };
             // up to 128 groups: one load of the offsets serves both the
-            // total and the prefix sums
-            const bool one_pass = p.G <= 128;
+            // total and the prefix sums (and every later lookup)
             int total = 0;
-            if (one_pass) {
-                load(0);
-                scan();
-                total = __shfl(incl, 63, 64);
+            if (p.G <= 128) {
+                lk_load(0);
+                lk_scan();
+                total = __shfl(lk_incl, 63, 64);
+                s_lk[0][lane] = lk_o0; s_lk[1][lane] = lk_o1; s_lk[2][lane] = lk_o2;
+                s_lk[3][lane] = lk_c0; s_lk[4][lane] = lk_c1; s_lk[5][lane] = lk_incl;
             } else {
                 for (int gb = 0; gb < p.G; gb += 128) {
-                    load(gb);
-                    int c = c0 + c1;
+                    lk_load(gb);
+                    int c = lk_c0 + lk_c1;
 #pragma unroll
                     for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
                     total += c;
                 }
             }
+            // XCD x = bid % 8 owns items [x per, x per + per); its workgroups
+            // take them in turn, 8 / gridDim apart
             const int items = total * ntn;
             const int per = (items + 7) / 8;
             const int bid = blockIdx.x;
-            const int item = bid / 8 < per ? (bid % 8) * per + bid / 8 : items;
-            const int t = item < items ? item / ntn : -1;   // row tile, -1: no work
-            if (lane == 0) s_tile[2] = item - (item / ntn) * ntn;
-            // the lane whose group holds row tile t publishes the group, the
-            // tile's index in it and the group's row bounds
-            auto place = [&](int gb, int carry) {
-                const int start0 = carry + incl - (c0 + c1);
-                const int start1 = start0 + c0;
-                if (t >= start0 && t < start0 + c0) {
-                    s_tile[0] = gb + 2 * lane; s_tile[1] = t - start0; s_tile[3] = o0; s_tile[4] = o1;
-                }
-                if (t >= start1 && t < start1 + c1) {
-                    s_tile[0] = gb + 2 * lane + 1; s_tile[1] = t - start1; s_tile[3] = o1; s_tile[4] = o2;
-                }
-            };
-            if (one_pass) {
-                place(0, 0);
-            } else {
-                int carry = 0;
-                for (int gb = 0; gb < p.G; gb += 128) {
-                    load(gb);
-                    scan();
-                    place(gb, carry);
-                    carry += __shfl(incl, 63, 64);
-                }
-            }
+            const int first = (bid % 8) * per + bid / 8;
+            const int last = min((bid % 8) * per + per, items);
+            if (lane == 0) { s_range[0] = first; s_range[1] = last; s_range[2] = items; }
+            lookup(first < last ? first : items, items, 0);
         }
         __syncthreads();
-        // the lookup results are workgroup-uniform: kept in scalar registers,
-        // so the copies' base addresses need no per-lane arithmetic
-        const int g = __builtin_amdgcn_readfirstlane(s_tile[0]);
-        if (g < 0) return;                         // uniform: no tile for this work item
-        const int lt = __builtin_amdgcn_readfirstlane(s_tile[1]);
-        m_begin = __builtin_amdgcn_readfirstlane(s_tile[3]) + lt * BM;
-        m_end = min(__builtin_amdgcn_readfirstlane(s_tile[4]), m_begin + BM);
-        n0 = __builtin_amdgcn_readfirstlane(s_tile[2]) * (SWIGLU ? 128 : BN);   // SWIGLU: first h column
-        bptr += (int64_t)g * p.b_sg;
-        sbp += (int64_t)g * p.sb_sg * ((MODE == MODE_MX || MODE == MODE_P2) ? 1 : 4);
+        it_item = __builtin_amdgcn_readfirstlane(s_range[0]);
+        it_end = __builtin_amdgcn_readfirstlane(s_range[1]);
+        it_items = __builtin_amdgcn_readfirstlane(s_range[2]);
+        if (!take_tile(0)) return;                 // uniform: no work item for this workgroup
     }
     auto arow = [&](int m_local) {             // physical A row of tile row m_local (clamped)
         int m = min(m_begin + m_local, m_end - 1);
@@ -390,19 +427,6 @@ k_gemm(KArgs p) {
     // past the tile's kCopiesB weight copies repeat the first ones.
     uint32_t offB[C::kDmaB], offA[C::kDmaA];
     auto bcopy = [&](int t) { const int j = wave * C::kDmaB + t; return j < C::kCopiesB ? j : j - C::kCopiesB; };
-#pragma unroll
-    for (int j = 0; j < C::kDmaB; ++j) {
-        const int row = bcopy(j) * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz(row);
-        const int brow = !SWIGLU ? min(n0 + row, p.N - 1) : row < 128 ? n0 + row : p.swi + n0 + row - 128;
-        offB[j] = (uint32_t)((int64_t)brow * p.ldb + chunk * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < C::kDmaA; ++j) {
-        const int row = (wave * C::kDmaA + j) * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz(row);
-        offA[j] = (uint32_t)((int64_t)arow(row) * p.lda + chunk * 16);
-    }
     // Scale copies (4-byte lanes).  Activation scales: waves [0, BM/64) copy
     // rows [64 w, +64).  Weight scales: BLOCK128 / P2 -> wave (BM/64) % WAVES copies the
     // two 128-row blocks of the tile; ROW128 / MX -> waves [0, ceil(BN/64))
@@ -412,24 +436,42 @@ k_gemm(KArgs p) {
     const bool has_sb = MODE != MODE_KINV &&
                         ((MODE == MODE_BLOCK128 || MODE == MODE_P2) ? wave == (BM / 64) % WAVES : wave < (BN + 63) / 64);
     uint32_t sa_off = 0, sb_off = 0;            // byte offsets without the slice term (< 4 GiB)
-    if (has_sa) {
-        const int m = arow(wave * 64 + lane);
-        sa_off = (uint32_t)((MODE == MODE_MX || MODE == MODE_P2) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4);
-    }
-    if (MODE == MODE_BLOCK128 || MODE == MODE_P2) {
-        const int nb = !SWIGLU ? min(n0 / 128 + (lane & 1), (p.N - 1) / 128)
-                               : ((lane & 1) ? (p.swi + n0) / 128 : n0 / 128);   // gate block, up block
-        sb_off = (uint32_t)((int64_t)nb * p.sb_sn * (MODE == MODE_P2 ? 1 : 4));
-    } else if (MODE != MODE_KINV) {
-        const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
-        sb_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4);
-    }
     // BLOCK128 weight scales: the wave's n-tiles before nb_w lie in the
     // tile's first 128-row block, the rest in the next one.  Tiles span at
     // most two blocks: 256 rows start at multiples of 256, 160 rows at
     // multiples of 160 (block offsets 0..96) and 192 rows at multiples of
     // 192 (offsets 0 or 64).
-    const int nb_w = NF == 8 ? NF : min(max(((n0 / 128 + 1) * 128 - (n0 + wn * 16 * NF)) / 16, 0), NF);
+    int nb_w = NF;
+    // per-lane copy offsets of the tile at (m_begin, m_end, n0, bptr, sbp)
+    auto setup_tile = [&]() {
+#pragma unroll
+        for (int j = 0; j < C::kDmaB; ++j) {
+            const int row = bcopy(j) * 8 + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz(row);
+            const int brow = !SWIGLU ? min(n0 + row, p.N - 1) : row < 128 ? n0 + row : p.swi + n0 + row - 128;
+            offB[j] = (uint32_t)((int64_t)brow * p.ldb + chunk * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < C::kDmaA; ++j) {
+            const int row = (wave * C::kDmaA + j) * 8 + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz(row);
+            offA[j] = (uint32_t)((int64_t)arow(row) * p.lda + chunk * 16);
+        }
+        if (has_sa) {
+            const int m = arow(wave * 64 + lane);
+            sa_off = (uint32_t)((MODE == MODE_MX || MODE == MODE_P2) ? (int64_t)m * p.sa_sm : (int64_t)m * p.sa_sm * 4);
+        }
+        if (MODE == MODE_BLOCK128 || MODE == MODE_P2) {
+            const int nb = !SWIGLU ? min(n0 / 128 + (lane & 1), (p.N - 1) / 128)
+                                   : ((lane & 1) ? (p.swi + n0) / 128 : n0 / 128);   // gate block, up block
+            sb_off = (uint32_t)((int64_t)nb * p.sb_sn * (MODE == MODE_P2 ? 1 : 4));
+        } else if (MODE != MODE_KINV) {
+            const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
+            sb_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4);
+        }
+        nb_w = NF == 8 ? NF : min(max(((n0 / 128 + 1) * 128 - (n0 + wn * 16 * NF)) / 16, 0), NF);
+    };
+    setup_tile();
     const uint32_t lds0 = lds_addr(smem);
     auto bstage = [&](int i) { return lds0 + (uint32_t)(i * C::kBStageBytes); };                      // weights + sb
     auto abuf = [&](int i) { return lds0 + (uint32_t)(C::kBStages * C::kBStageBytes + i * C::kABufBytes); };  // acts + sa
@@ -459,30 +501,29 @@ k_gemm(KArgs p) {
     };
 
     v4f acc[NF][4];
-#pragma unroll
-    for (int i = 0; i < NF; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // Issue order (the waits rely on it): step kb issues the copies of
     // activation slice kb + kLeadA (scales right after the barriers, tile in
     // the first n-tile steps) and then those of weight slice kb + kLeadB; the
     // prologue issues the same sequence for the steps -kLeadMax..-1.
     const int nk = p.K / BK;
+    auto prologue = [&]() {
 #pragma unroll
-    for (int j = -C::kLeadMax; j < 0; ++j) {
-        const int sa_kb = j + C::kLeadA, sb_kb = j + C::kLeadB;
-        if (sa_kb >= 0 && sa_kb < nk) {
-            copy_sa(sa_kb, sa_kb % C::kAStages);
+        for (int j = -C::kLeadMax; j < 0; ++j) {
+            const int sa_kb = j + C::kLeadA, sb_kb = j + C::kLeadB;
+            if (sa_kb >= 0 && sa_kb < nk) {
+                copy_sa(sa_kb, sa_kb % C::kAStages);
 #pragma unroll
-            for (int t = 0; t < C::kDmaA; ++t) copy_a(sa_kb, sa_kb % C::kAStages, t);
+                for (int t = 0; t < C::kDmaA; ++t) copy_a(sa_kb, sa_kb % C::kAStages, t);
+            }
+            if (sb_kb >= 0 && sb_kb < nk) {
+                copy_sb(sb_kb, sb_kb % C::kBStages);
+#pragma unroll
+                for (int t = 0; t < C::kDmaB; ++t) copy_b(sb_kb, sb_kb % C::kBStages, t);
+            }
         }
-        if (sb_kb >= 0 && sb_kb < nk) {
-            copy_sb(sb_kb, sb_kb % C::kBStages);
-#pragma unroll
-            for (int t = 0; t < C::kDmaB; ++t) copy_b(sb_kb, sb_kb % C::kBStages, t);
-        }
-    }
+    };
+    prologue();
 
     // One K slice.  CA / CB (compile time): this step copies activation slice
     // kb + kLeadA / weight slice kb + kLeadB.  Both hold in every step but the
@@ -635,6 +676,18 @@ k_gemm(KArgs p) {
             if (C::kDefer) promote(NF - 1, (NF - 1) & 1);
         }
     };
+    // Grouped: one work item per trip; dense: one trip.  Wave 0 publishes the
+    // next item at the start of each trip, in the slot not being read.
+    for (;;) {
+    if constexpr (GROUPED) {
+        it_item += (int)(gridDim.x / 8);
+        it_slot ^= 1;
+        if (wave == 0) lookup(it_item < it_end ? it_item : it_items, it_items, it_slot);
+    }
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     int kb = 0;
     for (; kb + C::kLeadMax < nk; ++kb) step(kb, std::true_type{}, std::true_type{});
     // At most kLeadMax (<= 2) steps remain.  With unequal leads the next to
@@ -649,11 +702,24 @@ k_gemm(KArgs p) {
     }
     for (; kb < nk; ++kb) step(kb, std::false_type{}, std::false_type{});
 
+    // Grouped: take the next work item; its first copies go out in the
+    // middle of this item's epilogue.  The barrier (LDS only: every wave has
+    // finished reading the last slice, and wave 0 has published the item)
+    // frees the first stages and the activation buffer; the epilogue stages
+    // its outputs in weight stage 2, which the next item's first steps do
+    // not fill.
+    const int32_t em_begin = m_begin, em_end = m_end, en0 = n0;
+    bool more = false;
+    if constexpr (GROUPED) {
+        lds_barrier();
+        more = take_tile(it_slot);
+    }
+
     // ---------------------------------------------------------- epilogue
     // N % 128 == 0: with 256-row tiles each wave covers 128 aligned n, so a
     // wave's columns are all inside the matrix or all outside; other tiles
     // check each 16-column n-tile (wave-uniform).  Rows are checked per lane.
-    const int nw0 = n0 + wn * 16 * NF;
+    const int nw0 = en0 + wn * 16 * NF;
     const bool wave_out = nw0 < p.N;
     if (MODE == MODE_KINV && wave_out) {
         // scales constant along K: each output times sa(m) * sb(n), once
@@ -661,7 +727,7 @@ k_gemm(KArgs p) {
         const float* sb = reinterpret_cast<const float*>(p.sb);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int m = min(m_begin + wm * 64 + mt * 16 + r16, m_end - 1);
+            const int m = min(em_begin + wm * 64 + mt * 16 + r16, em_end - 1);
             const float sam = sa[(int64_t)m * p.sa_sm];
 #pragma unroll
             for (int nt = 0; nt < NF; ++nt)
@@ -677,36 +743,58 @@ k_gemm(KArgs p) {
     // a lane holds 4 consecutive columns of one row per 16 x 16 block, and
     // storing those directly makes each store instruction write 32-byte
     // pieces of 16 different rows.  Each wave stages its 64 x 16 NF block in
-    // passes of 32 rows (row pitch padded by 16 bytes to spread the banks)
-    // and reads it back in 16-byte pieces of consecutive columns.  The first
-    // barrier frees the operand buffers; afterwards each wave touches only
-    // its own staging region, whose LDS accesses complete in program order.
+    // passes of kRows rows (row pitch padded by 16 bytes to spread the banks)
+    // and reads it back in 16-byte pieces of consecutive columns.  Dense: the
+    // staging uses the operand buffers, freed by a barrier, 32 rows a pass.
+    // Grouped: it uses weight stage 2 (the next item's copies are already on
+    // their way to the other buffers), 8 rows a pass.  Each wave then touches
+    // only its own staging region, whose LDS accesses complete in program
+    // order.
     constexpr int EB = OUTF32 ? 4 : 2;                 // output bytes per element
-    constexpr int kRows = 32;                          // rows per pass
+    constexpr int kRows = GROUPED ? 8 : 32;            // rows per pass
     constexpr int kPitch = 16 * NF * EB + 16;          // staged row, bytes
     constexpr int kChunks = 16 * NF * EB / 16;         // 16-byte pieces per row
-    static_assert(WAVES * kRows * kPitch <= C::kLdsBytes, "epilogue staging fits the operand buffers");
+    static_assert(GROUPED ? (C::kBStages == 3 && WAVES * kRows * kPitch <= C::kBStageBytes)
+                          : WAVES * kRows * kPitch <= C::kLdsBytes,
+                  "epilogue staging fits its region");
     static_assert((kRows * kChunks) % 64 == 0, "whole store instructions per pass");
-    __syncthreads();
-    if (!wave_out) return;
-    const uint32_t wst = lds0 + (uint32_t)(wave * kRows * kPitch);
+    if constexpr (!GROUPED) {
+        __syncthreads();
+        if (!wave_out) return;
+    }
+    const uint32_t ebase = GROUPED ? bstage(2) : lds0;
+    const uint32_t wst = ebase + (uint32_t)(wave * kRows * kPitch);
     uint8_t* cbase = static_cast<uint8_t*>(p.c) + (int64_t)nw0 * EB;
+    // SWIGLU tiles never leave the matrix (wave_out holds), so its barriers
+    // are met by every wave
 #pragma unroll
     for (int pass = 0; pass < 64 / kRows; ++pass) {
+        if (GROUPED && pass == 64 / kRows / 2 && more) {
+            // half of the accumulators are staged (and free): the next
+            // item's copy offsets and first copies fit beside the rest
+            setup_tile();
+            prologue();
+        }
+        if (wave_out) {
 #pragma unroll
-        for (int h = 0; h < kRows / 16; ++h) {
-            const int mt = pass * (kRows / 16) + h;
-            const uint32_t rowa = wst + (uint32_t)((h * 16 + r16) * kPitch + 4 * q * EB);
+            for (int h = 0; h < (kRows + 15) / 16; ++h) {
+                const int mt = (pass * kRows) / 16 + h;
+                const int ro = (pass * kRows) % 16;        // first m-tile row of the pass (kRows < 16)
+                const uint32_t rowa = wst + (uint32_t)((h * 16 + r16 - ro) * kPitch + 4 * q * EB);
+                if (kRows >= 16 || (r16 >= ro && r16 < ro + kRows)) {
 #pragma unroll
-            for (int nt = 0; nt < NF; ++nt) {
-                const uint32_t a = rowa + nt * 16 * EB;
-                if (OUTF32) {
-                    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>((uintptr_t)a) =
-                        f32x4{acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]};
-                } else {
-                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)a) =
-                        u32x2{pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]), pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3])};
+                    for (int nt = 0; nt < NF; ++nt) {
+                        const uint32_t a = rowa + nt * 16 * EB;
+                        if (OUTF32) {
+                            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>((uintptr_t)a) =
+                                f32x4{acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]};
+                        } else {
+                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)a) =
+                                u32x2{pack_bf16x2(acc[nt][mt][0], acc[nt][mt][1]),
+                                      pack_bf16x2(acc[nt][mt][2], acc[nt][mt][3])};
+                        }
+                    }
                 }
             }
         }
@@ -718,13 +806,14 @@ k_gemm(KArgs p) {
             // up are the bf16-rounded GEMM outputs and h uses the SiLU of the
             // separate SiLU*mul kernel, so codes and scales equal those of
             // the bf16 GEMM followed by fp8_silu_mul_quant.
-            __syncthreads();
+            lds_barrier();
             const int sub = lane & 15;
+            constexpr int kPerWave = 4 * kRows / WAVES;     // h rows per wave and pass
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int R = wave * 16 + it * 4 + (lane >> 4);      // row of the pass, 0..127
-                const int wr = R >> 5, rr = R & 31;
-                const uint32_t ga = lds0 + (uint32_t)(2 * wr * kRows * kPitch + rr * kPitch + sub * 16);
+            for (int it = 0; it < kPerWave / 4; ++it) {
+                const int R = wave * kPerWave + it * 4 + (lane >> 4);    // row of the pass, 0 .. 4 kRows - 1
+                const int wr = R / kRows, rr = R % kRows;
+                const uint32_t ga = ebase + (uint32_t)(2 * wr * kRows * kPitch + rr * kPitch + sub * 16);
                 const u32x4 gv = lds_read16(ga);
                 const u32x4 uv = lds_read16(ga + kRows * kPitch);
                 float g[8], u[8], v[8];
@@ -736,25 +825,27 @@ k_gemm(KArgs p) {
                 const float sc = amax / kE4M3Max;
                 uint32_t w0, w1;
                 encode8(v, sc, w0, w1);
-                const int m = m_begin + wr * 64 + pass * kRows + rr;
-                if (m < m_end) {
-                    *reinterpret_cast<uint2*>(p.hq + (int64_t)m * p.ld_hq + n0 + sub * 8) = make_uint2(w0, w1);
-                    if (sub == 0) p.hs[(int64_t)m * p.hs_sm + (int64_t)(n0 / 128) * p.hs_sg] = sc;
+                const int m = em_begin + wr * 64 + pass * kRows + rr;
+                if (m < em_end) {
+                    *reinterpret_cast<uint2*>(p.hq + (int64_t)m * p.ld_hq + en0 + sub * 8) = make_uint2(w0, w1);
+                    if (sub == 0) p.hs[(int64_t)m * p.hs_sm + (int64_t)(en0 / 128) * p.hs_sg] = sc;
                 }
             }
-            __syncthreads();     // the next pass overwrites the staging regions
-        } else {
+            lds_barrier();     // the next pass overwrites the staging regions
+        } else if (wave_out) {
 #pragma unroll
             for (int it = 0; it < kRows * kChunks / 64; ++it) {
                 const int sidx = it * 64 + lane;
                 const int row = sidx / kChunks, ch = sidx % kChunks;
                 const u32x4 v = lds_read16(wst + (uint32_t)(row * kPitch + ch * 16));
-                const int m = m_begin + wm * 64 + pass * kRows + row;
+                const int m = em_begin + wm * 64 + pass * kRows + row;
                 const int col = ch * (16 / EB);
-                if (m < m_end && (NF == 8 || nw0 + col < p.N))
+                if (m < em_end && (NF == 8 || nw0 + col < p.N))
                     *reinterpret_cast<u32x4*>(cbase + ((int64_t)m * p.ldc) * EB + col * EB) = v;
             }
         }
+    }
+    if (!more) break;
     }
 }
 
@@ -768,7 +859,7 @@ hipError_t launch(const KArgs& p, bool out_f32, hipStream_t st) {
         // upper bound on the work items (row tiles over all groups x n-tiles),
         // rounded up to a multiple of the 8 XCDs
         const int64_t items = ((int64_t)(p.M + C::BM - 1) / C::BM + p.G) * ((p.N + C::BN - 1) / C::BN);
-        grid = dim3((unsigned)((items + 7) / 8 * 8));
+        grid = dim3((unsigned)std::min<int64_t>((items + 7) / 8 * 8, kCUs));
     }
     if (out_f32)
         hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES, NF, WN>), grid, dim3(C::kThreads), 0, st, p);
@@ -800,7 +891,6 @@ int waves_for(int64_t rows, int64_t N, int64_t extra_tiles = 0) {
 // runs each tile at its lone speed, only about 12% faster per slice (a lone
 // 4-wave workgroup leaves each SIMD one wave, so pairs nearly double the
 // throughput).
-constexpr int kCUs = 256;
 struct TileCfg {
     int waves, nf, wn;
     double slice_cycles, tile_cycles;   // per round of tiles (wn = 1: two tiles per CU)
@@ -934,7 +1024,7 @@ hipError_t launch_gemm_grouped_swiglu(const GemmArgs& g, int64_t I, uint8_t* hq,
     // upper bound on the work items (row tiles x 128-column blocks of h),
     // rounded up to a multiple of the 8 XCDs
     const int64_t items = ((int64_t)(g.M + C::BM - 1) / C::BM + g.G) * (I / 128);
-    const dim3 grid((unsigned)((items + 7) / 8 * 8));
+    const dim3 grid((unsigned)std::min<int64_t>((items + 7) / 8 * 8, kCUs));
     hipLaunchKernelGGL((k_gemm<MODE_BLOCK128, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
     return hipGetLastError();
 }
