@@ -21,6 +21,8 @@ repetitions, each kernel bracketed by HIP events on the launch stream):
                      + 1x128 requantization, grouped down GEMM, combine
     moe_blockwise_fused  the same layer with SiLU*mul and the requantization
                      in the gate_up GEMM's epilogue
+    moe_mxfp8        the layer in MXFP8 (1x32 UE8M0 blocks); moe_mxfp8_fused
+                     with the fused gate_up epilogue
     moe_mxfp8        the same layer with 1x32 UE8M0 scales (MXFP8)
 
 Prints ONE JSON line: value = GEMM FLOPs of the headline step / step time
@@ -46,7 +48,7 @@ PEAK_HBM_GBS = 8000.0
 M_TOK, HID, INTER = 4096, 2560, 9728
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
 WORKLOADS = ("tiny_linear", "mlp_backward", "mlp_backward_mxfp8", "moe_blockwise", "moe_blockwise_fused", "moe_mxfp8",
-             "up_proj_rowwise",
+             "moe_mxfp8_fused", "up_proj_rowwise",
              "up_proj_pow2")
 
 
@@ -330,7 +332,9 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R, fused=False):
         "grouped_rows": rows, "seed": 3}
 
 
-def wl_moe_mxfp8(torch, ops, inputs, to_dev, R):
+def wl_moe_mxfp8(torch, ops, inputs, to_dev, R, fused=False):
+    """The MoE layer in MXFP8.  fused: SiLU*mul and the 1x32 quantization of
+    h in the gate/up GEMM's epilogue (mxfp8_grouped_gemm_swiglu_quant)."""
     d = _moe_inputs(inputs)
     r = d["routing"]
     T, H = d["x"].shape
@@ -346,7 +350,7 @@ def wl_moe_mxfp8(torch, ops, inputs, to_dev, R):
     qx, sx = u8(T, H), u8(T, H // 32)
     qgu, sgu = u8(E * N2, H), u8(E * N2, H // 32)
     qdt, sdt = u8(E * H, I), u8(E * H, I // 32)
-    gu = torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
+    gu = None if fused else torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
     qh, sh = u8(rows, I), u8(rows, I // 32)
     y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
     pos, wts = torch.from_numpy(r.token_rows).cuda(), torch.from_numpy(r.weights).cuda()
@@ -359,18 +363,24 @@ def wl_moe_mxfp8(torch, ops, inputs, to_dev, R):
          ("GB/s", qbytes_row(E * N2, H, 32, 1))),
         ("mx_quant_w_down_t", lambda i: ops.mxfp8_quant(wdt, E * H, I, I, qdt, I, sdt, I // 32, 1),
          ("GB/s", qbytes_row(E * H, I, 32, 1))),
+    ] + ([
+        ("mx_grouped_gemm_gate_up_swiglu_quant", lambda i: ops.mxfp8_grouped_gemm_swiglu_quant(
+            rows, I, H, G, offs, a_rows, T, qx, H, sx, H // 32, qgu, H, N2 * H, sgu, H // 32, N2 * (H // 32),
+            qh, I, sh, I // 32, 1), ("TFLOP/s", 2.0 * rows * N2 * H)),
+    ] if fused else [
         ("mx_grouped_gemm_gate_up", lambda i: ops.mxfp8_gemm(
             rows, N2, H, G, offs, a_rows, T, qx, H, sx, H // 32, qgu, H, N2 * H, sgu, H // 32, N2 * (H // 32),
             gu, N2, ops.OUT_BF16), ("TFLOP/s", 2.0 * rows * N2 * H)),
         ("silu_mul_quant_mx", lambda i: ops.fp8_silu_mul_quant(gu, rows, I, N2, 1, qh, I, sh, I // 32, 1, None, 0),
          ("GB/s", rows * N2 * 2 + rows * I + rows * (I // 32))),
+    ]) + [
         ("mx_grouped_gemm_down", lambda i: ops.mxfp8_gemm(
             rows, H, I, G, offs, None, rows, qh, I, sh, I // 32, qdt, I, H * I, sdt, I // 32, H * (I // 32),
             y, H, ops.OUT_BF16), ("TFLOP/s", 2.0 * rows * H * I)),
         ("combine", lambda i: ops.fp8_moe_combine(y, rows, H, H, pos, wts, T, k, out, H, ops.OUT_BF16),
          ("GB/s", combine_bytes(rows, H, T, k))),
-    ], {"workload": "moe_mxfp8", "tokens": T, "hidden": H, "experts": E, "intermediate": I, "top_k": 8,
-        "grouped_rows": rows, "seed": 3}
+    ], {"workload": "moe_mxfp8_fused" if fused else "moe_mxfp8", "tokens": T, "hidden": H, "experts": E,
+        "intermediate": I, "top_k": 8, "grouped_rows": rows, "seed": 3}
 
 
 # ---------------------------------------------------------- CPU baseline
@@ -548,7 +558,8 @@ def main():
     table = {"tiny_linear": wl_tiny_linear, "mlp_backward": wl_mlp_backward,
              "mlp_backward_mxfp8": wl_mlp_backward_mxfp8, "up_proj_pow2": wl_up_proj_pow2,
              "moe_blockwise": wl_moe_blockwise, "moe_mxfp8": wl_moe_mxfp8, "up_proj_rowwise": wl_up_proj_rowwise,
-             "moe_blockwise_fused": lambda *a: wl_moe_blockwise(*a, fused=True)}
+             "moe_blockwise_fused": lambda *a: wl_moe_blockwise(*a, fused=True),
+             "moe_mxfp8_fused": lambda *a: wl_moe_mxfp8(*a, fused=True)}
     others = {}
     for wname in wanted:
         if wname not in table:

@@ -489,6 +489,47 @@ fp8bs_status mxfp8_gemm(int64_t rows, int64_t N, int64_t K, int32_t G, const int
     return launched(launch_gemm_mx(g, stream), "mxfp8_gemm");
 }
 
+fp8bs_status mxfp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int64_t K, int32_t G,
+                                             const int32_t* offsets, const int32_t* a_rows, int64_t a_count,
+                                             const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t lds_a,
+                                             const uint8_t* b, int64_t ldb, int64_t b_stride_g, const uint8_t* sb,
+                                             int64_t lds_b, int64_t sb_stride_g, uint8_t* hq, int64_t ld_hq,
+                                             uint8_t* hs, int64_t hs_stride_row, int64_t hs_stride_group,
+                                             hipStream_t stream) {
+    if (G < 1) return fail(FP8BS_ERR_SHAPE, "G must be >= 1");
+    if (I < 0 || I % 128) return fail(FP8BS_ERR_SHAPE, "I %% 128 != 0 (I=%lld)", (long long)I);
+    if (I > INT32_MAX / 4) return fail(FP8BS_ERR_SHAPE, "size too large");
+    // the operands are checked as for the grouped mxfp8_gemm with N = 2 I;
+    // the bf16 gate/up output is never written (b stands in for it)
+    fp8bs_status v = check_gemm_common(total_rows, 2 * I, K, a, lda, b, ldb, b, 2 * I, FP8BS_OUT_BF16, 128);
+    if (v != FP8BS_OK) return v;
+    if (total_rows == 0 || I == 0) return ok();
+    if (!offsets || !sa || !sb || !hq || !hs) return fail(FP8BS_ERR_NULL, "offsets, sa, sb, hq and hs are required");
+    if (lds_a < K / 32 || lds_b < K / 32) return fail(FP8BS_ERR_STRIDE, "scale leading dimension < K/32");
+    if (lds_a % 4 || lds_b % 4 || !aligned(sa, 4) || !aligned(sb, 4) || !aligned(offsets, 4))
+        return fail(FP8BS_ERR_ALIGN, "scale arrays must be 4-byte aligned with lds %% 4 == 0");
+    if (ld_hq < I) return fail(FP8BS_ERR_STRIDE, "ld_hq < I");
+    if (ld_hq % 8 || !aligned(hq, 8)) return fail(FP8BS_ERR_ALIGN, "hq must be 8-byte aligned with ld_hq %% 8 == 0");
+    if (b_stride_g % 16) return fail(FP8BS_ERR_ALIGN, "b_stride_g %% 16 != 0");
+    const int64_t arows = a_rows ? a_count : total_rows;
+    if (a_rows && a_count < 1) return fail(FP8BS_ERR_SHAPE, "a_count must be >= 1 with a_rows");
+    if ((uint64_t)arows * (uint64_t)lda >= (1ull << 32) || (uint64_t)(2 * I) * (uint64_t)ldb >= (1ull << 32))
+        return fail(FP8BS_ERR_SHAPE, "an operand exceeds 4 GiB");
+    if (((total_rows + 127) / 128 + G) * (I / 128) >= (1ll << 31) - 8) return fail(FP8BS_ERR_SHAPE, "too many tiles");
+    if ((v = check_scale_extent("sa", arows, lds_a, 1, 0, 1)) != FP8BS_OK) return v;
+    if ((v = check_scale_extent("sb", 2 * I, lds_b, 1, 0, 1)) != FP8BS_OK) return v;
+    if ((v = check_scale_extent("hs", total_rows, hs_stride_row, I / 32, hs_stride_group, 1)) != FP8BS_OK) return v;
+    if (sb_stride_g < 0 || b_stride_g < 0) return fail(FP8BS_ERR_STRIDE, "negative group stride");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    MxGemmArgs g{};
+    g.M = total_rows; g.N = 2 * I; g.K = K; g.a = a; g.lda = lda; g.sa = sa; g.lds_a = lds_a;
+    g.b = b; g.ldb = ldb; g.b_sg = b_stride_g; g.sb = sb; g.lds_b = lds_b; g.sb_sg = sb_stride_g;
+    g.G = G; g.offsets = offsets; g.a_rows = a_rows;
+    return launched(launch_gemm_mx_swiglu(g, I, hq, ld_hq, hs, hs_stride_row, hs_stride_group, stream),
+                    "mxfp8_grouped_gemm_swiglu_quant");
+}
+
 fp8bs_status fp8bs_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
     if (n < 0) return fail(FP8BS_ERR_SHAPE, "n < 0");
     if (n == 0) return ok();

@@ -141,12 +141,13 @@ struct KArgs {
     void* c; int64_t ldc;
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
     int32_t kinv_row;                          // MODE_KINV: sb indexed by n (1) or n / 128 (0)
-    // SWIGLU (grouped gate/up GEMM with SiLU*mul and 1x128 quantization in
+    // SWIGLU (grouped gate/up GEMM with SiLU*mul and the quantization of h in
     // the epilogue): B rows [0, swi) are gate rows, [swi, 2 swi) up rows;
-    // h codes hq [rows][ld_hq], h scales hs[m * hs_sm + (j / 128) * hs_sg]
+    // h codes hq [rows][ld_hq]; h scales hs[m * hs_sm + group * hs_sg], fp32
+    // per 128 columns (BLOCK128) or UE8M0 bytes per 32 columns (MX)
     int32_t swi;
     uint8_t* hq; int64_t ld_hq;
-    float* hs; int64_t hs_sm, hs_sg;
+    void* hs; int64_t hs_sm, hs_sg;
 };
 
 __device__ __forceinline__ int swz(int r) { return r & 7; }
@@ -254,8 +255,9 @@ k_gemm(KArgs p) {
     using C = Cfg<WAVES, NF, (MODE == MODE_ROW128 || MODE == MODE_MX), WN>;
     // SWIGLU tiles: 256 weight rows = 128 gate rows (wave column 0) and the
     // matching 128 up rows (wave column 1) for 128 columns of h
-    static_assert(!SWIGLU || (GROUPED && MODE == MODE_BLOCK128 && !OUTF32 && WAVES == 8 && NF == 8 && WN == 2),
-                  "SiLU*mul epilogue: grouped BLOCK128 GEMM, 256 x 256 tiles, bf16 rounding of gate and up");
+    static_assert(!SWIGLU || (GROUPED && (MODE == MODE_BLOCK128 || MODE == MODE_MX) && !OUTF32 && WAVES == 8 &&
+                              NF == 8 && WN == 2),
+                  "SiLU*mul epilogue: grouped BLOCK128 or MX GEMM, 256 x 256 tiles, bf16 rounding of gate and up");
     constexpr int BM = C::BM, BN = C::BN;
     // per-row weight scales are copied by waves 0 .. ceil(BN / 64) - 1 in 64-row pieces
     static_assert(MODE == MODE_BLOCK128 || MODE == MODE_KINV || MODE == MODE_P2 || (BN + 63) / 64 <= WAVES,
@@ -466,7 +468,8 @@ k_gemm(KArgs p) {
                                    : ((lane & 1) ? (p.swi + n0) / 128 : n0 / 128);   // gate block, up block
             sb_off = (uint32_t)((int64_t)nb * p.sb_sn * (MODE == MODE_P2 ? 1 : 4));
         } else if (MODE != MODE_KINV) {
-            const int n = min(n0 + (wave & 3) * 64 + lane, p.N - 1);
+            const int r = (wave & 3) * 64 + lane;          // tile row
+            const int n = !SWIGLU ? min(n0 + r, p.N - 1) : r < 128 ? n0 + r : p.swi + n0 + r - 128;
             sb_off = (uint32_t)((MODE == MODE_MX) ? (int64_t)n * p.sb_sn : (int64_t)n * p.sb_sn * 4);
         }
         nb_w = NF == 8 ? NF : min(max(((n0 / 128 + 1) * 128 - (n0 + wn * 16 * NF)) / 16, 0), NF);
@@ -821,15 +824,32 @@ k_gemm(KArgs p) {
                 unpack8(make_uint4(uv.x, uv.y, uv.z, uv.w), u);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(silu_mul_bf16(g[i], u[i]) << 16);
-                const float amax = group16_max(absmax8(v));
-                const float sc = amax / kE4M3Max;
-                uint32_t w0, w1;
-                encode8(v, sc, w0, w1);
                 const int m = em_begin + wr * 64 + pass * kRows + rr;
-                if (m < em_end) {
-                    *reinterpret_cast<uint2*>(p.hq + (int64_t)m * p.ld_hq + en0 + sub * 8) = make_uint2(w0, w1);
-                    if (sub == 0) p.hs[(int64_t)m * p.hs_sm + (int64_t)(en0 / 128) * p.hs_sg] = sc;
+                uint32_t w0, w1;
+                if (MODE == MODE_MX) {
+                    // four 1x32 blocks per row: 4 lanes each, UE8M0 scales
+                    // (the rule of the MX quantizer)
+                    const float amax = group4_max(absmax8(v));
+                    const int e = mx_exponent(amax);
+                    const float f = pow2_neg(e);
+                    if (amax == 0.0f) {
+                        w0 = 0u; w1 = 0u;
+                    } else {
+                        w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+                        w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+                    }
+                    if (m < em_end && (sub & 3) == 0)
+                        static_cast<uint8_t*>(p.hs)[(int64_t)m * p.hs_sm + (int64_t)(en0 / 32 + (sub >> 2)) * p.hs_sg] =
+                            (uint8_t)(e + 127);
+                } else {
+                    const float amax = group16_max(absmax8(v));
+                    const float sc = amax / kE4M3Max;
+                    encode8(v, sc, w0, w1);
+                    if (m < em_end && sub == 0)
+                        static_cast<float*>(p.hs)[(int64_t)m * p.hs_sm + (int64_t)(en0 / 128) * p.hs_sg] = sc;
                 }
+                if (m < em_end)
+                    *reinterpret_cast<uint2*>(p.hq + (int64_t)m * p.ld_hq + en0 + sub * 8) = make_uint2(w0, w1);
             }
             lds_barrier();     // the next pass overwrites the staging regions
         } else if (wave_out) {
@@ -1026,6 +1046,20 @@ hipError_t launch_gemm_grouped_swiglu(const GemmArgs& g, int64_t I, uint8_t* hq,
     const int64_t items = ((int64_t)(g.M + C::BM - 1) / C::BM + g.G) * (I / 128);
     const dim3 grid((unsigned)std::min<int64_t>((items + 7) / 8 * 8, kCUs));
     hipLaunchKernelGGL((k_gemm<MODE_BLOCK128, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx_swiglu(const MxGemmArgs& g, int64_t I, uint8_t* hq, int64_t ld_hq, uint8_t* hs,
+                                 int64_t hs_sm, int64_t hs_sg, hipStream_t st) {
+    if (g.M == 0 || I == 0) return hipSuccess;
+    KArgs p = base_args(g.M, 2 * I, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, nullptr, 0);
+    p.sa_sm = g.lds_a; p.sa_sk = 1; p.b_sg = g.b_sg; p.sb_sg = g.sb_sg; p.sb_sn = g.lds_b; p.sb_sk = 1;
+    p.G = g.G; p.offsets = g.offsets; p.a_rows = g.a_rows;
+    p.swi = (int32_t)I; p.hq = hq; p.ld_hq = ld_hq; p.hs = hs; p.hs_sm = hs_sm; p.hs_sg = hs_sg;
+    using C = Cfg<8, 8>;
+    const int64_t items = ((int64_t)(g.M + C::BM - 1) / C::BM + g.G) * (I / 128);
+    const dim3 grid((unsigned)std::min<int64_t>((items + 7) / 8 * 8, kCUs));
+    hipLaunchKernelGGL((k_gemm<MODE_MX, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
     return hipGetLastError();
 }
 

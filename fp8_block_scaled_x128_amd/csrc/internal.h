@@ -67,6 +67,11 @@ struct MxGemmArgs {
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
 };
 hipError_t launch_gemm_mx(const MxGemmArgs& g, hipStream_t st);
+// Grouped MXFP8 gate/up GEMM (B = [G][2I][K]) whose epilogue forms h =
+// bf16(silu(gate) * up) and writes its 1x32 codes hq and UE8M0 scales
+// hs[m * hs_sm + (j / 32) * hs_sg].
+hipError_t launch_gemm_mx_swiglu(const MxGemmArgs& g, int64_t I, uint8_t* hq, int64_t ld_hq, uint8_t* hs,
+                                 int64_t hs_sm, int64_t hs_sg, hipStream_t st);
 
 // Block-wise GEMM with power-of-two UE8M0 scales: sa(m, kb) = sa[m * lds_a + kb],
 // sb(n / 128, kb) = sb[(n / 128) * lds_b + kb] (bytes).

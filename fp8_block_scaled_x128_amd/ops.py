@@ -25,7 +25,7 @@ OUT_BF16, OUT_FP32 = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
 EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_linear", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
-           "fp8_grouped_gemm", "fp8_grouped_gemm_swiglu_quant",
+           "fp8_grouped_gemm", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
            "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
            "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
@@ -65,6 +65,8 @@ def load():
                                  P, I64, INT, P],
             "fp8_grouped_gemm_swiglu_quant": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P,
                                               I64, I64, I64, P, I64, P, I64, I64, P],
+            "mxfp8_grouped_gemm_swiglu_quant": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64,
+                                                I64, P, I64, P, I64, I64, P],
             "fp8_silu_mul_quant": [P, I64, I64, I64, INT, P, I64, P, I64, I64, P, I64, P],
             "fp8_moe_combine": [P, I64, I64, I64, P, P, I64, I32, P, I64, INT, P],
             "mxfp8_quant": [P, I64, I64, I64, P, I64, P, I64, I64, P],
@@ -163,6 +165,16 @@ def fp8_grouped_gemm_swiglu_quant(total_rows, I, K, G, offsets, a_rows, a_count,
                                               sb_stride_n, sb_stride_k, _p(hq), ld_hq, _p(hs), hs_stride_row,
                                               hs_stride_group, _stream(stream))
     return _check("fp8_grouped_gemm_swiglu_quant", st, raise_on_error)
+
+
+def mxfp8_grouped_gemm_swiglu_quant(total_rows, I, K, G, offsets, a_rows, a_count, a, lda, sa, lds_a, b, ldb,
+                                    b_stride_g, sb, lds_b, sb_stride_g, hq, ld_hq, hs, hs_stride_row,
+                                    hs_stride_group, stream=None, raise_on_error=True):
+    st = load().mxfp8_grouped_gemm_swiglu_quant(total_rows, I, K, G, _p(offsets), _p(a_rows), a_count, _p(a), lda,
+                                                _p(sa), lds_a, _p(b), ldb, b_stride_g, _p(sb), lds_b, sb_stride_g,
+                                                _p(hq), ld_hq, _p(hs), hs_stride_row, hs_stride_group,
+                                                _stream(stream))
+    return _check("mxfp8_grouped_gemm_swiglu_quant", st, raise_on_error)
 
 
 def fp8_grouped_gemm(total_rows, N, K, G, offsets, a_rows, a_count, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb,

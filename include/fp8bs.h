@@ -277,6 +277,28 @@ fp8bs_status fp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int64_
                                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * mxfp8_grouped_gemm_swiglu_quant -- the MXFP8 counterpart: the grouped
+ * mxfp8_gemm gate/up product (G >= 1, N = 2 I, B = [G][2I][K] with rows
+ * [0, I) gate and [I, 2I) up, UE8M0 scales per row and 32-wide K block)
+ * rounded to bf16, h = bf16(silu(gate) * up), and h quantized in 1x32
+ * blocks with UE8M0 scales.  Codes and scales equal those of mxfp8_gemm (bf16
+ * out) followed by fp8_silu_mul_quant(mx = 1).
+ *
+ * a .. sb_stride_g : as mxfp8_gemm with G >= 1 and N = 2 I.
+ * hq : [total_rows][ld_hq] h codes.   hs(m, j/32) = hs[m * hs_stride_row +
+ *      (j / 32) * hs_stride_group] (UE8M0 bytes).
+ * Requirements: as mxfp8_gemm; I % 128 == 0; ld_hq >= I, ld_hq % 8 == 0,
+ * hq 8-byte aligned.
+ * ------------------------------------------------------------------------ */
+fp8bs_status mxfp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int64_t K, int32_t G,
+                                             const int32_t* offsets, const int32_t* a_rows, int64_t a_count,
+                                             const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t lds_a,
+                                             const uint8_t* b, int64_t ldb, int64_t b_stride_g, const uint8_t* sb,
+                                             int64_t lds_b, int64_t sb_stride_g, uint8_t* hq, int64_t ld_hq,
+                                             uint8_t* hs, int64_t hs_stride_row, int64_t hs_stride_group,
+                                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_silu_mul_quant -- the step between the MoE gate/up and down GEMMs:
  * h = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)) in fp32, then
  * quantization of h, 1x128 with FP32 scales (mx == 0) or 1x32 with UE8M0

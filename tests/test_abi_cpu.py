@@ -113,6 +113,16 @@ def test_host_validation_rejects_before_launch(lib):
     assert swi(256, 128, 256, hq=fake + 4) == 4   # h codes not 8-byte aligned
     assert swi(256, 128, 256, ldb=64) == 3        # ldb < K
     assert swi(0, 128, 256) == 0                  # no rows: a successful no-op
+    # its MXFP8 counterpart
+    mxs = lambda rows, I, K, G=2, lds=None, hs=fake: ops.mxfp8_grouped_gemm_swiglu_quant(
+        rows, I, K, G, fake, None, rows, fake, K, fake, K // 32 if lds is None else lds, fake, K, 2 * I * K, fake,
+        K // 32 if lds is None else lds, 2 * I * (K // 32), fake, I, hs, I // 32, 1, stream=0, raise_on_error=False)
+    assert mxs(256, 96, 256) == 2                 # I % 128
+    assert mxs(256, 128, 256, G=0) == 2           # G < 1
+    assert mxs(256, 128, 256, lds=4) == 3         # scale leading dimension < K/32
+    assert mxs(256, 128, 256, lds=10) == 4        # scale leading dimension % 4
+    assert mxs(256, 128, 256, hs=None) == 1       # NULL h scales
+    assert mxs(0, 128, 256) == 0
 
 
 def test_dense_tile_plan(lib):

@@ -231,6 +231,45 @@ def _fused_gate_up_matches(rows, G, offs, a_rows, a_count, qx, sx, qgu, sgu, qh,
     assert torch.equal(shf.view(torch.int32), shb.view(torch.int32)), "fused h scales differ"
 
 
+def _fused_mx_gate_up_matches(rows, G, offs, a_rows, a_count, qx, sx, qgu, sgu, qh, sh):
+    """The MXFP8 gate/up GEMM with SiLU*mul and the 1x32 quantization of h in
+    its epilogue: codes and UE8M0 scales byte-identical to the bf16 grouped
+    MXFP8 GEMM followed by fp8_silu_mul_quant(mx = 1), every row."""
+    E_, N2, K = qgu.shape
+    I = N2 // 2
+    _say("MXFP8 gate_up with SiLU*mul and 1x32 quantization in the epilogue: %d rows, G=%d" % (rows, G))
+    qhf = torch.full((rows, I), 0xAA, dtype=torch.uint8, device="cuda")
+    shf = torch.full((rows, I // 32), 0xAA, dtype=torch.uint8, device="cuda")
+    ops.mxfp8_grouped_gemm_swiglu_quant(rows, I, K, G, offs, a_rows, a_count, qx, K, sx, K // 32, qgu, K, N2 * K,
+                                        sgu, K // 32, N2 * (K // 32), qhf, I, shf, I // 32, 1)
+    torch.cuda.synchronize()
+    bad = torch.nonzero(qhf != qh)
+    assert bad.numel() == 0, "fused MX h codes differ at %s" % bad[:5].tolist()
+    assert torch.equal(shf, sh), "fused MX h scales differ"
+
+
+def test_mx_gate_up_swiglu_quant_small_moe():
+    """The MXFP8 fused gate/up epilogue on the scaled-down MoE layer with
+    empty experts and the dispatch gather."""
+    d = inputs.small_moe()
+    r = d["routing"]
+    rows, G = r.row_token.size, r.offsets.size - 1
+    E_, N2, K = d["w_gu"].shape
+    I = N2 // 2
+    qx, sx = ops.mx_quant(dev_bf16(d["x"]))
+    qgu, sgu = ops.mx_quant(dev_bf16(d["w_gu"]).view(E_ * N2, K))
+    offs, a_rows = dev(r.offsets), dev(r.row_token)
+    gu16 = torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
+    ops.mxfp8_gemm(rows, N2, K, G, offs, a_rows, qx.shape[0], qx, K, sx, K // 32, qgu, K, N2 * K, sgu, K // 32,
+                   N2 * (K // 32), gu16, N2, ops.OUT_BF16)
+    qh = torch.empty((rows, I), dtype=torch.uint8, device="cuda")
+    sh = torch.empty((rows, I // 32), dtype=torch.uint8, device="cuda")
+    ops.fp8_silu_mul_quant(gu16, rows, I, N2, 1, qh, I, sh, I // 32, 1, None, 0)
+    torch.cuda.synchronize()
+    _fused_mx_gate_up_matches(rows, G, offs, a_rows, qx.shape[0], qx, sx, qgu.view(E_, N2, K),
+                              sgu.view(E_, N2, K // 32), qh, sh)
+
+
 @pytest.mark.parametrize("gather", [True, False])
 def test_gate_up_swiglu_quant_small_moe(gather):
     """The fused gate/up epilogue on the scaled-down MoE layer with empty
@@ -320,6 +359,8 @@ def test_moe_mxfp8_chain_full_size(moe):
     ops.fp8_silu_mul_quant(gu16, rows, INTER, 2 * INTER, 1, qh, INTER, sh, INTER // 32, 1, h, INTER)
     torch.cuda.synchronize()
     _check_h(gu16, h, qh, sh, np.random.default_rng(53).integers(0, rows, 256), mx=True)
+    _fused_mx_gate_up_matches(rows, G, offs, a_rows, x.shape[0], qx, sx, qgu.view(E, 2 * INTER, HID),
+                              sgu.view(E, 2 * INTER, HID // 32), qh, sh)
     dn16 = mx_grouped(HID, INTER, None, rows, qh, sh, qdt, sdt, torch.bfloat16)
     dn32 = mx_grouped(HID, INTER, None, rows, qh, sh, qdt, sdt, torch.float32)
     torch.cuda.synchronize()
