@@ -50,6 +50,26 @@ constexpr int BK = 128;                         // K bytes per slice
 constexpr int kE8M0One = 127;                  // UE8M0 code of 1.0
 constexpr int kCUs = 256;                       // MI355X compute units
 
+// Lane-group maxima by DPP for code where every lane of the wave is active
+// (the fused SiLU*mul epilogue): each step is one VALU op reading another
+// lane's register, where a shuffle through ds_bpermute is an LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float max_dpp(float v) {
+    const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false);
+    return fmaxf(v, __int_as_float(o));
+}
+constexpr int kDppXor1 = 0xb1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowMirror = 0x140;    // lane i <- lane 15 - i of its 16-lane row
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7 - i of its 8-lane half row
+// Max over each aligned group of 4 lanes.
+__device__ __forceinline__ float quad_max_dpp(float v) { return max_dpp<kDppXor2>(max_dpp<kDppXor1>(v)); }
+// Max over each 16-lane row: quads, then the half-row mirror joins quads 0-1
+// and 2-3, then the row mirror joins the two halves.
+__device__ __forceinline__ float row16_max_dpp(float v) {
+    return max_dpp<kDppRowMirror>(max_dpp<kDppHalfMirror>(quad_max_dpp(v)));
+}
+
 // Tile configurations.  Every wave computes NF 16-row weight tiles (16 NF
 // weight rows) x 64 activation rows; waves are arranged 2 (n) x WAVES/2 (m),
 // so a tile is 32 NF weight rows x 32 WAVES activation rows.
@@ -829,7 +849,7 @@ k_gemm(KArgs p) {
                 if (MODE == MODE_MX) {
                     // four 1x32 blocks per row: 4 lanes each, UE8M0 scales
                     // (the rule of the MX quantizer)
-                    const float amax = group4_max(absmax8(v));
+                    const float amax = quad_max_dpp(absmax8(v));
                     const int e = mx_exponent(amax);
                     const float f = pow2_neg(e);
                     if (amax == 0.0f) {
@@ -842,7 +862,7 @@ k_gemm(KArgs p) {
                         static_cast<uint8_t*>(p.hs)[(int64_t)m * p.hs_sm + (int64_t)(en0 / 32 + (sub >> 2)) * p.hs_sg] =
                             (uint8_t)(e + 127);
                 } else {
-                    const float amax = group16_max(absmax8(v));
+                    const float amax = row16_max_dpp(absmax8(v));
                     const float sc = amax / kE4M3Max;
                     encode8(v, sc, w0, w1);
                     if (m < em_end && sub == 0)
