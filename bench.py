@@ -21,9 +21,8 @@ repetitions, each kernel bracketed by HIP events on the launch stream):
                      + 1x128 requantization, grouped down GEMM, combine
     moe_blockwise_fused  the same layer with SiLU*mul and the requantization
                      in the gate_up GEMM's epilogue
-    moe_mxfp8        the layer in MXFP8 (1x32 UE8M0 blocks); moe_mxfp8_fused
-                     with the fused gate_up epilogue
-    moe_mxfp8        the same layer with 1x32 UE8M0 scales (MXFP8)
+    moe_mxfp8        the layer in MXFP8 (1x32 UE8M0 blocks)
+    moe_mxfp8_fused  the MXFP8 layer with the fused gate_up epilogue
 
 Prints ONE JSON line: value = GEMM FLOPs of the headline step / step time
 (TFLOP/s); per-kernel times with TFLOP/s or GB/s against MI355X's peaks; a
