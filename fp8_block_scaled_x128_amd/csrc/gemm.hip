@@ -772,12 +772,15 @@ k_gemm(KArgs p) {
     // Grouped: it uses weight stage 2 (the next item's copies are already on
     // their way to the other buffers), 8 rows a pass.  Each wave then touches
     // only its own staging region, whose LDS accesses complete in program
-    // order.
+    // order.  SiLU*mul: 16 rows a pass, waves 0-3 in weight stage 2 and
+    // waves 4-7 in s_swi (fewer passes, so fewer barriers between staging
+    // and the cross-wave reads of gate and up).
     constexpr int EB = OUTF32 ? 4 : 2;                 // output bytes per element
-    constexpr int kRows = GROUPED ? 8 : 32;            // rows per pass
+    constexpr int kRows = SWIGLU ? 16 : GROUPED ? 8 : 32;   // rows per pass
     constexpr int kPitch = 16 * NF * EB + 16;          // staged row, bytes
     constexpr int kChunks = 16 * NF * EB / 16;         // 16-byte pieces per row
-    static_assert(GROUPED ? (C::kBStages == 3 && WAVES * kRows * kPitch <= C::kBStageBytes)
+    constexpr int kStageWaves = SWIGLU ? 4 : WAVES;    // waves per staging region
+    static_assert(GROUPED ? (C::kBStages == 3 && kStageWaves * kRows * kPitch <= C::kBStageBytes)
                           : WAVES * kRows * kPitch <= C::kLdsBytes,
                   "epilogue staging fits its region");
     static_assert((kRows * kChunks) % 64 == 0, "whole store instructions per pass");
@@ -786,7 +789,14 @@ k_gemm(KArgs p) {
         if (!wave_out) return;
     }
     const uint32_t ebase = GROUPED ? bstage(2) : lds0;
-    const uint32_t wst = ebase + (uint32_t)(wave * kRows * kPitch);
+    uint32_t ebase2 = ebase;
+    if constexpr (SWIGLU) {
+        // staging of waves 4-7 (wave rows 2 and 3); the other kernels do not
+        // allocate it
+        __shared__ __attribute__((aligned(16))) uint8_t s_swi[kStageWaves * kRows * kPitch];
+        ebase2 = lds_addr(s_swi);
+    }
+    const uint32_t wst = (SWIGLU && wave >= 4 ? ebase2 : ebase) + (uint32_t)((wave % kStageWaves) * kRows * kPitch);
     uint8_t* cbase = static_cast<uint8_t*>(p.c) + (int64_t)nw0 * EB;
     // SWIGLU tiles never leave the matrix (wave_out holds), so its barriers
     // are met by every wave
@@ -836,7 +846,9 @@ k_gemm(KArgs p) {
             for (int it = 0; it < kPerWave / 4; ++it) {
                 const int R = wave * kPerWave + it * 4 + (lane >> 4);    // row of the pass, 0 .. 4 kRows - 1
                 const int wr = R / kRows, rr = R % kRows;
-                const uint32_t ga = ebase + (uint32_t)(2 * wr * kRows * kPitch + rr * kPitch + sub * 16);
+                // waves 2 wr and 2 wr + 1 share a staging region
+                const uint32_t ga = (wr < 2 ? ebase : ebase2) +
+                                    (uint32_t)(2 * (wr & 1) * kRows * kPitch + rr * kPitch + sub * 16);
                 const u32x4 gv = lds_read16(ga);
                 const u32x4 uv = lds_read16(ga + kRows * kPitch);
                 float g[8], u[8], v[8];
