@@ -770,16 +770,18 @@ k_gemm(KArgs p) {
     // and reads it back in 16-byte pieces of consecutive columns.  Dense: the
     // staging uses the operand buffers, freed by a barrier, 32 rows a pass.
     // Grouped: it uses weight stage 2 (the next item's copies are already on
-    // their way to the other buffers), 8 rows a pass.  Each wave then touches
-    // only its own staging region, whose LDS accesses complete in program
-    // order.  SiLU*mul: 16 rows a pass, waves 0-3 in weight stage 2 and
-    // waves 4-7 in s_swi (fewer passes, so fewer barriers between staging
-    // and the cross-wave reads of gate and up).
+    // their way to the other buffers).  With bf16 output, 16 rows a pass:
+    // waves 0-3 in weight stage 2 and waves 4-7 in a second region of the
+    // same size (fewer passes, and for SiLU*mul fewer barriers between the
+    // staging and the cross-wave reads of gate and up); with fp32 output,
+    // 8 rows a pass in weight stage 2.  Each wave then touches only its own
+    // staging region, whose LDS accesses complete in program order.
     constexpr int EB = OUTF32 ? 4 : 2;                 // output bytes per element
-    constexpr int kRows = SWIGLU ? 16 : GROUPED ? 8 : 32;   // rows per pass
+    constexpr bool kTwoRegions = GROUPED && !OUTF32 && WAVES == 8;  // 16 rows a pass in two regions
+    constexpr int kRows = kTwoRegions ? 16 : GROUPED ? 8 : 32;   // rows per pass
     constexpr int kPitch = 16 * NF * EB + 16;          // staged row, bytes
     constexpr int kChunks = 16 * NF * EB / 16;         // 16-byte pieces per row
-    constexpr int kStageWaves = SWIGLU ? 4 : WAVES;    // waves per staging region
+    constexpr int kStageWaves = kTwoRegions ? 4 : WAVES;    // waves per staging region
     static_assert(GROUPED ? (C::kBStages == 3 && kStageWaves * kRows * kPitch <= C::kBStageBytes)
                           : WAVES * kRows * kPitch <= C::kLdsBytes,
                   "epilogue staging fits its region");
@@ -790,13 +792,13 @@ k_gemm(KArgs p) {
     }
     const uint32_t ebase = GROUPED ? bstage(2) : lds0;
     uint32_t ebase2 = ebase;
-    if constexpr (SWIGLU) {
+    if constexpr (kTwoRegions) {
         // staging of waves 4-7 (wave rows 2 and 3); the other kernels do not
         // allocate it
-        __shared__ __attribute__((aligned(16))) uint8_t s_swi[kStageWaves * kRows * kPitch];
-        ebase2 = lds_addr(s_swi);
+        __shared__ __attribute__((aligned(16))) uint8_t s_stage2[kStageWaves * kRows * kPitch];
+        ebase2 = lds_addr(s_stage2);
     }
-    const uint32_t wst = (SWIGLU && wave >= 4 ? ebase2 : ebase) + (uint32_t)((wave % kStageWaves) * kRows * kPitch);
+    const uint32_t wst = (kTwoRegions && wave >= 4 ? ebase2 : ebase) + (uint32_t)((wave % kStageWaves) * kRows * kPitch);
     uint8_t* cbase = static_cast<uint8_t*>(p.c) + (int64_t)nw0 * EB;
     // SWIGLU tiles never leave the matrix (wave_out holds), so its barriers
     // are met by every wave
