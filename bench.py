@@ -59,12 +59,18 @@ def parse():
     # (GEMM time falls by 10-20% over the first ~10 ms): 200 untimed steps
     # (about 70 ms) come first
     ap.add_argument("--warmup", type=int, default=200)
+    # before the counted warm-up steps, step passes run for at least this long
+    # so that a short --warmup still times the settled clock
+    ap.add_argument("--settle-ms", type=float, default=300.0)
+    ap.add_argument("--batch", type=int, default=10,
+                    help="back-to-back launches per event pair in the per-kernel pass")
     ap.add_argument("--copies", type=int, default=4, help="activation copies rotated across steps")
     ap.add_argument("--reps", type=int, default=10, help="repetitions per kernel of the other workloads")
     ap.add_argument("--workloads", default=",".join(WORKLOADS),
                     help="other workloads to time after the headline step (comma list, or 'none')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=288, help="token rows in the CPU-oracle sample")
+    ap.add_argument("--cpu-rows-1t", type=int, default=24, help="token rows in the one-thread CPU-oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB 3 times (counter calibration)")
     return ap.parse_args()
@@ -120,6 +126,62 @@ def time_sequence(torch, stream, launches, reps, warmup, warm_ms=60.0):
         ev[i][len(launches)].record(stream)
     torch.cuda.synchronize()
     return [float(np.median([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(reps)])) for k in range(len(launches))]
+
+
+class ClockSampler:
+    """Samples the GPU shader clock (the current DPM level of the sclk table
+    in sysfs, MHz) from a host thread while the GPU runs.  A sample is the
+    clock the power manager set; under a matrix-heavy load it drops below the
+    2.4 GHz the peak figures assume.  source is None where no readable sysfs
+    clock exists (then sclk_mhz_timed_region is null)."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.mark_at = 0
+        self.source = None
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            if self._read(f) is not None:
+                self.source = f
+                break
+        self._stop = threading.Event()
+        self._thr = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split()[0].lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read(self.source)
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.source:
+            self._thr.start()
+
+    def mark(self):
+        self.mark_at = len(self.samples)
+
+    def since_mark(self):
+        s = self.samples[self.mark_at:]
+        return round(float(np.median(s)), 1) if s else None
+
+    def stop(self):
+        self._stop.set()
+        if self._thr.is_alive():
+            self._thr.join()
 
 
 # ------------------------------------------------------------- workloads
@@ -383,12 +445,9 @@ def wl_moe_mxfp8(torch, ops, inputs, to_dev, R, fused=False):
 
 
 # ---------------------------------------------------------- CPU baseline
-def cpu_baseline(d, rows):
-    """Time the CPU oracle on a bounded sample of the headline step: the first
-    `rows` tokens of both activations (1x128), both full weights (128x128) and
-    both GEMMs for those tokens.  Reported in the metric's unit (TFLOP/s of
-    GEMM work per second of oracle time)."""
-    import oracle
+def _oracle_step_sample(oracle, d, rows):
+    """The oracle on the first `rows` tokens of the headline step; returns
+    (seconds, GEMM flops)."""
     t0 = time.perf_counter()
     qa, sa = oracle.quant_1x128(d["x_up"][:rows])
     qw, sw = oracle.quant_128x128(d["w_up"])
@@ -400,12 +459,40 @@ def cpu_baseline(d, rows):
     mi2 = np.repeat(np.arange(rows), HID)
     ni2 = np.tile(np.arange(HID), rows)
     oracle.gemm_blockscaled_sampled(qa2, sa2, qw2, sw2, mi2, ni2)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * INTER * HID * 2
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "first %d of 4096 tokens: 1x128 quantization of both activations, 128x128 quantization "
-                      "of both full weights, fp64 reference GEMMs up and down for those tokens (%.1f s)"
-                      % (rows, dt)}
+    return time.perf_counter() - t0, 2.0 * rows * INTER * HID * 2
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(d, rows, rows_1t):
+    """Time the CPU oracle on a bounded sample of the headline step: the first
+    `rows` tokens of both activations (1x128), both full weights (128x128) and
+    both GEMMs for those tokens, on every host thread; then the first
+    `rows_1t` tokens on one thread.  Reported in the metric's unit (TFLOP/s of
+    GEMM work per second of oracle time)."""
+    import oracle
+    threads = os.cpu_count() or 1
+    oracle.set_num_threads(threads)
+    dt, flops = _oracle_step_sample(oracle, d, rows)
+    used = oracle.num_threads()
+    oracle.set_num_threads(1)
+    dt1, flops1 = _oracle_step_sample(oracle, d, rows_1t)
+    oracle.set_num_threads(threads)
+    sample = ("first %d of 4096 tokens: 1x128 quantization of both activations, 128x128 quantization of both "
+              "full weights, fp64 reference GEMMs up and down for those tokens")
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": sample % rows + " (%.1f s)" % dt, "cpu_model": cpu_model(), "nproc": threads,
+            "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": sample % rows_1t + " (%.1f s)" % dt1}}
 
 
 def traffic_record():
@@ -483,41 +570,76 @@ def main():
     # quantization was measured slower (0.305 ms per step): the concurrent
     # quantizers share HBM and the cross-stream waits add latency.
     main_h = stream.cuda_stream
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
-          for _ in range(args.steps)]
 
-    def step(i, events=None):
+    def step(i, only=None, events=None):
+        """One step; with `only` = k, events bracket launch k alone."""
         r = i % R
         for k in range(len(names)):
-            if events is not None:
-                events[k][0].record(stream)
+            if k == only:
+                events[0].record(stream)
             launches[k](r, main_h)
-            if events is not None:
-                events[k][1].record(stream)
+            if k == only:
+                events[1].record(stream)
 
+    clock = ClockSampler()
+    clock.start()
+    # the shader clock settles over tens of milliseconds of sustained load:
+    # step passes for at least --settle-ms, then the counted warm-up steps
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        step(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    clock.mark()
     t_start.record(stream)
     for i in range(args.steps):
         step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
+    clock_mhz = clock.since_mark()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    # per-kernel times: the same schedule again, each launch bracketed by events
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-
+    # Per-kernel times in the step's schedule: one kernel per pass has events
+    # around it (events around every launch paced the GPU).  They include the
+    # launch gap before the kernel, 1-3 us.
     kernels = {}
     for k, n in enumerate(names):
-        ms = float(np.mean([ev[i][k][0].elapsed_time(ev[i][k][1]) for i in range(args.steps)]))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(i, k, evs[i])
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
         kernels[n] = kernel_entry(*work[n], ms)
+    # The GEMMs for the roofline: events around a batch of back-to-back
+    # launches of the same GEMM on the launch stream (its operands are the
+    # codes the step's quantizers wrote, still in the last-level cache as in
+    # the step), median over batches: the kernel's average launch duration
+    # without the event overhead of a single launch.
+    gemm_b2b = {}
+    for k, n in enumerate(names):
+        if not n.startswith("gemm"):
+            continue
+        per = []
+        for rep in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for j in range(args.batch):
+                launches[k](0, main_h)
+            b.record(stream)
+            torch.cuda.synchronize()
+            per.append(a.elapsed_time(b) / args.batch)
+        gemm_b2b[n] = float(np.median(per))
+        kernels[n]["ms_back_to_back"] = round(gemm_b2b[n], 5)
+    clock.stop()
 
-    gemm_ms = (kernels["gemm_up"]["ms"] + kernels["gemm_down"]["ms"]) / 2
+    gemm_ms = (gemm_b2b["gemm_up"] + gemm_b2b["gemm_down"]) / 2
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     value = 2 * gemm_flops / (ms_step * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(dev)
@@ -542,7 +664,11 @@ def main():
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": (round(trec["hbm_bytes_per_launch"]) if trec else None),
                      "kernel": "k_gemm, block-scaled FP8 GEMM (gemm_up and gemm_down of the step)",
-                     "per_launch": "2*M*N*K = %.4g FLOP" % gemm_flops},
+                     "per_launch": "2*M*N*K = %.4g FLOP" % gemm_flops,
+                     "timing": "HIP events around %d back-to-back launches on the launch stream, median of 5, "
+                               "mean of gemm_up and gemm_down" % args.batch},
+        "clock": {"sclk_mhz_timed_region": clock_mhz, "source": clock.source,
+                  "settle_ms": args.settle_ms},
         "kernels": kernels,
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
@@ -584,7 +710,7 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(d, args.cpu_rows)
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_rows, args.cpu_rows_1t)
     print(json.dumps(res), flush=True)
 
 

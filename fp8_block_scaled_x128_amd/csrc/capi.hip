@@ -290,6 +290,15 @@ fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t 
     return launched(launch_gemm_grouped(g, stream), "fp8_grouped_gemm");
 }
 
+fp8bs_status fp8_grouped_gemm_ws_size(int64_t max_total_rows, int32_t G, int64_t N, size_t* bytes) {
+    if (!bytes) return fail(FP8BS_ERR_NULL, "bytes is required");
+    if (max_total_rows < 0 || G < 1 || N < 0)
+        return fail(FP8BS_ERR_SHAPE, "max_total_rows=%lld G=%d N=%lld", (long long)max_total_rows, (int)G,
+                    (long long)N);
+    *bytes = 0;     // the work-item lookup reads the device offsets; no table in memory
+    return ok();
+}
+
 fp8bs_status fp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int64_t K, int32_t G, const int32_t* offsets,
                                            const int32_t* a_rows, int64_t a_count, const uint8_t* a, int64_t lda,
                                            const float* sa, int64_t sa_stride_m, int64_t sa_stride_k,

@@ -25,7 +25,7 @@ OUT_BF16, OUT_FP32 = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
 EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_linear", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
-           "fp8_grouped_gemm", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
+           "fp8_grouped_gemm", "fp8_grouped_gemm_ws_size", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
            "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
            "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
@@ -63,6 +63,7 @@ def load():
             "fp8_blockscaled_gemm_plan": [I64, I64, I64, P],
             "fp8_grouped_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64,
                                  P, I64, INT, P],
+            "fp8_grouped_gemm_ws_size": [I64, I32, I64, P],
             "fp8_grouped_gemm_swiglu_quant": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P,
                                               I64, I64, I64, P, I64, P, I64, I64, P],
             "mxfp8_grouped_gemm_swiglu_quant": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64,
@@ -155,6 +156,15 @@ def fp8_blockscaled_gemm_plan(M, N, K):
     out = (ctypes.c_int32 * 5)()
     _check("fp8_blockscaled_gemm_plan", load().fp8_blockscaled_gemm_plan(M, N, K, ctypes.cast(out, ctypes.c_void_p)))
     return (out[0], out[1]), ((out[2], out[3]) if out[2] else None), out[4]
+
+
+def fp8_grouped_gemm_ws_size(max_total_rows, G, N, raise_on_error=True):
+    """Workspace bytes of the grouped GEMMs (host only); always 0."""
+    out = ctypes.c_size_t(0)
+    st = load().fp8_grouped_gemm_ws_size(max_total_rows, G, N, ctypes.byref(out))
+    if _check("fp8_grouped_gemm_ws_size", st, raise_on_error) != 0:
+        return None
+    return out.value
 
 
 def fp8_grouped_gemm_swiglu_quant(total_rows, I, K, G, offsets, a_rows, a_count, a, lda, sa, sa_stride_m, sa_stride_k,

@@ -179,8 +179,11 @@ fp8bs_status fp8_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int
  * a  : [M][lda] E4M3 codes, K contiguous.      sa(m, kb) = sa[m * sa_stride_m + kb * sa_stride_k]
  * b  : [N][ldb] E4M3 codes, K contiguous.      sb(n, kb) = sb[r * sb_stride_n + kb * sb_stride_k]
  *      with r = n / 128 (FP8BS_BSCALE_BLOCK128) or r = n (FP8BS_BSCALE_ROW128).
+ *      B is always [N][K] with K contiguous; there is no [K][N] layout flag.
  *      The data-gradient GEMM dX = dY W reads W through the transposed copy
- *      q_t of fp8_quant_block2d and W's scales with the two strides swapped.
+ *      q_t of fp8_quant_block2d (the same codes, written once per weight
+ *      quantization: 1 more byte per weight element) and W's 128x128 scales
+ *      with the two strides swapped (the blocks are transpose-invariant).
  * c  : [M][ldc] bf16 (round to nearest even) or fp32, per `out`.
  * Scales constant along K (sa_stride_k == 0 and sb_stride_k == 0: the
  * rowwise and tensorwise scalings of fp8_quant_rowwise/_tensorwise, or any
@@ -235,6 +238,8 @@ fp8bs_status fp8_blockscaled_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t*
  * sb      : 128x128 block scales; expert g, block (n/128, kb) at
  *           sb[g * sb_stride_g + (n/128) * sb_stride_n + kb * sb_stride_k].
  * c       : [total_rows][ldc], bf16 or fp32.
+ * The schedule needs no workspace: every workgroup derives its work items
+ * from the device offsets (see fp8_grouped_gemm_ws_size).
  * Requirements: as fp8_blockscaled_gemm; G >= 1; b_stride_g % 16 == 0.
  * ------------------------------------------------------------------------ */
 fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t G,
@@ -244,6 +249,21 @@ fp8bs_status fp8_grouped_gemm(int64_t total_rows, int64_t N, int64_t K, int32_t 
                               const uint8_t* b, int64_t ldb, int64_t b_stride_g,
                               const float* sb, int64_t sb_stride_g, int64_t sb_stride_n, int64_t sb_stride_k,
                               void* c, int64_t ldc, fp8bs_out out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_grouped_gemm_ws_size -- device workspace, in bytes, that the grouped
+ * GEMMs (fp8_grouped_gemm, fp8_grouped_gemm_swiglu_quant, grouped
+ * mxfp8_gemm and mxfp8_grouped_gemm_swiglu_quant) need for a problem of at
+ * most max_total_rows rows over G groups with N output columns.  Always 0:
+ * the persistent workgroups find each work item's group with a prefix scan
+ * of the per-group tile counts, read from the device offsets, so the
+ * scheduler keeps no table in memory and the calls take no workspace
+ * argument.  Kept so that a caller can size (and skip) a workspace from the
+ * problem statement alone.  Host only; launches nothing.
+ * bytes : written on FP8BS_OK.
+ * Requirements: max_total_rows >= 0, G >= 1, N >= 0; bytes not NULL.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_grouped_gemm_ws_size(int64_t max_total_rows, int32_t G, int64_t N, size_t* bytes);
 
 /* ------------------------------------------------------------------------
  * fp8_grouped_gemm_swiglu_quant -- the MoE expert gate/up GEMM
@@ -303,6 +323,13 @@ fp8bs_status mxfp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int6
  * h = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)) in fp32, then
  * quantization of h, 1x128 with FP32 scales (mx == 0) or 1x32 with UE8M0
  * scales (mx == 1, see mxfp8_quant).
+ * The pages do not describe this step.  It is the plainest reading of the
+ * expert MLP of the Qwen3-30B-A3B MoE layer that "Low Precision RL" runs in
+ * block-wise FP8 and MXFP8 (table "Choose a precision"): the gate/up GEMM's
+ * output, rounded to bf16, feeds SiLU*mul, and h is the activation operand of
+ * the down GEMM, so it is quantized with the activation grouping of the
+ * recipe (1x128, section "2. Unified block-wise FP8 (DeepSeek-style)"; 1x32,
+ * section "3. Unified MXFP8 (Blackwell)").
  *
  * gate_up : bf16 [rows][ld_in]; columns [0, I) hold the gate projection and
  *           columns [I, 2I) the up projection.

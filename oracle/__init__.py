@@ -33,10 +33,14 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp8_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libfp8_oracle.so")
-
 GCC_FLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
              "-Wall", "-shared", "-fPIC"]
+# FP8_ORACLE_SANITIZE=1 selects a second build of the same source with
+# AddressSanitizer and UndefinedBehaviorSanitizer (host code only; the
+# process must preload the ASan runtime, see tests/test_oracle_sanitized.py).
+SANITIZE = os.environ.get("FP8_ORACLE_SANITIZE", "") == "1"
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+_LIB_PATH = os.path.join(_HERE, "libfp8_oracle_san.so" if SANITIZE else "libfp8_oracle.so")
 
 _lock = threading.Lock()
 _lib = None
@@ -47,7 +51,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH) or \
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", *GCC_FLAGS, *(SANITIZE_FLAGS if SANITIZE else []), _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -92,6 +96,8 @@ def _load():
         lib.or_moe_combine.restype = None
         lib.or_num_threads.argtypes = []
         lib.or_num_threads.restype = ctypes.c_int
+        lib.or_set_num_threads.argtypes = [ctypes.c_int]
+        lib.or_set_num_threads.restype = None
         _lib = lib
         return lib
 
@@ -110,6 +116,11 @@ def _bf16_view(x) -> np.ndarray:
 
 def num_threads() -> int:
     return _load().or_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (results are independent of it)."""
+    _load().or_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- codecs

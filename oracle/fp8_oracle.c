@@ -508,3 +508,15 @@ OR_EXPORT int or_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set the number of OpenMP threads of the parallel loops above (timing of
+ * the oracle at one thread and at every core; the results do not depend on
+ * it: every loop only splits independent rows or groups). */
+OR_EXPORT void or_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -26,12 +26,38 @@ def lib():
     return ops.load()
 
 
+# The boundary the problem statement fixes: the quantizers (S = max|X| / 448,
+# Q = round(x / S): "Unified FP8: Beyond Mixed Precision...", section "FP8
+# Quantization"), the block-scaled, grouped and MXFP8 GEMMs and the SiLU*mul
+# step between the MoE GEMMs, the grouped GEMM's workspace query and the two
+# status helpers.
+BOUNDARY = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_blockscaled_gemm", "fp8_grouped_gemm",
+            "fp8_grouped_gemm_ws_size", "fp8_silu_mul_quant", "mxfp8_quant", "mxfp8_gemm",
+            "fp8bs_status_string", "fp8bs_last_error_detail"]
+BOUNDARY_ENUMS = ["fp8bs_status", "fp8bs_axis", "fp8bs_out", "fp8bs_bscale"]
+
+
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_blockscaled_gemm", "fp8_grouped_gemm",
-              "fp8_silu_mul_quant", "mxfp8_quant", "mxfp8_gemm", "fp8bs_e4m3_encode",
-              "fp8bs_status_string", "fp8bs_last_error_detail"]:
+    for n in BOUNDARY + ["fp8bs_e4m3_encode"]:
         assert n in names, n
+    text = open(HEADER).read()
+    for e in BOUNDARY_ENUMS:
+        assert re.search(r"}\s*%s\s*;" % e, text), e
+
+
+def test_boundary_exported(lib):
+    for n in BOUNDARY:
+        assert hasattr(lib, n), "missing export %s" % n
+
+
+def test_grouped_gemm_needs_no_workspace(lib):
+    from fp8_block_scaled_x128_amd import ops
+    assert ops.fp8_grouped_gemm_ws_size(131072, 128, 2048) == 0
+    assert ops.fp8_grouped_gemm_ws_size(0, 1, 0) == 0
+    assert ops.fp8_grouped_gemm_ws_size(-1, 128, 2048, raise_on_error=False) is None
+    assert ops.fp8_grouped_gemm_ws_size(16, 0, 128, raise_on_error=False) is None
+    assert lib.fp8_grouped_gemm_ws_size(16, 4, 128, None) == 1      # FP8BS_ERR_NULL
 
 
 def test_library_exports_every_declared_symbol(lib):

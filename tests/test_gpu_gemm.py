@@ -53,7 +53,7 @@ def test_tiny_linear_forward():
     d = inputs.tiny_linear(0)
     qa, sa, qb, sb = _linear_operands(d["x"], d["w"])
     y16, y32 = _run_both(qa, sa, qb, sb)
-    verify(host(qa), host(sa), host(qb), host(sb), y32, y16)
+    verify(host(qa), host(sa), host(qb), host(sb), y32, y16, record="tiny_linear")
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 384, 1024), (1, 128, 128), (513, 640, 384), (64, 256, 2048)])
@@ -199,7 +199,7 @@ def test_qwen3_4b_mlp_full_size_sampled(part):
     y16, y32 = _run_both(qa, sa, qb, sb)
     M, N = y32.shape
     mi, ni = sample_indices(M, N, 3000, 7)
-    verify(host(qa), host(sa), host(qb), host(sb), y32, y16, mi=mi, ni=ni)
+    verify(host(qa), host(sa), host(qb), host(sb), y32, y16, mi=mi, ni=ni, record="qwen3_4b_mlp_" + part)
 
 
 def test_qwen3_4b_backward_full_size_sampled():
@@ -216,7 +216,7 @@ def test_qwen3_4b_backward_full_size_sampled():
     _say("dgrad", tuple(dx.shape))
     mi, ni = sample_indices(dx.shape[0], dx.shape[1], 3000, 21)
     verify(host(qdy), host(sdy), np.ascontiguousarray(host(qw).T), np.ascontiguousarray(host(sw).T), host(dx),
-           mi=mi, ni=ni)
+           mi=mi, ni=ni, record="qwen3_4b_dgrad")
     del dx
     qa, sa = ops.quant_rowblock(dev_bf16(dy), ops.AXIS_COL, "m_major")
     qb, sb = ops.quant_rowblock(dev_bf16(x), ops.AXIS_COL, "m_major")
@@ -224,7 +224,7 @@ def test_qwen3_4b_backward_full_size_sampled():
     torch.cuda.synchronize()
     _say("wgrad", tuple(dw.shape))
     mi, ni = sample_indices(dw.shape[0], dw.shape[1], 3000, 22)
-    verify(host(qa), host(sa), host(qb), host(sb), host(dw), bscale_row=True, mi=mi, ni=ni)
+    verify(host(qa), host(sa), host(qb), host(sb), host(dw), bscale_row=True, mi=mi, ni=ni, record="qwen3_4b_wgrad")
 
 
 # ---------------------------------------------------------------- grouped
@@ -344,16 +344,38 @@ def test_grouped_exact_integer_case_256x256_tiles():
     qa, sa, _, _ = _exact_case(rows, 128, K, 11)
     qbs, sbs = zip(*[_exact_case(128, N, K, 200 + g)[2:] for g in range(G)])
     qb, sb = np.stack(qbs), np.stack(sbs)
-    c = torch.full((rows, N), float("nan"), dtype=torch.float32, device="cuda")
-    dsa, dqb, dsb = dev(sa), dev(qb), dev(sb)
-    ops.fp8_grouped_gemm(rows, N, K, G, dev(offsets), None, rows, dev(qa), K, dsa, dsa.stride(0), dsa.stride(1),
-                         dqb, K, N * K, dsb, dsb.stride(0), dsb.stride(1), dsb.stride(2), c, N, ops.OUT_FP32)
-    torch.cuda.synchronize()
-    ch = host(c)
+    dqa, dsa, dqb, dsb, doffs = dev(qa), dev(sa), dev(qb), dev(sb), dev(offsets)
+
+    def run(out):
+        dt = torch.float32 if out == ops.OUT_FP32 else torch.bfloat16
+        c = torch.full((rows, N), float("nan"), dtype=dt, device="cuda")
+        ops.fp8_grouped_gemm(rows, N, K, G, doffs, None, rows, dqa, K, dsa, dsa.stride(0), dsa.stride(1),
+                             dqb, K, N * K, dsb, dsb.stride(0), dsb.stride(1), dsb.stride(2), c, N, out)
+        return c
+
+    ch, ch16 = _twice_bitwise(run)
     for g, (mi, ni) in _group_samples(offsets, N, 12).items():
         r0, r1 = int(offsets[g]), int(offsets[g + 1])
         yref, _ = oracle.gemm_blockscaled_sampled(qa[r0:r1], sa[r0:r1], qb[g], sb[g], mi, ni)
         assert np.array_equal(ch[r0:r1][mi, ni].astype(np.float64), yref), "group %d" % g
+    # bf16 output (staged through the two-region epilogue) equals the RNE
+    # rounding of the exact fp32 output (single-region staging), everywhere
+    assert np.array_equal(ch16, oracle.f64_to_bf16(ch.astype(np.float64)))
+
+
+def _twice_bitwise(run):
+    """Run a GEMM launcher twice per output type on the same inputs; the two
+    results must be identical bytes (an LDS-pipeline race shows up as a
+    difference).  Returns the host fp32 and bf16 results."""
+    res = []
+    for out in (ops.OUT_FP32, ops.OUT_BF16):
+        c1 = run(out)
+        c2 = run(out)
+        torch.cuda.synchronize()
+        h1, h2 = host(c1), host(c2)
+        assert h1.tobytes() == h2.tobytes(), "second launch differs (%s)" % out
+        res.append(h1)
+    return res
 
 
 def test_mx_grouped_exact_integer_case_256x256_tiles():
@@ -366,15 +388,21 @@ def test_mx_grouped_exact_integer_case_256x256_tiles():
     ea = rng.integers(126, 129, size=(rows, K // 32)).astype(np.uint8)
     qb = oracle.e4m3_encode(rng.integers(-8, 9, size=(G, N, K)).astype(np.float32))
     eb = rng.integers(126, 129, size=(G, N, K // 32)).astype(np.uint8)
-    c = torch.full((rows, N), float("nan"), dtype=torch.float32, device="cuda")
-    ops.mxfp8_gemm(rows, N, K, G, dev(offsets), None, rows, dev(qa), K, dev(ea), K // 32, dev(qb), K, N * K,
-                   dev(eb), K // 32, N * (K // 32), c, N, ops.OUT_FP32)
-    torch.cuda.synchronize()
-    ch = host(c)
+    dqa, dea, dqb, deb, doffs = dev(qa), dev(ea), dev(qb), dev(eb), dev(offsets)
+
+    def run(out):
+        dt = torch.float32 if out == ops.OUT_FP32 else torch.bfloat16
+        c = torch.full((rows, N), float("nan"), dtype=dt, device="cuda")
+        ops.mxfp8_gemm(rows, N, K, G, doffs, None, rows, dqa, K, dea, K // 32, dqb, K, N * K,
+                       deb, K // 32, N * (K // 32), c, N, out)
+        return c
+
+    ch, ch16 = _twice_bitwise(run)
     for g, (mi, ni) in _group_samples(offsets, N, 14).items():
         r0, r1 = int(offsets[g]), int(offsets[g + 1])
         yref, _ = oracle.gemm_mx_sampled(qa[r0:r1], ea[r0:r1], qb[g], eb[g], mi, ni)
         assert np.array_equal(ch[r0:r1][mi, ni].astype(np.float64), yref), "group %d" % g
+    assert np.array_equal(ch16, oracle.f64_to_bf16(ch.astype(np.float64)))
 
 
 # ---------------------------------------------------------------------- MX
@@ -457,7 +485,7 @@ def test_mx_backward_full_size_sampled():
     assert np.array_equal(host(qwt)[rows], qr) and np.array_equal(host(swt)[rows], sr)
     _say("mx dgrad", tuple(dx.shape))
     mi, ni = sample_indices(dx.shape[0], dx.shape[1], 3000, 24)
-    verify(host(qdy), host(sdy), host(qwt), host(swt), host(dx), mi=mi, ni=ni, mx=True)
+    verify(host(qdy), host(sdy), host(qwt), host(swt), host(dx), mi=mi, ni=ni, mx=True, record="qwen3_4b_mx_dgrad")
     del dx
     qa, sa = ops.mx_quant_t(dev_bf16(dy))
     qb, sb = ops.mx_quant_t(dev_bf16(x))
@@ -468,7 +496,7 @@ def test_mx_backward_full_size_sampled():
     assert np.array_equal(host(qa)[rows], qr) and np.array_equal(host(sa)[rows], sr)
     _say("mx wgrad", tuple(dw.shape))
     mi, ni = sample_indices(dw.shape[0], dw.shape[1], 3000, 26)
-    verify(host(qa), host(sa), host(qb), host(sb), host(dw), mi=mi, ni=ni, mx=True)
+    verify(host(qa), host(sa), host(qb), host(sb), host(dw), mi=mi, ni=ni, mx=True, record="qwen3_4b_mx_wgrad")
 
 
 def test_mx_quant_t_rejects_bad_shapes():

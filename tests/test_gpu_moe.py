@@ -66,7 +66,7 @@ def _sample_rc(n_rows, n_cols, rng):
     return rows, cols, mi, ni
 
 
-def _check_grouped(offsets, groups, seed, c16, c32, operands, mx=False):
+def _check_grouped(offsets, groups, seed, c16, c32, operands, mx=False, record=None):
     """Verify sampled outputs of the grouped GEMM.  operands(g, r0, r1) gives
     the host (qa, sa, qb, sb) of group g's rows [r0, r1)."""
     rng = np.random.default_rng(seed)
@@ -80,7 +80,8 @@ def _check_grouped(offsets, groups, seed, c16, c32, operands, mx=False):
         y32[rows] = host(c32[r0 + torch.from_numpy(rows).cuda()])
         y16[rows] = host(c16[r0 + torch.from_numpy(rows).cuda()])
         _say("group %d: %d rows" % (g, r1 - r0))
-        verify(qa, sa, qb, sb, y32, y16, mi=mi, ni=ni, mx=mx)
+        verify(qa, sa, qb, sb, y32, y16, mi=mi, ni=ni, mx=mx,
+               record=None if record is None else "%s_group%d" % (record, g))
 
 
 def _check_rows_quant_1x128(x_bits, q, s, rows):
@@ -162,7 +163,7 @@ def _blockwise_weights(d):
     return qgu, sgu, qdt, sd.transpose(1, 2)
 
 
-def _blockwise_chain(d, routing, seed, check_down=True, weights=None):
+def _blockwise_chain(d, routing, seed, check_down=True, weights=None, name=None):
     r = routing
     rows, G = r.row_token.size, r.offsets.size - 1
     offs = dev(r.offsets)
@@ -179,7 +180,8 @@ def _blockwise_chain(d, routing, seed, check_down=True, weights=None):
     groups = _sample_groups(r.offsets, seed)
     qx_h, sx_h = host(qx), host(sx)
     _check_grouped(r.offsets, groups, seed + 1, gu16, gu32,
-                   lambda g, r0, r1: (qx_h[r.row_token[r0:r1]], sx_h[r.row_token[r0:r1]], host(qgu[g]), host(sgu[g])))
+                   lambda g, r0, r1: (qx_h[r.row_token[r0:r1]], sx_h[r.row_token[r0:r1]], host(qgu[g]), host(sgu[g])),
+                   record=name and name + "_gate_up")
     del gu32
     if not check_down:
         return
@@ -197,7 +199,8 @@ def _blockwise_chain(d, routing, seed, check_down=True, weights=None):
     torch.cuda.synchronize()
     qh_h, sh_h = host(qh), host(sh)
     _check_grouped(r.offsets, groups, seed + 3, dn16, dn32,
-                   lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g]), host(sdt[g])))
+                   lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g]), host(sdt[g])),
+                   record=name and name + "_down")
     del dn32
     _say("combine")
     T = r.token_rows.shape[0]
@@ -303,7 +306,7 @@ def blockwise_weights(moe):
 def test_moe_blockwise_chain_full_size(moe, blockwise_weights):
     r = moe["routing"]
     assert r.row_token.size == 16384 * 8
-    _blockwise_chain(moe, r, 30, weights=blockwise_weights)
+    _blockwise_chain(moe, r, 30, weights=blockwise_weights, name="moe_blockwise")
 
 
 def test_moe_blockwise_chain_skewed_routing(moe, blockwise_weights):
@@ -312,7 +315,7 @@ def test_moe_blockwise_chain_skewed_routing(moe, blockwise_weights):
     r = moe["routing_skewed"]
     sizes = np.diff(r.offsets)
     assert np.sum(sizes == 0) == 8 and np.any(sizes % 128 != 0)
-    _blockwise_chain(moe, r, 40, check_down=True, weights=blockwise_weights)
+    _blockwise_chain(moe, r, 40, check_down=True, weights=blockwise_weights, name="moe_blockwise_skewed")
 
 
 def test_moe_mxfp8_chain_full_size(moe):
@@ -351,7 +354,7 @@ def test_moe_mxfp8_chain_full_size(moe):
     _check_grouped(r.offsets, groups, 52, gu16, gu32,
                    lambda g, r0, r1: (qx_h[r.row_token[r0:r1]], sx_h[r.row_token[r0:r1]],
                                       host(qgu[g * n_gu:(g + 1) * n_gu]), host(sgu[g * n_gu:(g + 1) * n_gu])),
-                   mx=True)
+                   mx=True, record="moe_mxfp8_gate_up")
     del gu32
     qh = torch.empty((rows, INTER), dtype=torch.uint8, device="cuda")
     sh = torch.empty((rows, INTER // 32), dtype=torch.uint8, device="cuda")
@@ -368,7 +371,7 @@ def test_moe_mxfp8_chain_full_size(moe):
     _check_grouped(r.offsets, groups, 54, dn16, dn32,
                    lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g * HID:(g + 1) * HID]),
                                       host(sdt[g * HID:(g + 1) * HID])),
-                   mx=True)
+                   mx=True, record="moe_mxfp8_down")
 
 
 # ------------------------------------------------------------------ combine

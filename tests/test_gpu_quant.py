@@ -119,6 +119,37 @@ def test_rowblock_qwen3_4b_activation_full():
     _assert_same_scales(s, sr)
 
 
+def test_rowblock_grid_stride_past_65536_workgroups():
+    """A tensor larger than one trip of the row-group grid (65,536
+    workgroups x 16 rows of 16 lanes x 4 runs = 4,194,304 runs of 128
+    values, about 537M elements): 33,000 x 16,384 (4,224,000 runs) takes the
+    grid-stride loop for its last runs, and the streaming-store variant (codes
+    above 256 MB).  Every code and scale, both scale layouts, and the MX
+    quantizer on the same tensor.  The input is random finite bf16 bit
+    patterns (sign, exponent 2^-15..2^9, mantissa uniform): the test is about
+    indexing, not value distribution."""
+    rows, cols = 33000, 16384
+    assert rows * (cols // 128) > 65536 * 16 * 4
+    rng = np.random.default_rng(91)
+    x = rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint16) & np.uint16(0x807F)
+    x |= (rng.integers(112, 137, size=(rows, cols), dtype=np.uint16) << np.uint16(7)).astype(np.uint16)
+    _say("grid-stride rowblock", x.shape)
+    xd = dev_bf16(x)
+    qr, sr = oracle.quant_1x128(x)
+    for layout in ("m_major", "row_major"):
+        q, s = ops.quant_rowblock(xd, ops.AXIS_ROW, layout)
+        torch.cuda.synchronize()
+        _assert_same_codes(q, qr)
+        _assert_same_scales(s, sr)
+        del q, s
+    del qr, sr
+    qm, sm = ops.mx_quant(xd)
+    torch.cuda.synchronize()
+    qr, sr = oracle.mx_quant_1x32(x)
+    _assert_same_codes(qm, qr)
+    assert np.array_equal(host(sm), sr)
+
+
 # ------------------------------------------------------------- 128x1 groups
 @pytest.mark.parametrize("shape", [(512, 384), (272, 72), (16, 8)])
 def test_colblock_small(shape):
