@@ -66,6 +66,7 @@ def parse():
                     help="back-to-back launches per event pair in the per-kernel pass")
     ap.add_argument("--copies", type=int, default=4, help="activation copies rotated across steps")
     ap.add_argument("--reps", type=int, default=10, help="repetitions per kernel of the other workloads")
+    ap.add_argument("--warm-ms", type=float, default=60.0, help="warm-up of each other workload (ms)")
     ap.add_argument("--workloads", default=",".join(WORKLOADS),
                     help="other workloads to time after the headline step (comma list, or 'none')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -692,7 +693,7 @@ def main():
             sys.exit(2)
         print("timing %s" % wname, file=sys.stderr, flush=True)
         seq, cfg = table[wname](torch, ops, inputs, to_dev, R)
-        ms = time_sequence(torch, stream, [fn for _, fn, _ in seq], args.reps, 10)
+        ms = time_sequence(torch, stream, [fn for _, fn, _ in seq], args.reps, min(10, args.reps), args.warm_ms)
         ks = {n: kernel_entry(*wk, t) for (n, _, wk), t in zip(seq, ms)}
         others[wname] = {"config": cfg, "ms_per_pass": round(float(sum(ms)), 5), "kernels": ks}
         del seq

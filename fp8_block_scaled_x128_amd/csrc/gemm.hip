@@ -264,14 +264,25 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
+// FP32 partial of one 128-K slice of a 16 x 16 tile, unscaled.  Constant
+// zero scale operands make the compiler emit the plain
+// v_mfma_f32_16x16x128_f8f6f4 (one 8-byte instruction, no scaling) instead of
+// the scaled form, which is issued as a v_mfma_ld_scale_b32 prefix plus the
+// matrix instruction (16 bytes): 2-4% faster on the MLP shapes, bit-identical
+// results (the exact-operand tests compare every tiling bit for bit).
 __device__ __forceinline__ v4f mfma_unit(const v8i& a, const v8i& b) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, kE8M0One, 0, kE8M0One);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF, int WN, bool SWIGLU = false>
+// GATHER: grouped launches whose A rows are gathered through a_rows (the MoE
+// dispatch); a separate instantiation, so that the launches with and without
+// the gather (gate/up and down projections) also show as separate kernels in
+// profiles.
+template <int MODE, bool GROUPED, bool OUTF32, int WAVES, int NF, int WN, bool SWIGLU = false, bool GATHER = false>
 __global__ void __launch_bounds__((Cfg<WAVES, NF, false, WN>::kThreads), (Cfg<WAVES, NF, false, WN>::kMinWavesPerEU))
 k_gemm(KArgs p) {
+    static_assert(!GATHER || GROUPED, "row gather: grouped launches only");
     using C = Cfg<WAVES, NF, (MODE == MODE_ROW128 || MODE == MODE_MX), WN>;
     // SWIGLU tiles: 256 weight rows = 128 gate rows (wave column 0) and the
     // matching 128 up rows (wave column 1) for 128 columns of h
@@ -438,7 +449,7 @@ k_gemm(KArgs p) {
     }
     auto arow = [&](int m_local) {             // physical A row of tile row m_local (clamped)
         int m = min(m_begin + m_local, m_end - 1);
-        if (GROUPED && p.a_rows != nullptr) m = p.a_rows[m];
+        if (GATHER) m = p.a_rows[m];
         return m;
     };
 
@@ -587,7 +598,7 @@ k_gemm(KArgs p) {
         for (int mt = 0; mt < 4; ++mt) {
             if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
             else if (MODE == MODE_P2) mxa[mt] = lds_readu8(sa_lds + mt * 64 + (kb & 3));
-            else if (MODE == MODE_KINV) mxa[mt] = kE8M0One;
+            else if (MODE == MODE_KINV) mxa[mt] = 0;    // constant 0: the plain (unscaled) instruction, see mfma_unit
             else sam[mt] = lds_readf(sa_lds + mt * 64);
         }
         if (C::kABarrier) {
@@ -622,7 +633,7 @@ k_gemm(KArgs p) {
 #pragma unroll
             for (int nt = 0; nt < NF; ++nt) {
                 const v8i fb = read_frag(bb, nt * 16 * BK);
-                const int mxb = MODE == MODE_KINV ? kE8M0One
+                const int mxb = MODE == MODE_KINV ? 0
                                 : MODE == MODE_P2 ? ((NF == 8 || nt < nb_w) ? pb0 : pb1)
                                                   : lds_readu8(sb8 + nt * 64);
 #pragma unroll
@@ -915,10 +926,18 @@ hipError_t launch(const KArgs& p, bool out_f32, hipStream_t st) {
         const int64_t items = ((int64_t)(p.M + C::BM - 1) / C::BM + p.G) * ((p.N + C::BN - 1) / C::BN);
         grid = dim3((unsigned)std::min<int64_t>((items + 7) / 8 * 8, kCUs));
     }
-    if (out_f32)
+    if (GROUPED && p.a_rows != nullptr) {
+        if (out_f32)
+            hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES, NF, WN, false, GROUPED>), grid, dim3(C::kThreads), 0,
+                               st, p);
+        else
+            hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false, WAVES, NF, WN, false, GROUPED>), grid, dim3(C::kThreads), 0,
+                               st, p);
+    } else if (out_f32) {
         hipLaunchKernelGGL((k_gemm<MODE, GROUPED, true, WAVES, NF, WN>), grid, dim3(C::kThreads), 0, st, p);
-    else
+    } else {
         hipLaunchKernelGGL((k_gemm<MODE, GROUPED, false, WAVES, NF, WN>), grid, dim3(C::kThreads), 0, st, p);
+    }
     return hipGetLastError();
 }
 
@@ -1079,7 +1098,10 @@ hipError_t launch_gemm_grouped_swiglu(const GemmArgs& g, int64_t I, uint8_t* hq,
     // rounded up to a multiple of the 8 XCDs
     const int64_t items = ((int64_t)(g.M + C::BM - 1) / C::BM + g.G) * (I / 128);
     const dim3 grid((unsigned)std::min<int64_t>((items + 7) / 8 * 8, kCUs));
-    hipLaunchKernelGGL((k_gemm<MODE_BLOCK128, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
+    if (p.a_rows != nullptr)
+        hipLaunchKernelGGL((k_gemm<MODE_BLOCK128, true, false, 8, 8, 2, true, true>), grid, dim3(C::kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_gemm<MODE_BLOCK128, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1093,7 +1115,10 @@ hipError_t launch_gemm_mx_swiglu(const MxGemmArgs& g, int64_t I, uint8_t* hq, in
     using C = Cfg<8, 8>;
     const int64_t items = ((int64_t)(g.M + C::BM - 1) / C::BM + g.G) * (I / 128);
     const dim3 grid((unsigned)std::min<int64_t>((items + 7) / 8 * 8, kCUs));
-    hipLaunchKernelGGL((k_gemm<MODE_MX, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
+    if (p.a_rows != nullptr)
+        hipLaunchKernelGGL((k_gemm<MODE_MX, true, false, 8, 8, 2, true, true>), grid, dim3(C::kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_gemm<MODE_MX, true, false, 8, 8, 2, true>), grid, dim3(C::kThreads), 0, st, p);
     return hipGetLastError();
 }
 

@@ -3,13 +3,23 @@
     python -m fp8_block_scaled_x128_amd.profiling stats STATS_CSV --command CMD --out FILE.md
         per-kernel duration table from a `rocprofv3 --kernel-trace --stats` run
 
+    python -m fp8_block_scaled_x128_amd.profiling pmc CSV [CSV ...] --command CMD [--command CMD ...]
+            --out FILE.md [--copy-mib N]
+        per-kernel counter table from `rocprofv3 --pmc` runs (one CSV per
+        pass), kernels told apart by name and grid size, with the derived
+        figures: matrix-pipe utilization SQ_VALU_MFMA_BUSY_CYCLES / (cycles x
+        1024 SIMDs), the shader clock GRBM_GUI_ACTIVE / duration, FP8 matrix
+        TFLOP/s from SQ_INSTS_VALU_MFMA_MOPS_F8 (512 flop per MOP), and HBM
+        bytes and GB/s from FETCH_SIZE and WRITE_SIZE scaled by what they read
+        for the plain device copy of N MiB that bench.py --copy-probe-mib N
+        runs (known bytes).  GRBM_GUI_ACTIVE is summed over the 8 XCDs.
+
     python -m fp8_block_scaled_x128_amd.profiling traffic --fetch CSV --write CSV
-            --copy-mib N --gemm-calls C --command-fetch CMD --command-write CMD --out FILE.json
-        HBM bytes per dense GEMM call from two `rocprofv3 --pmc` runs
-        (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) of a program that
-        makes C dense BLOCK128 GEMM calls, half of them the MLP up projection
-        and half the down projection (a call may launch two tilings).  Each
-        counter is scaled by what it reads for the plain device copy of N MiB
+            --copy-mib N --grids G1,G2 --command-fetch CMD --command-write CMD --out FILE.json
+        HBM bytes per launch of the MLP up and down GEMMs (dense BLOCK128,
+        bf16 out, told apart by their grid sizes G1 and G2) from two
+        `rocprofv3 --pmc` runs (FETCH_SIZE, then WRITE_SIZE, in KiB per
+        dispatch).  Each counter is scaled by what it reads for the plain device copy of N MiB
         that bench.py --copy-probe-mib N runs after its timed region (known
         bytes read and written).  The record carries a hash of the GEMM
         sources, so bench.py reports it only while the kernel is unchanged.
@@ -78,7 +88,17 @@ def _per_kernel(counter_csv: str, counter: str):
     return res
 
 
-def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, calls: int, cmd_fetch: str, cmd_write: str) -> dict:
+def _probe_mean(values):
+    """Mean counter value of the copy probe's dispatches: the largest device
+    copies of the run (other, smaller copies are the program's own uploads)."""
+    top = max(values)
+    return statistics.mean(v for v in values if v >= 0.5 * top)
+
+
+def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, grids, cmd_fetch: str, cmd_write: str) -> dict:
+    """HBM bytes per launch of the headline step's two GEMMs (dense BLOCK128,
+    bf16 out), told apart by grid size: the mean per dispatch of each, then
+    the mean of the two."""
     fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
     write = _per_kernel(write_csv, "WRITE_SIZE")
     copy_bytes = copy_mib * (1 << 20)
@@ -89,8 +109,8 @@ def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, calls: int, cm
             raise SystemExit("no dispatches of %s in the counter file" % sub)
         return [v for k in keys for v in d[k]]
 
-    f_copy = statistics.mean(v for _, v in pick(fetch, COPY_KERNEL)) * 1024
-    w_copy = statistics.mean(v for _, v in pick(write, COPY_KERNEL)) * 1024
+    f_copy = _probe_mean([v for _, v in pick(fetch, COPY_KERNEL)]) * 1024
+    w_copy = _probe_mean([v for _, v in pick(write, COPY_KERNEL)]) * 1024
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
     g_f = pick(fetch, DENSE_GEMM_KERNEL)
     g_w = pick(write, DENSE_GEMM_KERNEL)
@@ -99,8 +119,11 @@ def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, calls: int, cm
         by_grid.setdefault(grid, {"fetch": [], "write": []})["fetch"].append(v * 1024 * f_scale)
     for grid, v in g_w:
         by_grid.setdefault(grid, {"fetch": [], "write": []})["write"].append(v * 1024 * w_scale)
-    fetch_pl = sum(v * 1024 * f_scale for _, v in g_f) / calls
-    write_pl = sum(v * 1024 * w_scale for _, v in g_w) / calls
+    missing = [g for g in grids if g not in by_grid]
+    if missing:
+        raise SystemExit("no GEMM dispatches with grid size %s" % missing)
+    fetch_pl = statistics.mean(statistics.mean(by_grid[g]["fetch"]) for g in grids)
+    write_pl = statistics.mean(statistics.mean(by_grid[g]["write"]) for g in grids)
     # the two GEMMs of the MLP step: up (M 4096, N 9728, K 2560) and down (M 4096, N 2560, K 9728);
     # minimum bytes = both FP8 operands, their FP32 scales and the bf16 output, once each
     mins = []
@@ -109,18 +132,76 @@ def traffic_record(fetch_csv: str, write_csv: str, copy_mib: int, calls: int, cm
     return {
         "kernel": DENSE_GEMM_KERNEL,
         "gemm_sources_sha256": gemm_sources_hash(),
-        "gemm_calls": calls,
+        "grids": list(grids),
         "hbm_bytes_per_launch": fetch_pl + write_pl,
         "fetch_bytes_per_launch": fetch_pl,
         "write_bytes_per_launch": write_pl,
         "algorithmic_min_bytes_per_launch": statistics.mean(mins),
         "per_grid_size": {str(g): {"dispatches": len(v["fetch"]), "fetch_bytes": statistics.mean(v["fetch"]),
                                    "write_bytes": statistics.mean(v["write"])}
-                          for g, v in by_grid.items()},
+                          for g, v in by_grid.items() if g in grids},
         "copy_calibration": {"bytes": copy_bytes, "fetch_counter_bytes": f_copy, "write_counter_bytes": w_copy,
                              "fetch_scale": f_scale, "write_scale": w_scale},
         "source": {"fetch": cmd_fetch, "write": cmd_write},
     }
+
+
+XCDS, SIMDS = 8, 1024
+
+
+def _pmc_rows(csvs):
+    """{(kernel, grid): {"dur": [ns], counter: [values]}} over all passes."""
+    res = {}
+    for f in csvs:
+        seen = set()
+        for r in csv.DictReader(open(f)):
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            d = res.setdefault(key, {"dur": []})
+            d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            did = (f, r["Dispatch_Id"])
+            if did not in seen:
+                seen.add(did)
+                d["dur"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return res
+
+
+def pmc_markdown(csvs, commands, copy_mib=0) -> str:
+    res = _pmc_rows(csvs)
+    mean = statistics.mean
+    fs = ws = None
+    if copy_mib:
+        cf = [v for (name, _), d in res.items() if COPY_KERNEL in name for v in d.get("FETCH_SIZE", [])]
+        cw = [v for (name, _), d in res.items() if COPY_KERNEL in name for v in d.get("WRITE_SIZE", [])]
+        fs = copy_mib * (1 << 20) / (_probe_mean(cf) * 1024) if cf else None
+        ws = copy_mib * (1 << 20) / (_probe_mean(cw) * 1024) if cw else None
+    counters = sorted({c for d in res.values() for c in d if c != "dur"})
+    out = ["# rocprofv3 counters per kernel", "", "Commands (one pass each):", "", "```"] + list(commands) + ["```", ""]
+    if fs or ws:
+        out += ["Copy calibration (%d MiB device copy): FETCH_SIZE x %s, WRITE_SIZE x %s." % (
+            copy_mib, "%.4f" % fs if fs else "-", "%.4f" % ws if ws else "-"), ""]
+    out += ["Derived (per dispatch, mean; durations are those of the counter runs, which serialize dispatches):", "",
+            "| kernel | grid | dispatches | us | clock GHz | MFMA busy % | FP8 TFLOP/s | HBM read MB | HBM write MB | HBM GB/s |",
+            "|---|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid), d in sorted(res.items(), key=lambda kv: -mean(kv[1]["dur"]) * len(kv[1]["dur"])):
+        us = mean(d["dur"]) / 1e3
+        cyc = mean(d["GRBM_GUI_ACTIVE"]) / XCDS if "GRBM_GUI_ACTIVE" in d else None
+        clk = "%.2f" % (cyc / (us * 1e3)) if cyc else "-"
+        busy = "%.1f" % (100 * mean(d["SQ_VALU_MFMA_BUSY_CYCLES"]) / (cyc * SIMDS)) \
+            if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in d else "-"
+        tf = "%.0f" % (mean(d["SQ_INSTS_VALU_MFMA_MOPS_F8"]) * 512 / (us * 1e-6) / 1e12) \
+            if "SQ_INSTS_VALU_MFMA_MOPS_F8" in d and mean(d["SQ_INSTS_VALU_MFMA_MOPS_F8"]) > 0 else "-"
+        rd = mean(d["FETCH_SIZE"]) * 1024 * fs if fs and "FETCH_SIZE" in d else None
+        wr = mean(d["WRITE_SIZE"]) * 1024 * ws if ws and "WRITE_SIZE" in d else None
+        gbs = "%.0f" % ((rd + wr) / (us * 1e-6) / 1e9) if rd is not None and wr is not None else "-"
+        out.append("| `%s` | %d | %d | %.1f | %s | %s | %s | %s | %s | %s |" % (
+            name, grid, len(d["dur"]), us, clk, busy, tf, "%.1f" % (rd / 1e6) if rd is not None else "-",
+            "%.1f" % (wr / 1e6) if wr is not None else "-", gbs))
+    out += ["", "Raw counters (mean per dispatch):", "",
+            "| kernel | grid | " + " | ".join(counters) + " |", "|---|---|" + "---|" * len(counters)]
+    for (name, grid), d in sorted(res.items()):
+        out.append("| `%s` | %d | " % (name, grid) + " | ".join(
+            "%.4g" % mean(d[c]) if c in d else "-" for c in counters) + " |")
+    return "\n".join(out) + "\n"
 
 
 def main(argv=None):
@@ -130,11 +211,16 @@ def main(argv=None):
     s.add_argument("stats_csv")
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
+    m = sub.add_parser("pmc")
+    m.add_argument("csvs", nargs="+")
+    m.add_argument("--command", action="append", required=True)
+    m.add_argument("--copy-mib", type=int, default=0)
+    m.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-mib", type=int, required=True)
-    t.add_argument("--gemm-calls", type=int, required=True)
+    t.add_argument("--grids", required=True, help="grid sizes of the up and down GEMM launches, comma list")
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out", required=True)
@@ -142,8 +228,12 @@ def main(argv=None):
     if a.cmd == "stats":
         with open(a.out, "w") as fh:
             fh.write(stats_markdown(a.stats_csv, a.command))
+    elif a.cmd == "pmc":
+        with open(a.out, "w") as fh:
+            fh.write(pmc_markdown(a.csvs, a.command, a.copy_mib))
     else:
-        rec = traffic_record(a.fetch, a.write, a.copy_mib, a.gemm_calls, a.command_fetch, a.command_write)
+        rec = traffic_record(a.fetch, a.write, a.copy_mib, [int(g) for g in a.grids.split(",")], a.command_fetch,
+                             a.command_write)
         with open(a.out, "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
