@@ -173,14 +173,15 @@ def check_vs_oracle_and_model(y_gpu, yref, babs, y_model, bf16_out=False, record
 
 
 def record_rel_error(name, rel, rel_model, allowed):
-    """Append one line per checked GEMM to gpurun_out/gemm_rel_errors.jsonl
-    when that folder exists (the figures quoted for each workload)."""
+    """Append one JSON line per checked GEMM to the file named by the
+    environment variable FP8BS_GEMM_ERROR_LOG, if set (the per-workload
+    error figures)."""
     import json
     import os
-    out = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    if not os.path.isdir(out):
+    path = os.environ.get("FP8BS_GEMM_ERROR_LOG")
+    if not path:
         return
-    with open(os.path.join(out, "gemm_rel_errors.jsonl"), "a") as fh:
+    with open(path, "a") as fh:
         fh.write(json.dumps({"case": name, "rel_vs_oracle": rel, "rel_vs_model": rel_model,
                              "allowed_vs_oracle": allowed}) + "\n")
 
