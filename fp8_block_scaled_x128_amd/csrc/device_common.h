@@ -152,32 +152,159 @@ __device__ __forceinline__ float absmax8(const float v[8]) {
     return m;
 }
 
-// silu(g) * u rounded to bf16 and widened back (the value the next GEMM consumes).
+// silu(g) * u in fp32, before rounding to bf16, for g >= -44.
 // silu(g) = g * sigmoid(g), with sigmoid(g) = 1 / (1 + t) for g >= 0 and
 // t / (1 + t) for g < 0, t = exp(-|g|) in (0, 1]: no overflow, and 1 + t in
-// [1, 2] for the hardware reciprocal.  t = 2^a with a = -|g| log2(e) split
-// into a rounded part for the hardware exp2 and its exact residual applied to
-// first order, so t is good to about one fp32 ulp.  Where t would be an fp32
-// denormal (a < -64, that is |g| above about 44.4) it is formed scaled by 2^64
-// and the scale is removed from the final product.  The accurate expf and IEEE
-// division cost about 25 more instructions per element, enough to make this
-// kernel VALU bound.  The product is rounded once to bf16: the result stays
-// within one bf16 ulp of the exactly rounded value, and differs from it only
-// where the exact value lies a few fp32 ulp from a bf16 rounding midpoint.
-__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+// [1, 2] for the hardware reciprocal; t stays an fp32 normal over the range.
+// t = 2^a with a = -|g| log2(e) split into a rounded part for the hardware
+// exp2 and its exact residual applied to first order.  Measured over every
+// bf16 g >= -44 (except 0 < |g| < 2^-124), g * sigmoid(g) is within 3.53 *
+// 2^-24 of its exact value relatively, so h = (g * sigmoid(g)) * u is within
+// 4.03 fp32 ulps of the exact h.
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
     constexpr float kLog2e = 1.4426950216293335f;       // log2(e) rounded to fp32
     constexpr float kLog2eLo = 1.925963033500011e-08f;  // log2(e) - kLog2e
     constexpr float kLn2 = 0.6931471824645996f;
-    const float ng = -fabsf(g);
+    // |g| clamped to 128 (where t is far below fp32's resolution of 1 + t)
+    // so that a_hi cannot overflow
+    const float ng = fmaxf(-fabsf(g), -128.0f);
     const float a_hi = ng * kLog2e;
     const float a_lo = __builtin_fmaf(ng, kLog2e, -a_hi) + ng * kLog2eLo;
-    const bool tiny = a_hi < -64.0f;
-    const float t = __builtin_amdgcn_exp2f(tiny ? a_hi + 64.0f : a_hi) * __builtin_fmaf(a_lo, kLn2, 1.0f);
-    const float r = __builtin_amdgcn_rcpf(1.0f + (tiny ? 0.0f : t));
+    const float t = __builtin_amdgcn_exp2f(a_hi) * __builtin_fmaf(a_lo, kLn2, 1.0f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + t);
     const float sig = g >= 0.0f ? r : t * r;
-    float h = (g * sig) * u;
-    if (tiny && g < 0.0f) h *= 0x1p-64f;
-    return f32_to_bf16_rne(h);
+    return (g * sig) * u;
+}
+
+// Where silu_mul_f32 cannot decide the bf16 rounding of h (finite inputs):
+// h lies within kSiluNearUlps fp32 ulps of a bf16 rounding midpoint (an fp32
+// pattern whose low 16 bits are 0x8000); g < -44, where t leaves the fp32
+// normal range; or 0 < |g| < 2^-124, where g * sigmoid(g) can lose precision
+// to fp32 denormals.
+constexpr uint32_t kSiluNearUlps = 5;
+constexpr float kSiluGMin = -44.0f;
+constexpr float kSiluGTiny = 0x1p-124f;
+__device__ __forceinline__ uint32_t silu_mid_dist(float h) {
+    // 0 .. 2 kSiluNearUlps where h is near a midpoint
+    return (__float_as_uint(h) + (kSiluNearUlps - 0x8000u)) & 0xffffu;
+}
+__device__ __forceinline__ bool silu_needs_f64(float g, float h) {
+    return silu_mid_dist(h) <= 2u * kSiluNearUlps || g < kSiluGMin ||
+           (fabsf(g) < kSiluGTiny && g != 0.0f);
+}
+
+// fp64 -> bf16 pattern, round to nearest even.  bf16 has fp32's exponent
+// range: 8 significant bits down to 2^-126, then a fixed spacing of 2^-133.
+// The magnitude is scaled so that one bf16 spacing becomes 1 and rounded to
+// an integer q; the pattern is then (exponent of the spacing + 133) * 2^7 + q,
+// which also carries q = 256 into the next binade and gives 0x7f80
+// (infinity) past the largest finite value.
+__device__ __forceinline__ uint32_t bf16_from_f64_rne(double x) {
+    const uint64_t bits = (uint64_t)__double_as_longlong(x);
+    const uint32_t sign = (uint32_t)(bits >> 48) & 0x8000u;
+    const uint32_t hi = (uint32_t)(bits >> 32) & 0x7fffffffu;
+    if (hi >= 0x7ff00000u) return sign | ((hi > 0x7ff00000u || (uint32_t)bits != 0u) ? 0x7fc0u : 0x7f80u);
+    const double ax = fabs(x);
+    int e2;
+    (void)frexp(ax, &e2);                       // ax in [2^(e2-1), 2^e2)
+    const int se = (e2 - 1 < -126 ? -126 : e2 - 1) - 7;
+    const double q = rint(ldexp(ax, -se));      // exact scaling, then ties to even
+    if (q == 0.0) return sign;
+    const uint32_t b = (uint32_t)((se + 133) * 128) + (uint32_t)q;
+    return sign | (b >= 0x7f80u ? 0x7f80u : b);
+}
+
+// Constants of the rare fp64 path: log2(e); ln(2) as a 39-bit head (n * head
+// is exact for the |n| <= 1077 used) and the rounded rest; the clamp of the
+// exponential's argument to [-746, 710] (beyond it the result is 0 or
+// infinite in fp64 already); then 1/k! for k = 13 .. 0, each rounded to the
+// nearest double.
+__device__ const double kSiluF64[19] = {
+    0x1.71547652b82fep+0,  0x1.62e42fefa2000p-1,  0x1.9ef35793c7673p-41, 0x1.63p+9, -0x1.75p+9,
+    0x1.6124613a86d09p-33, 0x1.1eed8eff8d898p-29, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22,
+    0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16, 0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10,
+    0x1.1111111111111p-7,  0x1.5555555555555p-5,  0x1.5555555555555p-3,  0x1p-1, 0x1p+0, 0x1p+0};
+
+// exp(x) in fp64: x = n ln 2 + r with n = rint(x log2 e) and |r| <= ln(2)/2
+// (Cody-Waite reduction with the split ln 2), e^r from its Taylor series to
+// degree 13 (the first dropped term is below 2^-57 relative), scaled by 2^n.
+// `c` is kSiluF64.
+typedef __attribute__((address_space(4))) const double* silu_cptr;     // scalar-loadable
+__device__ __forceinline__ double silu_exp_f64(double x, silu_cptr c) {
+    x = fmin(fmax(x, c[4]), c[3]);
+    const double n = rint(x * c[0]);
+    double r = fma(-n, c[1], x);
+    r = fma(-n, c[2], r);
+    double p = c[5];
+#pragma unroll
+    for (int k = 6; k < 19; ++k) p = fma(p, r, c[k]);
+    return ldexp(p, (int)n);
+}
+
+// h = g / (1 + exp(-g)) * u evaluated in fp64 and rounded once to bf16: the
+// definition of the bf16 h that the next GEMM consumes.  The constants are
+// read through a pointer the compiler cannot see through, so that they are
+// loaded here, on the rare path that needs them, instead of being hoisted out
+// of the callers' loops into registers held throughout.
+__device__ __forceinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
+    silu_cptr c = (silu_cptr)kSiluF64;
+    asm volatile("" : "+s"(c));
+    const double gd = g;
+    return bf16_from_f64_rne(gd / (1.0 + silu_exp_f64(-gd, c)) * (double)u);
+}
+
+// The values of silu_mul_f32 for eight (g, u) as bf16 patterns, and whether
+// this lane holds one that they cannot round (about 2^-12 of the values at
+// GEMM-output magnitudes); one test over the eight (their minima) decides it.
+__device__ __forceinline__ bool silu_mul8_bf16_fast(const float g[8], const float u[8], uint32_t hb[8], float h[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = silu_mul_f32(g[i], u[i]);
+    float gmin = g[0], amin = fabsf(g[0]);
+    uint32_t dmin = silu_mid_dist(h[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        gmin = fminf(gmin, g[i]);
+        amin = fminf(amin, fabsf(g[i]));
+        dmin = min(dmin, silu_mid_dist(h[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const uint32_t w = pack_bf16x2(h[i], h[i + 1]);
+        hb[i] = w & 0xffffu;
+        hb[i + 1] = w >> 16;
+    }
+    return gmin < kSiluGMin || amin < kSiluGTiny || dmin <= 2u * kSiluNearUlps;
+}
+
+// Replaces, in hb, each value that the fp32 evaluation h cannot round by the
+// fp64 evaluation (on the lanes and values that need it).
+__device__ __forceinline__ void silu_fix8(const float g[8], const float u[8], const float h[8], uint32_t hb[8]) {
+    uint32_t need = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) need |= (uint32_t)silu_needs_f64(g[i], h[i]) << i;
+    while (need != 0) {
+        const int k = __builtin_ctz(need);
+        need &= need - 1;
+        float gk = g[0], uk = u[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            gk = k == i ? g[i] : gk;
+            uk = k == i ? u[i] : uk;
+        }
+        const uint32_t r = silu_mul_bf16_f64(gk, uk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hb[i] = k == i ? r : hb[i];
+    }
+}
+
+// h = bf16(silu(g) * u) for the eight bf16 (g, u) pairs packed in gw, uw,
+// bit-exact against the fp64 evaluation: the fp32 one, and on the rare lanes
+// where it cannot decide a rounding, the fp64 one for those values.
+__device__ __forceinline__ void silu_mul8_bf16(const uint4 gw, const uint4 uw, uint32_t hb[8]) {
+    float g[8], u[8], h[8];
+    unpack8(gw, g);
+    unpack8(uw, u);
+    if (__builtin_expect(silu_mul8_bf16_fast(g, u, hb, h), 0)) silu_fix8(g, u, h, hb);
 }
 
 }  // namespace fp8bs

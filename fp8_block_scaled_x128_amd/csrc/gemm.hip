@@ -864,11 +864,11 @@ k_gemm(KArgs p) {
                                     (uint32_t)(2 * (wr & 1) * kRows * kPitch + rr * kPitch + sub * 16);
                 const u32x4 gv = lds_read16(ga);
                 const u32x4 uv = lds_read16(ga + kRows * kPitch);
-                float g[8], u[8], v[8];
-                unpack8(make_uint4(gv.x, gv.y, gv.z, gv.w), g);
-                unpack8(make_uint4(uv.x, uv.y, uv.z, uv.w), u);
+                float v[8];
+                uint32_t hb[8];
+                silu_mul8_bf16(make_uint4(gv.x, gv.y, gv.z, gv.w), make_uint4(uv.x, uv.y, uv.z, uv.w), hb);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(silu_mul_bf16(g[i], u[i]) << 16);
+                for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(hb[i] << 16);
                 const int m = em_begin + wr * 64 + pass * kRows + rr;
                 uint32_t w0, w1;
                 if (MODE == MODE_MX) {

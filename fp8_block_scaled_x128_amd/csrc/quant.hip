@@ -77,14 +77,10 @@ __device__ __forceinline__ void rowgroup_body(const RowArgs& p, int32_t block, i
             float v[8];
             unpack8(raw[u], v);
             if (SILU) {
-                float up[8];
-                unpack8(raw_u[u], up);
                 uint32_t hb[8];
+                silu_mul8_bf16(raw[u], raw_u[u], hb);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    hb[i] = silu_mul_bf16(v[i], up[i]);
-                    v[i] = __uint_as_float(hb[i] << 16);
-                }
+                for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(hb[i] << 16);
                 if (p.h != nullptr && valid) {
                     uint4 hw = make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
                                           hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16));

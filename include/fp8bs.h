@@ -320,7 +320,7 @@ fp8bs_status mxfp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int6
 
 /* ------------------------------------------------------------------------
  * fp8_silu_mul_quant -- the step between the MoE gate/up and down GEMMs:
- * h = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)) in fp32, then
+ * h = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)), then
  * quantization of h, 1x128 with FP32 scales (mx == 0) or 1x32 with UE8M0
  * scales (mx == 1, see mxfp8_quant).
  * The pages do not describe this step.  It is the plainest reading of the
@@ -339,8 +339,12 @@ fp8bs_status mxfp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int6
  * Requirements: I % 128 == 0 (I % 32 == 0 when mx == 1); ld_in >= 2 I,
  * ld_in % 8 == 0, gate_up 16-byte aligned; ld_q >= I, ld_q % 8 == 0;
  * ld_h >= I if h_out.
- * silu is evaluated with the hardware exp2 and reciprocal (a few fp32 ulp);
- * h agrees with an exactly rounded fp64 evaluation to within one bf16 ulp.
+ * h is bit-exact against g / (1 + exp(-g)) * u evaluated in fp64 and
+ * rounded once to bf16, for every finite bf16 g and u: an fp32 evaluation
+ * (hardware exp2 and reciprocal, within 4.03 fp32 ulps of the exact value)
+ * rounds it wherever it lies farther than 5 fp32 ulps from a bf16 rounding
+ * midpoint, and an fp64 evaluation decides the rest (about 2^-12 of the
+ * values at GEMM-output magnitudes, and every g below -44).
  * ------------------------------------------------------------------------ */
 fp8bs_status fp8_silu_mul_quant(const uint16_t* gate_up, int64_t rows, int64_t I, int64_t ld_in, int mx,
                                 uint8_t* q, int64_t ld_q, void* s, int64_t s_stride_row, int64_t s_stride_group,
