@@ -163,7 +163,110 @@ hipError_t launch_rowgroup(RowArgs p, bool row_fast, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Token-axis groups with transposed output: 128x1 with FP32 scales, or (MX)
-// 32x1 with UE8M0 scales.  Tile: 128 rows x 64 cols, staged in LDS as
+// 32x1 with UE8M0 scales.  No LDS.  A lane holds RPL consecutive rows of 8
+// columns (RPL loads of 16 bytes); the 128 / RPL lanes of a lane group hold
+// the 128 rows of a row group for the same 8 columns, and the wave's 64 / (128
+// / RPL) lane groups sit side by side in columns.  Column k of a lane is the
+// k-th bf16 of each of its RPL words, so the lane's values of a column are RPL
+// consecutive codes of the transposed row: one store, and a lane group writes
+// 128 contiguous bytes.  Column maxima: 16-bit integer maxima of the |bf16|
+// bit patterns (ordered as the values), two columns per instruction, then
+// across the lanes of a 128-row group (FP32 scales) or of a 32-row block (MX)
+// by DPP.
+// ---------------------------------------------------------------------------
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pkmax_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t pkmax_dpp(uint32_t v) {
+    return pkmax_u16(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false));
+}
+// maximum over aligned groups of N lanes (N = 2, 4, 8 or 16) by DPP
+template <int N>
+__device__ __forceinline__ uint32_t pkmax_lanes(uint32_t v) {
+    constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kHalfMirror = 0x141, kRowMirror = 0x140;
+    v = pkmax_dpp<kQuadXor1>(v);
+    if (N >= 4) v = pkmax_dpp<kQuadXor2>(v);
+    if (N >= 8) v = pkmax_dpp<kHalfMirror>(v);
+    if (N >= 16) v = pkmax_dpp<kRowMirror>(v);
+    return v;
+}
+__device__ __forceinline__ uint32_t word_at(const uint4& w, int i) {
+    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
+
+constexpr int kColTRows = 16;            // rows per lane (8 lanes x 16 bytes: whole 128-byte row pieces)
+constexpr int kColTWaves = 2;            // waves per workgroup
+constexpr int kColTCols = 8 * 64 / (128 / kColTRows);     // columns per wave
+// Below this many workgroups (4 per CU) the LDS kernel is used.  Measured with
+// inputs rotated past the last-level cache: 4096 x 9728 (2432 workgroups)
+// 34.1 -> 30.2 us here; 4096 x 2560 (640) 12.0 us with LDS against 14.6 here.
+constexpr int64_t kColTMinBlocks = 1024;
+
+template <bool MX>
+__global__ void __launch_bounds__(64 * kColTWaves) k_quant_col_t(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
+                                                                 int64_t ld_x, uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                                 void* __restrict__ s, int64_t ssr, int64_t ssg) {
+    constexpr int R = kColTRows, LPG = 128 / R;
+    const int lane = threadIdx.x & 63;
+    const int gi = lane / LPG, j = lane % LPG;
+    const int32_t c = ((int32_t)blockIdx.x * kColTWaves + (int32_t)(threadIdx.x >> 6)) * kColTCols + 8 * gi;
+    const int32_t rl = (int32_t)blockIdx.y * 128 + R * j;
+    // cols % 8 == 0 and rows % 16 == 0 (% 32 for MX): a lane's block is
+    // valid or empty, and so is each 32-row MX block
+    const bool valid = c < cols && rl < rows;
+    uint4 raw[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        raw[i] = make_uint4(0, 0, 0, 0);
+        if (valid) raw[i] = *reinterpret_cast<const uint4*>(x + (int64_t)(rl + i) * ld_x + c);
+    }
+    uint32_t m[4] = {0u, 0u, 0u, 0u};      // |bf16| maxima, columns 2w (low half) and 2w + 1
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) m[w] = pkmax_u16(m[w], word_at(raw[i], w) & 0x7fff7fffu);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m[w] = MX ? pkmax_lanes<32 / R>(m[w]) : pkmax_lanes<LPG>(m[w]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t mw = m[k >> 1];
+        const float amax = __uint_as_float((k & 1) ? (mw & 0xffff0000u) : (mw << 16));
+        float v[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const uint32_t wd = word_at(raw[i], k >> 1);
+            v[i] = (k & 1) ? bf16_hi(wd) : bf16_lo(wd);
+        }
+        uint32_t q[R / 4];
+        if (!MX) {
+            const float sc = amax / kE4M3Max;
+#pragma unroll
+            for (int i = 0; i < R / 8; ++i) encode8(&v[8 * i], sc, q[2 * i], q[2 * i + 1]);
+            if (valid && j == 0) static_cast<float*>(s)[(int64_t)(c + k) * ssr + (int64_t)blockIdx.y * ssg] = sc;
+        } else {
+            const int e = mx_exponent(amax);
+            const float f = pow2_neg(e);
+#pragma unroll
+            for (int i = 0; i < R / 4; ++i)
+                q[i] = amax == 0.0f ? 0u : enc4(v[4 * i] * f, v[4 * i + 1] * f, v[4 * i + 2] * f, v[4 * i + 3] * f);
+            if (valid && (rl & 31) == 0)
+                static_cast<uint8_t*>(s)[(int64_t)(c + k) * ssr + (int64_t)(rl / 32) * ssg] = (uint8_t)(e + 127);
+        }
+        if (valid) {
+            uint8_t* dst = qt + (int64_t)(c + k) * ld_qt + rl;
+            if (R == 16) *reinterpret_cast<uint4*>(dst) = make_uint4(q[0], q[1], q[2], q[R / 4 - 1]);
+            else *reinterpret_cast<uint2*>(dst) = make_uint2(q[0], q[1]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The same through LDS, for tensors too small to fill the chip with the
+// kernel below (its 16-load, 128-value lanes then leave a long serial tail).
+// Tile: 128 rows x 64 cols, staged in LDS as
 // [column pair][row] words (a word is a bf16 pair of one row).  Thread t then
 // owns column t/4 and rows 32*(t%4) .. +32 and writes those 32 contiguous
 // codes of the transposed row.  128x1: the four threads of a column reduce
@@ -171,7 +274,7 @@ hipError_t launch_rowgroup(RowArgs p, bool row_fast, hipStream_t st) {
 // block.
 // ---------------------------------------------------------------------------
 template <bool MX>
-__global__ void __launch_bounds__(kThreads) k_quant_col_t(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
+__global__ void __launch_bounds__(kThreads) k_quant_col_t_lds(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
                                                           int64_t ld_x, uint8_t* __restrict__ qt, int64_t ld_qt,
                                                           void* __restrict__ s, int64_t ssr, int64_t ssg) {
     __shared__ __attribute__((aligned(16))) uint32_t tile[32][132];
@@ -514,18 +617,28 @@ hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t rows, int64_t I, in
 hipError_t launch_quant_128x1_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt,
                                 int64_t ld_qt, float* s, int64_t ssr, int64_t ssg, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
-    hipLaunchKernelGGL(k_quant_col_t<false>, grid, dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, qt,
-                       ld_qt, (void*)s, ssr, ssg);
+    const unsigned gy = (unsigned)((rows + 127) / 128);
+    const unsigned gx = (unsigned)((cols + kColTCols * kColTWaves - 1) / (kColTCols * kColTWaves));
+    if ((int64_t)gx * gy >= kColTMinBlocks)
+        hipLaunchKernelGGL(k_quant_col_t<false>, dim3(gx, gy), dim3(64 * kColTWaves), 0, st, x, (int32_t)rows,
+                           (int32_t)cols, ld_x, qt, ld_qt, (void*)s, ssr, ssg);
+    else
+        hipLaunchKernelGGL(k_quant_col_t_lds<false>, dim3((unsigned)((cols + 63) / 64), gy), dim3(kThreads), 0, st, x,
+                           (int32_t)rows, (int32_t)cols, ld_x, qt, ld_qt, (void*)s, ssr, ssg);
     return hipGetLastError();
 }
 
 hipError_t launch_mx_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt, int64_t ld_qt,
                              uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 127) / 128));
-    hipLaunchKernelGGL(k_quant_col_t<true>, grid, dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, qt,
-                       ld_qt, (void*)s, ssr, ssg);
+    const unsigned gy = (unsigned)((rows + 127) / 128);
+    const unsigned gx = (unsigned)((cols + kColTCols * kColTWaves - 1) / (kColTCols * kColTWaves));
+    if ((int64_t)gx * gy >= kColTMinBlocks)
+        hipLaunchKernelGGL(k_quant_col_t<true>, dim3(gx, gy), dim3(64 * kColTWaves), 0, st, x, (int32_t)rows,
+                           (int32_t)cols, ld_x, qt, ld_qt, (void*)s, ssr, ssg);
+    else
+        hipLaunchKernelGGL(k_quant_col_t_lds<true>, dim3((unsigned)((cols + 63) / 64), gy), dim3(kThreads), 0, st, x,
+                           (int32_t)rows, (int32_t)cols, ld_x, qt, ld_qt, (void*)s, ssr, ssg);
     return hipGetLastError();
 }
 

@@ -452,11 +452,12 @@ def test_mx_grouped_small_moe():
 
 
 # ------------------------------------------------------- MXFP8 backward
-@pytest.mark.parametrize("shape", [(256, 512), (96, 264), (32, 8), (4096, 2560), (9728, 2560)])
+@pytest.mark.parametrize("shape", [(256, 512), (96, 264), (32, 8), (4096, 2560), (9728, 2560), (4192, 4040)])
 def test_mx_quant_t_bit_exact(shape):
     """32x1 MX blocks down each column, written transposed: codes and scale
     bytes equal the oracle's 1x32 quantization of the transpose (partial
-    128-row and 64-column tiles included)."""
+    128-row and 64-column tiles included; (9728, 2560) and (4192, 4040) take
+    the register kernel, the others the LDS kernel)."""
     _say("mx_quant_t", shape)
     x = _bits(shape, 60, 1.0, 0.01, 50.0)
     if shape[0] >= 64 and shape[1] >= 3:

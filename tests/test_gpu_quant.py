@@ -151,10 +151,18 @@ def test_rowblock_grid_stride_past_65536_workgroups():
 
 
 # ------------------------------------------------------------- 128x1 groups
-@pytest.mark.parametrize("shape", [(512, 384), (272, 72), (16, 8)])
+@pytest.mark.parametrize("shape", [(512, 384), (272, 72), (16, 8), (400, 520), (4096, 2560), (4208, 4040)])
 def test_colblock_small(shape):
+    """128x1 groups down each column, written transposed, with an all-zero
+    group, a saturating group and a group of bf16 subnormals.  Grids under
+    1024 workgroups take the LDS kernel, (4208, 4040) the register kernel;
+    partial 128-row groups and partial 64- and 128-column tiles included."""
     _say("colblock", shape)
     x = _bits(shape, 4)
+    if shape[0] >= 256 and shape[1] >= 3:
+        x[:128, 0] = 0
+        x[128:256, 1] = inputs.to_bf16_bits(np.full(128, 3e38, np.float32))
+        x[:128, 2] = inputs.to_bf16_bits((np.arange(128) * 1e-39).astype(np.float32))
     qt, s = ops.quant_rowblock(dev_bf16(x), ops.AXIS_COL, "row_major")
     torch.cuda.synchronize()
     qr, sr = oracle.quant_128x1_t(x)
