@@ -480,11 +480,17 @@ struct LinearArgs {
 template <bool ROW_FAST>
 __global__ void __launch_bounds__(kThreads) k_quant_linear(LinearArgs a) {
     const int32_t b = (int32_t)blockIdx.x;
-    if (b < a.w_blocks)
+    // W blocks and X workgroups dealt in proportion (workgroup b is a W block
+    // when floor((b + 1) W / n) > floor(b W / n)), so that the heavier W
+    // blocks do not all run first: 1-2% faster than W first on the MLP
+    // operand pairs
+    const int64_t n = (int64_t)a.w_blocks + a.x_blocks;
+    const int32_t wb = (int32_t)((int64_t)b * a.w_blocks / n);
+    if ((int32_t)(((int64_t)b + 1) * a.w_blocks / n) > wb)
         block2d_body<false, false, false>(a.w, a.w_rows, a.cols, a.ld_w, a.qw, a.ld_qw, nullptr, 0, a.sw, a.nbr, a.nbc,
-                                          b % a.nbc, b / a.nbc, 0);
+                                          wb % a.nbc, wb / a.nbc, 0);
     else
-        rowgroup_body<false, false, ROW_FAST, 4, false, false>(a.x, b - a.w_blocks, a.x_blocks);
+        rowgroup_body<false, false, ROW_FAST, 4, false, false>(a.x, b - wb, a.x_blocks);
 }
 
 __global__ void __launch_bounds__(kThreads) k_e4m3_encode(const float* __restrict__ in, uint8_t* __restrict__ out,
