@@ -524,6 +524,53 @@ __device__ __forceinline__ float block_max(float m, float* red) {
     return m;
 }
 
+// Rows of at most 64 R chunks of 8 values: one wave per row (4 rows per
+// workgroup) and the row held in registers: R loads per lane issued
+// together, the maximum by wave shuffles, then the codes from the registers.
+// No LDS, no barrier, one HBM read.
+template <int R>
+__global__ void __launch_bounds__(kThreads) k_quant_rowwise_wave(const uint16_t* __restrict__ x, int32_t rows,
+                                                                 int32_t cols, int64_t ld_x, uint8_t* __restrict__ q,
+                                                                 int64_t ld_q, float* __restrict__ s) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (r >= rows) return;                  // whole waves: nothing below needs other waves
+    const uint16_t* xr = x + r * ld_x;
+    uint8_t* qr = q + r * ld_q;
+    const int nch = cols / 8;
+    uint4 raw[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int c = lane + 64 * i;
+        raw[i] = make_uint4(0, 0, 0, 0);
+        if (c < nch) raw[i] = *reinterpret_cast<const uint4*>(xr + 8 * c);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        float v[8];
+        unpack8(raw[i], v);
+        m = fmaxf(m, absmax8(v));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float sc = m / kE4M3Max;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+            float v[8];
+            unpack8(raw[i], v);
+            uint32_t w0, w1;
+            encode8(v, sc, w0, w1);
+            *reinterpret_cast<uint2*>(qr + 8 * c) = make_uint2(w0, w1);
+        }
+    }
+    if (lane == 0) s[r] = sc;
+}
+
+// Longer rows: one workgroup per row, two passes over the row (the second
+// served by the cache).
 __global__ void __launch_bounds__(kThreads) k_quant_rowwise(const uint16_t* __restrict__ x, int32_t cols, int64_t ld_x,
                                                             uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ s) {
     __shared__ float red[kThreads / 64];
@@ -551,24 +598,43 @@ __global__ void __launch_bounds__(kThreads) k_quant_rowwise(const uint16_t* __re
 
 __global__ void k_fill_zero(float* s) { s[0] = 0.0f; }
 
+// WIDE: chunk indices past 2^32 (64-bit division per chunk; 32-bit otherwise)
+template <bool WIDE>
 __global__ void __launch_bounds__(kThreads) k_tensor_amax(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
                                                           int64_t ld_x, float* s) {
+    // each thread takes 8 chunks of 8 values per trip, all loads issued
+    // before the maxima; few workgroups (one atomic each on the scale cell)
+    constexpr int U = 8;
     __shared__ float red[kThreads / 64];
-    const int nch = cols / 8;
+    const uint32_t nch = (uint32_t)cols / 8;
     const int64_t total = (int64_t)rows * nch;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
     float m = 0.0f;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
-        const int64_t r = i / nch, c = i - r * nch;
-        float v[8];
-        unpack8(*reinterpret_cast<const uint4*>(x + r * ld_x + 8 * c), v);
-        m = fmaxf(m, absmax8(v));
+    for (int64_t base = (int64_t)blockIdx.x * kThreads + threadIdx.x; base < total; base += stride * U) {
+        uint4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * stride;
+            raw[u] = make_uint4(0, 0, 0, 0);
+            if (i < total) {
+                int64_t r, c;
+                if (WIDE) { r = i / nch; c = i - r * nch; }
+                else { const uint32_t i32 = (uint32_t)i, r32 = i32 / nch; r = r32; c = i32 - r32 * nch; }
+                raw[u] = *reinterpret_cast<const uint4*>(x + r * ld_x + 8 * c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[8];
+            unpack8(raw[u], v);
+            m = fmaxf(m, absmax8(v));
+        }
     }
     m = block_max(m, red);
     // fl(m / 448) is monotone in m, so the maximum of the blocks' scales is
     // the scale of the tensor's amax; non-negative floats order as their bits
     if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(s), __float_as_uint(m / kE4M3Max));
 }
-
 __global__ void __launch_bounds__(kThreads) k_tensor_encode(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
                                                             int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
                                                             const float* s) {
@@ -710,7 +776,16 @@ hipError_t launch_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, in
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,
                                 float* s, hipStream_t st) {
     if (rows == 0) return hipSuccess;                 // cols == 0: every scale 0
-    hipLaunchKernelGGL(k_quant_rowwise, dim3((unsigned)rows), dim3(kThreads), 0, st, x, (int32_t)cols, ld_x, q, ld_q, s);
+    const int64_t nch = cols / 8;
+    const dim3 wgrid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64)));
+    auto wave = [&](auto kern) {
+        hipLaunchKernelGGL(kern, wgrid, dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, q, ld_q, s);
+    };
+    if (nch <= 64 * 2) wave(k_quant_rowwise_wave<2>);
+    else if (nch <= 64 * 4) wave(k_quant_rowwise_wave<4>);
+    else if (nch <= 64 * 8) wave(k_quant_rowwise_wave<8>);
+    else if (nch <= 64 * 16) wave(k_quant_rowwise_wave<16>);
+    else hipLaunchKernelGGL(k_quant_rowwise, dim3((unsigned)rows), dim3(kThreads), 0, st, x, (int32_t)cols, ld_x, q, ld_q, s);
     return hipGetLastError();
 }
 
@@ -721,10 +796,16 @@ hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols
         return hipGetLastError();
     }
     const int64_t chunks = rows * (cols / 8);
-    int64_t blocks = (chunks + kThreads * 4 - 1) / (kThreads * 4);
-    if (blocks > 256 * 8) blocks = 256 * 8;
+    int64_t blocks = (chunks + kThreads * 8 - 1) / (kThreads * 8);
+    if (blocks > 256 * 2) blocks = 256 * 2;
     hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(1), 0, st, s);
-    hipLaunchKernelGGL(k_tensor_amax, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols, ld_x, s);
+    // 32-bit chunk indices when every index of the grid-stride loop fits
+    if (chunks + (int64_t)blocks * kThreads * 8 < ((int64_t)1 << 32))
+        hipLaunchKernelGGL(k_tensor_amax<false>, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, (int32_t)rows,
+                           (int32_t)cols, ld_x, s);
+    else
+        hipLaunchKernelGGL(k_tensor_amax<true>, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, (int32_t)rows,
+                           (int32_t)cols, ld_x, s);
     int64_t eblocks = (chunks + kThreads - 1) / kThreads;
     if (eblocks > 256 * 64) eblocks = 256 * 64;
     hipLaunchKernelGGL(k_tensor_encode, dim3((unsigned)eblocks), dim3(kThreads), 0, st, x, (int32_t)rows, (int32_t)cols,

@@ -46,8 +46,12 @@ def _same_scales(s_gpu, s_ref):
 
 
 # -------------------------------------------------------------- quantizers
-@pytest.mark.parametrize("shape", [(256, 512), (7, 264), (1, 8), (300, 1000), (64, 7168), (3, 40000)])
+@pytest.mark.parametrize("shape", [(256, 512), (7, 264), (1, 8), (300, 1000), (50, 2048), (513, 2560),
+                                   (21, 4104), (64, 7168), (3, 40000)])
 def test_rowwise_quant(shape):
+    """One wave per row with the row in registers up to 8192 columns (2, 4, 8
+    or 16 chunks per lane: each size and each boundary), one workgroup and
+    two passes beyond."""
     _say("rowwise", shape)
     x = _bits(shape, 11)
     q, s = ops.quant_rowwise(dev_bf16(x))
@@ -78,7 +82,7 @@ def test_rowwise_special_rows_and_stride():
     _same_scales(s, sr)
 
 
-@pytest.mark.parametrize("shape", [(256, 512), (7, 264), (1, 8), (4096, 7168), (10001, 136)])
+@pytest.mark.parametrize("shape", [(256, 512), (7, 264), (1, 8), (4096, 7168), (10001, 136), (4096, 2560)])
 def test_tensorwise_quant(shape):
     """Sizes from one workgroup to more than the amax grid (many atomics)."""
     _say("tensorwise", shape)
