@@ -60,7 +60,9 @@ __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
 }
 
 // Quotient x / s rounded to nearest fp32, given y = RN(1 / s) and s >= 2^-80:
-// q0 = RN(x y), r = RN(x - s q0) (one FMA), q = RN(q0 + r y) (one FMA).  For
+// q0 = RN(x y), r = RN(x - s q0) (one FMA), q = RN(q0 + r y) (one FMA) --
+// Markstein's correction step for a quotient from a correctly rounded
+// reciprocal.  For
 // binary32 operands whose significands are those of bf16 values (x) and of
 // RN(bf16 / 448) (s), this sequence returns exactly RN(x / s): the rounding
 // depends only on the two significands when nothing under- or overflows,

@@ -317,14 +317,12 @@ def test_moe_blockwise_chain_skewed_routing(moe, blockwise_weights):
     _blockwise_chain(moe, r, 40, check_down=True, weights=blockwise_weights, name="moe_blockwise_skewed")
 
 
-def test_moe_mxfp8_chain_full_size(moe):
-    d, r = moe, moe["routing"]
-    rows, G = r.row_token.size, r.offsets.size - 1
-    offs = dev(r.offsets)
-    x = dev_bf16(d["x"])
-    qx, sx = ops.mx_quant(x)
-    torch.cuda.synchronize()
-    _check_rows_mx(d["x"], qx, sx, np.random.default_rng(50).integers(0, x.shape[0], 64))
+@pytest.fixture(scope="module")
+def mx_weights(moe):
+    """The MoE layer's expert weights in 1x32 MX blocks along K (gate/up by
+    rows of W_gu, down through its transpose), rows of the first and last
+    expert checked bit-exact."""
+    d = moe
     wgu = dev_bf16(d["w_gu"])
     qgu, sgu = ops.mx_quant(wgu.view(E * 2 * INTER, HID))
     del wgu
@@ -336,6 +334,17 @@ def test_moe_mxfp8_chain_full_size(moe):
         _check_rows_mx(np.ascontiguousarray(d["w_d"][e].T), qdt[e * HID:(e + 1) * HID], sdt[e * HID:(e + 1) * HID],
                        np.arange(HID))
     del wdt
+    return {"qgu": qgu, "sgu": sgu, "qdt": qdt, "sdt": sdt}
+
+
+def _mx_chain(d, r, mxw, seed, name):
+    rows, G = r.row_token.size, r.offsets.size - 1
+    offs = dev(r.offsets)
+    qgu, sgu, qdt, sdt = mxw["qgu"], mxw["sgu"], mxw["qdt"], mxw["sdt"]
+    x = dev_bf16(d["x"])
+    qx, sx = ops.mx_quant(x)
+    torch.cuda.synchronize()
+    _check_rows_mx(d["x"], qx, sx, np.random.default_rng(seed).integers(0, x.shape[0], 64))
 
     def mx_grouped(N, K, a_rows, a_count, a, sa, b, sb, out_dtype):
         c = torch.empty((rows, N), dtype=out_dtype, device="cuda")
@@ -347,30 +356,43 @@ def test_moe_mxfp8_chain_full_size(moe):
     gu16 = mx_grouped(2 * INTER, HID, a_rows, x.shape[0], qx, sx, qgu, sgu, torch.bfloat16)
     gu32 = mx_grouped(2 * INTER, HID, a_rows, x.shape[0], qx, sx, qgu, sgu, torch.float32)
     torch.cuda.synchronize()
-    groups = _sample_groups(r.offsets, 51)
+    groups = _sample_groups(r.offsets, seed + 1)
     qx_h, sx_h = host(qx), host(sx)
     n_gu = 2 * INTER
-    _check_grouped(r.offsets, groups, 52, gu16, gu32,
+    _check_grouped(r.offsets, groups, seed + 2, gu16, gu32,
                    lambda g, r0, r1: (qx_h[r.row_token[r0:r1]], sx_h[r.row_token[r0:r1]],
                                       host(qgu[g * n_gu:(g + 1) * n_gu]), host(sgu[g * n_gu:(g + 1) * n_gu])),
-                   mx=True, record="moe_mxfp8_gate_up")
+                   mx=True, record=name + "_gate_up")
     del gu32
     qh = torch.empty((rows, INTER), dtype=torch.uint8, device="cuda")
     sh = torch.empty((rows, INTER // 32), dtype=torch.uint8, device="cuda")
     h = torch.empty((rows, INTER), dtype=torch.bfloat16, device="cuda")
     ops.fp8_silu_mul_quant(gu16, rows, INTER, 2 * INTER, 1, qh, INTER, sh, INTER // 32, 1, h, INTER)
     torch.cuda.synchronize()
-    _check_h(gu16, h, qh, sh, np.random.default_rng(53).integers(0, rows, 256), mx=True)
+    _check_h(gu16, h, qh, sh, np.random.default_rng(seed + 3).integers(0, rows, 256), mx=True)
     _fused_mx_gate_up_matches(rows, G, offs, a_rows, x.shape[0], qx, sx, qgu.view(E, 2 * INTER, HID),
                               sgu.view(E, 2 * INTER, HID // 32), qh, sh)
     dn16 = mx_grouped(HID, INTER, None, rows, qh, sh, qdt, sdt, torch.bfloat16)
     dn32 = mx_grouped(HID, INTER, None, rows, qh, sh, qdt, sdt, torch.float32)
     torch.cuda.synchronize()
     qh_h, sh_h = host(qh), host(sh)
-    _check_grouped(r.offsets, groups, 54, dn16, dn32,
+    _check_grouped(r.offsets, groups, seed + 4, dn16, dn32,
                    lambda g, r0, r1: (qh_h[r0:r1], sh_h[r0:r1], host(qdt[g * HID:(g + 1) * HID]),
                                       host(sdt[g * HID:(g + 1) * HID])),
-                   mx=True, record="moe_mxfp8_down")
+                   mx=True, record=name + "_down")
+
+
+def test_moe_mxfp8_chain_full_size(moe, mx_weights):
+    _mx_chain(moe, moe["routing"], mx_weights, 50, "moe_mxfp8")
+
+
+def test_moe_mxfp8_chain_skewed_routing(moe, mx_weights):
+    """The MXFP8 chain on the parity-only skewed routing (8 empty experts,
+    group sizes from tens to thousands, not multiples of 128)."""
+    r = moe["routing_skewed"]
+    sizes = np.diff(r.offsets)
+    assert np.sum(sizes == 0) == 8 and np.any(sizes % 128 != 0)
+    _mx_chain(moe, r, mx_weights, 60, "moe_mxfp8_skewed")
 
 
 # ------------------------------------------------------------------ combine
