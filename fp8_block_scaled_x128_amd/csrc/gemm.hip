@@ -565,8 +565,14 @@ k_gemm(KArgs p) {
     // block, so the sched_barrier below really bounds the scheduler (with a
     // branch per copy the compiler sank every matrix instruction below all
     // fragment reads).
-    auto step = [&](int kb, auto ca_tag, auto cb_tag) {
+    // ACT (compile time): the wave has rows of the tile inside the matrix
+    // (or its group).  A wave without any issues only its share of the
+    // copies and meets the barriers: on a ragged last tile of a group the
+    // waves of the empty half then leave their SIMDs' matrix units to the
+    // waves that have rows.
+    auto step = [&](int kb, auto ca_tag, auto cb_tag, auto act_tag) {
         constexpr bool CA = decltype(ca_tag)::value, CB = decltype(cb_tag)::value;
+        constexpr bool ACT = decltype(act_tag)::value;
         // Wait for this wave's copies of slice kb (scale copies were issued
         // before the tile copies of their step, so counting tile copies only
         // is conservative).
@@ -587,19 +593,21 @@ k_gemm(KArgs p) {
         const uint32_t tA = abuf(kb % C::kAStages);
 
         v8i fa[4];
-        const FragOff ab = frag_base(tA + wm * 64 * BK, fo);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) fa[mt] = read_frag(ab, mt * 16 * BK);
-        // activation-side scales of the wave's 4 m-tiles (bytes in MX mode)
-        const uint32_t sa_lds = opaque(tA + BM * BK + (wm * 64 + r16) * 4);
         int mxa[4];
         float sam[4];
+        if constexpr (ACT) {
+            const FragOff ab = frag_base(tA + wm * 64 * BK, fo);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
-            else if (MODE == MODE_P2) mxa[mt] = lds_readu8(sa_lds + mt * 64 + (kb & 3));
-            else if (MODE == MODE_KINV) mxa[mt] = 0;    // constant 0: the plain (unscaled) instruction, see mfma_unit
-            else sam[mt] = lds_readf(sa_lds + mt * 64);
+            for (int mt = 0; mt < 4; ++mt) fa[mt] = read_frag(ab, mt * 16 * BK);
+            // activation-side scales of the wave's 4 m-tiles (bytes in MX mode)
+            const uint32_t sa_lds = opaque(tA + BM * BK + (wm * 64 + r16) * 4);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
+                else if (MODE == MODE_P2) mxa[mt] = lds_readu8(sa_lds + mt * 64 + (kb & 3));
+                else if (MODE == MODE_KINV) mxa[mt] = 0;    // constant 0: the plain (unscaled) instruction, see mfma_unit
+                else sam[mt] = lds_readf(sa_lds + mt * 64);
+            }
         }
         if (C::kABarrier) {
             // Every wave has its activation fragments and scales in
@@ -619,7 +627,10 @@ k_gemm(KArgs p) {
                 if (CB && C::b_slot(t) == nt) copy_b(b_kb, cst, t);
         };
 
-        if (MODE == MODE_MX || MODE == MODE_KINV || MODE == MODE_P2) {
+        if constexpr (!ACT) {
+#pragma unroll
+            for (int nt = 0; nt < NF; ++nt) copy_step(nt);
+        } else if (MODE == MODE_MX || MODE == MODE_KINV || MODE == MODE_P2) {
             const uint32_t sb8 = opaque(tB + BN * BK + (wn * 16 * NF + r16) * 4 + q);
             // P2: the tile's two 128-row weight blocks, byte kb % 4 of each
             // block's copied word (chosen per n-tile as in BLOCK128)
@@ -722,19 +733,25 @@ k_gemm(KArgs p) {
     for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    int kb = 0;
-    for (; kb + C::kLeadMax < nk; ++kb) step(kb, std::true_type{}, std::true_type{});
-    // At most kLeadMax (<= 2) steps remain.  With unequal leads the next to
-    // last step still copies the side with the longer lead; the last step
-    // copies nothing.
-    if constexpr (C::kLeadA != C::kLeadB) {
-        if (kb + 2 == nk) {
-            step(kb, std::integral_constant<bool, (C::kLeadA < C::kLeadB)>{},
-                 std::integral_constant<bool, (C::kLeadB < C::kLeadA)>{});
-            ++kb;
+    auto kloop = [&](auto act_tag) {
+        int kb = 0;
+        for (; kb + C::kLeadMax < nk; ++kb) step(kb, std::true_type{}, std::true_type{}, act_tag);
+        // At most kLeadMax (<= 2) steps remain.  With unequal leads the next to
+        // last step still copies the side with the longer lead; the last step
+        // copies nothing.
+        if constexpr (C::kLeadA != C::kLeadB) {
+            if (kb + 2 == nk) {
+                step(kb, std::integral_constant<bool, (C::kLeadA < C::kLeadB)>{},
+                     std::integral_constant<bool, (C::kLeadB < C::kLeadA)>{}, act_tag);
+                ++kb;
+            }
         }
-    }
-    for (; kb < nk; ++kb) step(kb, std::false_type{}, std::false_type{});
+        for (; kb < nk; ++kb) step(kb, std::false_type{}, std::false_type{}, act_tag);
+    };
+    // grouped: the last row tile of a group is ragged (wave-uniform test:
+    // m_begin, m_end and wm are); dense tiles keep the one loop
+    if (!GROUPED || m_begin + wm * 64 < m_end) kloop(std::true_type{});
+    else kloop(std::false_type{});
 
     // Grouped: take the next work item; its first copies go out in the
     // middle of this item's epilogue.  The barrier (LDS only: every wave has
