@@ -569,7 +569,10 @@ def main():
     # ms per step); the per-kernel times come from a second pass.  Running
     # each weight quantization on a second stream next to the activation
     # quantization was measured slower (0.305 ms per step): the concurrent
-    # quantizers share HBM and the cross-stream waits add latency.
+    # quantizers share HBM and the cross-stream waits add latency.  So was
+    # quantizing W_down on a second stream from the start of GEMM up (it does
+    # not depend on it), with X_down alone on this stream: 267-272 against
+    # 262-264 us per step with inputs rotated past the last-level cache.
     main_h = stream.cuda_stream
 
     def step(i, only=None, events=None):
