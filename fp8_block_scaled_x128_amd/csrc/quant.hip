@@ -136,9 +136,11 @@ __global__ void __launch_bounds__(kThreads) k_rowgroup(RowArgs p) {
 
 template <bool SILU, bool MX, bool P2 = false>
 hipError_t launch_rowgroup(RowArgs p, bool row_fast, hipStream_t st) {
-    // SILU: three runs per trip (its exact path keeps 91 registers live with
-    // three, 105 with four: 5 against 4 waves per SIMD, 2-3% faster)
-    constexpr int U = SILU ? 3 : 4;
+    // Runs per trip, measured with inputs rotated past the last-level cache:
+    // SILU three (its exact path keeps 91 registers live with three, 105
+    // with four: 5 against 4 waves per SIMD, 2-3% faster); 1x128 two (2-3%
+    // faster than four, six and eight were slower); MX four (two: 4% slower)
+    constexpr int U = SILU ? 3 : MX ? 4 : 2;
     if (p.total_runs == 0) return hipSuccess;
     const int64_t rows16 = ((int64_t)p.total_runs + U - 1) / U;            // 16-lane rows needed
     int64_t blocks = (rows16 + (kThreads / 16) - 1) / (kThreads / 16);
