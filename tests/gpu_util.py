@@ -203,7 +203,7 @@ def sample_indices(M, N, count, seed):
 def verify(qa, sa, qb, sb, y32, y16=None, bscale_row=False, mi=None, ni=None, mx=False, record=None):
     """Check GPU outputs (full matrices, or the entries (mi, ni)) against the
     oracle and against the datapath truncation model.  `record` names the
-    case in gpurun_out/gemm_rel_errors.jsonl."""
+    case in the error log that record_rel_error writes."""
     M, N = qa.shape[0], qb.shape[0]
     if mi is None:
         mi, ni = (g.reshape(-1) for g in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
