@@ -341,7 +341,7 @@ fp8bs_status mxfp8_grouped_gemm_swiglu_quant(int64_t total_rows, int64_t I, int6
  * ld_h >= I if h_out.
  * h is bit-exact against g / (1 + exp(-g)) * u evaluated in fp64 and
  * rounded once to bf16, for every finite bf16 g and u: an fp32 evaluation
- * (hardware exp2 and reciprocal, within 4.03 fp32 ulps of the exact value)
+ * (hardware exp2 and reciprocal, within 3.72 fp32 ulps of the exact value)
  * rounds it wherever it lies farther than 5 fp32 ulps from a bf16 rounding
  * midpoint, and an fp64 evaluation decides the rest (about 2^-12 of the
  * values at GEMM-output magnitudes, and every g below -44).
