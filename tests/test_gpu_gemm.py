@@ -363,6 +363,37 @@ def test_grouped_exact_integer_case_256x256_tiles():
     assert np.array_equal(ch16, oracle.f64_to_bf16(ch.astype(np.float64)))
 
 
+def test_grouped_exact_integer_case_256x256_tiles_many_groups():
+    """The 256 x 256 persistent configuration with 200 groups (the work-item
+    lookup walks the offsets in chunks of 128 groups), 30% of them empty and
+    the rest ragged (each group's last row tile runs with its empty waves
+    idle): sampled outputs of every group bit-exact, launches repeatable."""
+    rng = np.random.default_rng(21)
+    G, N, K = 200, 1024, 256
+    counts = np.where(rng.random(G) < 0.3, 0, rng.integers(1, 600, G))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    qa, sa, _, _ = _exact_case(rows, 128, K, 22)
+    qbs, sbs = zip(*[_exact_case(128, N, K, 3000 + g)[2:] for g in range(G)])
+    qb, sb = np.stack(qbs), np.stack(sbs)
+    dqa, dsa, dqb, dsb, doffs = dev(qa), dev(sa), dev(qb), dev(sb), dev(offsets)
+    _say("grouped 256x256, %d groups, %d rows" % (G, rows))
+
+    def run(out):
+        dt = torch.float32 if out == ops.OUT_FP32 else torch.bfloat16
+        c = torch.full((rows, N), float("nan"), dtype=dt, device="cuda")
+        ops.fp8_grouped_gemm(rows, N, K, G, doffs, None, rows, dqa, K, dsa, dsa.stride(0), dsa.stride(1),
+                             dqb, K, N * K, dsb, dsb.stride(0), dsb.stride(1), dsb.stride(2), c, N, out)
+        return c
+
+    ch, ch16 = _twice_bitwise(run)
+    for g, (mi, ni) in _group_samples(offsets, N, 23, per_group=6).items():
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        yref, _ = oracle.gemm_blockscaled_sampled(qa[r0:r1], sa[r0:r1], qb[g], sb[g], mi, ni)
+        assert np.array_equal(ch[r0:r1][mi, ni].astype(np.float64), yref), "group %d" % g
+    assert np.array_equal(ch16, oracle.f64_to_bf16(ch.astype(np.float64)))
+
+
 def _twice_bitwise(run):
     """Run a GEMM launcher twice per output type on the same inputs; the two
     results must be identical bytes (an LDS-pipeline race shows up as a
