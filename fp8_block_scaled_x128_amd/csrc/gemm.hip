@@ -97,12 +97,13 @@ struct Cfg {
     static constexpr int BN = 16 * NF * WN;
     static constexpr int BM = 64 * (WAVES / WN);
     static constexpr bool kDefer = true;
-    // Workgroups resident per compute unit.  A 4-wave tile with one wave
-    // column (WN = 1) is sized for two per CU: each SIMD then runs two waves
-    // of different workgroups, so one workgroup's barriers, fragment reads,
-    // pipeline fill and output writes overlap the other's matrix work (the
-    // two waves of a SIMD in an 8-wave workgroup meet the same barriers).
-    static constexpr int kPerCU = WN == 1 ? 2 : 1;
+    // Workgroups resident per compute unit.  The 4-wave tiles with one wave
+    // column (WN = 1, 128 x 256) and the 4-wave 160 x 128 tile are sized for
+    // two per CU: each SIMD then runs two waves of different workgroups, so
+    // one workgroup's barriers, fragment reads, pipeline fill and output
+    // writes overlap the other's matrix work (the two waves of a SIMD in an
+    // 8-wave workgroup meet the same barriers).
+    static constexpr int kPerCU = (WN == 1 || (WAVES == 4 && NF == 5 && WN == 2)) ? 2 : 1;
     static constexpr int kMinWavesPerEU = kPerCU * WAVES / 4;
     static constexpr int kLdsMax = 160 * 1024 / kPerCU;
     // Measured on the MLP shapes (M 4096; N 9728, K 2560 and N 2560, K 9728):
@@ -992,22 +993,26 @@ int waves_for(int64_t rows, int64_t N, int64_t extra_tiles = 0) {
 // 160 of 256 x 256 for 256 CUs, against 256 tiles of 160 x 256).  The
 // estimate per region is rounds x (K slices x cycles per slice + cycles per
 // tile), with the cycle figures fitted to the MLP shapes (M 4096; N 9728,
-// K 2560; N 2560, K 9728; and M 9728, N 2560, K 4096).  For the 128 x 256
-// tile a round is two tiles per CU; a last round of at most one tile per CU
-// runs each tile at its lone speed, only about 12% faster per slice (a lone
-// 4-wave workgroup leaves each SIMD one wave, so pairs nearly double the
-// throughput).
+// K 2560; N 2560, K 9728; and M 9728, N 2560, K 4096).  For the tiles sized
+// two per CU a round is two tiles per CU; a last round of at most one tile
+// per CU runs each tile at its lone speed (128 x 256: only about 12% faster
+// per slice, as a lone 4-wave workgroup leaves each SIMD one wave).  The
+// 160 x 128 pair is ~8% faster per slice than one 160 x 256 tile but costs
+// ~4.7 us more per tile (K 9728 against K 4096, M 4096, N 2560): it wins
+// with long K and full rounds (the down projection and dgrad), and its lone
+// figure is the 192 x 128 tile's scaled by their measured ratio.
 struct TileCfg {
-    int waves, nf, wn;
-    double slice_cycles, tile_cycles;   // per round of tiles (wn = 1: two tiles per CU)
-    double lone_slice_cycles;           // wn = 1: one tile on the CU
+    int waves, nf, wn, per_cu;
+    double slice_cycles, tile_cycles;   // per round of tiles (per_cu = 2: two tiles per CU)
+    double lone_slice_cycles;           // per_cu = 2: one tile on the CU
 };
 constexpr TileCfg kDenseCfgs[] = {
-    {8, 8, 2, 3300, 9000, 0},       // 256 x 256
-    {4, 8, 2, 2450, 7000, 0},       // 256 x 128
-    {8, 5, 2, 2520, 8000, 0},       // 160 x 256
-    {4, 6, 2, 2400, 6000, 0},       // 192 x 128
-    {4, 8, 1, 3100, 8000, 2700},    // 128 x 256, two per CU
+    {8, 8, 2, 1, 3300, 9000, 0},       // 256 x 256
+    {4, 8, 2, 1, 2450, 7000, 0},       // 256 x 128
+    {8, 5, 2, 1, 2520, 8000, 0},       // 160 x 256
+    {4, 6, 2, 1, 2400, 6000, 0},       // 192 x 128
+    {4, 8, 1, 2, 3100, 8000, 2700},    // 128 x 256, two per CU
+    {4, 5, 2, 2, 2324, 18400, 2750},   // 160 x 128, two per CU
 };
 // A second launch on the stream: its ramp-up and the first region's tail.
 constexpr double kLaunchCycles = 15000;
@@ -1019,7 +1024,7 @@ double region_cycles(const TileCfg& c, int64_t M, int64_t N, int64_t nk) {
     const int64_t bm = cfg_bm(c), bn = cfg_bn(c);
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     const double round = (double)nk * c.slice_cycles + c.tile_cycles;
-    if (c.wn != 1) return (double)((tiles + kCUs - 1) / kCUs) * round;
+    if (c.per_cu != 2) return (double)((tiles + kCUs - 1) / kCUs) * round;
     const int64_t full = tiles / (2 * kCUs), rest = tiles % (2 * kCUs);
     const double last = rest == 0 ? 0.0 : rest <= kCUs ? (double)nk * c.lone_slice_cycles + c.tile_cycles : round;
     return (double)full * round + last;
@@ -1060,7 +1065,8 @@ hipError_t launch_dense(int ci, const KArgs& p, bool out_f32, hipStream_t st) {
         case 1: return launch<MODE, false, 4, 8>(p, out_f32, st);
         case 2: return launch<MODE, false, 8, 5>(p, out_f32, st);
         case 3: return launch<MODE, false, 4, 6>(p, out_f32, st);
-        default: return launch<MODE, false, 4, 8, 1>(p, out_f32, st);
+        case 4: return launch<MODE, false, 4, 8, 1>(p, out_f32, st);
+        default: return launch<MODE, false, 4, 5, 2>(p, out_f32, st);
     }
 }
 

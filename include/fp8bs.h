@@ -214,7 +214,8 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
  *                     tiling covers all columns (then plan[4] == N);
  *   a tile covers 32 * waves activation rows (m), except the tile of 128
  *   weight rows (4 waves, two workgroups per compute unit), which covers
- *   256.
+ *   256.  The 4-wave tile of 160 weight rows also runs two workgroups per
+ *   compute unit.
  * Requirements: M, N, K >= 0; K % 128 == 0; N % 128 == 0.
  * ------------------------------------------------------------------------ */
 fp8bs_status fp8_blockscaled_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t* plan);

@@ -156,7 +156,7 @@ def test_dense_tile_plan(lib):
     every region's tiling is one the library builds, and the MLP shapes get
     tilings that fill whole rounds of 256 compute units."""
     from fp8_block_scaled_x128_amd import ops
-    tilings = {(8, 256), (4, 256), (8, 160), (4, 192), (4, 128)}
+    tilings = {(8, 256), (4, 256), (8, 160), (4, 192), (4, 128), (4, 160)}
     for M in (1, 130, 1000, 4096, 4100, 16384):
         for N in (128, 640, 1408, 2560, 4096, 9728):
             for K in (128, 2560, 9728):
@@ -167,9 +167,11 @@ def test_dense_tile_plan(lib):
                 else:
                     assert second in tilings and second != first
                     assert 0 < split < N and split % 128 == 0 and split % first[1] == 0
-    # down projection: 16 x 16 tiles of 160 x 256; up projection and wgrad:
-    # 128 x 256 tiles, two per compute unit
-    assert ops.fp8_blockscaled_gemm_plan(4096, 2560, 9728) == ((8, 160), None, 2560)
+    # down projection (and dgrad): 32 x 16 tiles of 160 x 128, two per
+    # compute unit (one round); up projection and wgrad: 128 x 256 tiles, two
+    # per compute unit; K 4096 at the down projection's M and N: 160 x 256
+    assert ops.fp8_blockscaled_gemm_plan(4096, 2560, 9728) == ((4, 160), None, 2560)
+    assert ops.fp8_blockscaled_gemm_plan(4096, 2560, 4096) == ((8, 160), None, 2560)
     assert ops.fp8_blockscaled_gemm_plan(4096, 9728, 2560) == ((4, 128), None, 9728)
     assert ops.fp8_blockscaled_gemm_plan(9728, 2560, 4096) == ((4, 128), None, 2560)
     assert lib.fp8_blockscaled_gemm_plan(128, 100, 128, ctypes.c_void_p(1 << 20)) == 2

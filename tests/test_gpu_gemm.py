@@ -103,6 +103,7 @@ PLAN_CASES = [
     ((3200, 10112, 2048), ((4, 256), (4, 128), 5120)),
     ((2816, 9344, 4096), ((4, 128), (8, 160), 5760)),
     ((1664, 14464, 4096), ((8, 160), (4, 128), 5120)),
+    ((4000, 2432, 6912), ((4, 160), None, 2432)),
 ]
 
 
