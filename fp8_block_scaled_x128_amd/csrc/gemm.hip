@@ -110,8 +110,8 @@ struct Cfg {
     // 256x256 tile: 3 weight stages + 1 activation buffer with the second
     // barrier beats 2 + 2 without it (equal on the first shape, 9% faster on
     // the second); 256x128 tile: 3 + 2 without the second barrier is 2-3%
-    // faster than with it.  Two workgroups per CU leave room for 2 weight
-    // stages and 1 activation buffer.
+    // faster than with it.  Two workgroups per CU leave each room for 2
+    // weight stages and 1 activation buffer (128 x 256) or 2 (160 x 128).
     static constexpr int kBStages = kPerCU == 2 ? 2 : 3;
     static constexpr int kBStageBytes = BN * BK + (ROWSC ? (BN + 63) / 64 * 64 : BN) * 4;   // weight tile + scales
     static constexpr int kABufBytes = BM * BK + BM * 4;     // activation tile + activation scales
