@@ -399,3 +399,75 @@ def test_moe_combine_padded(out):
     _say("combine padded", out)
     ops.fp8_moe_combine(ydv, rows, H, ld_y, dev(pos), dev(w), T, k, o, ld_out, out)
     _check_c(o, T, H, ref, out)
+
+
+@pytest.mark.parametrize("mx", [0, 1])
+def test_fused_gate_up_padded_gather(mx):
+    """The gate/up GEMM with SiLU*mul and the quantization of h in its
+    epilogue (FP32 1x128 scales, or UE8M0 1x32), reading its activation rows
+    through the dispatch gather from a padded buffer, expert weights with
+    padded rows and expert stride, and writing h codes and scales through
+    padded layouts.  Against the oracle chain: the exact grouped GEMM,
+    rounded to bf16, SiLU*mul, then the quantization of h."""
+    T, K, I, G = 120, 256, 128, 3
+    N2, lda, ldb, ld_hq = 2 * I, 272, 288, 144
+    offsets = np.array([0, 90, 90, 200], np.int32)
+    rows = int(offsets[-1])
+    rng = np.random.default_rng(27 + mx)
+    a_rows = rng.integers(0, T, size=rows).astype(np.int32)
+    qx = _ints((T, K), rng)
+    qgu = np.stack([_ints((N2, K), rng) for _ in range(G)])
+    _, av = _padded(qx, lda, NAN_E4M3)
+    b_stride_g = (N2 + 1) * ldb
+    bbuf = np.full((G * (N2 + 1) + 1, ldb), NAN_E4M3, np.uint8)
+    for g in range(G):
+        bbuf[g * (N2 + 1):g * (N2 + 1) + N2, :K] = qgu[g]
+    qa_g = qx[a_rows]
+    y = np.zeros((rows, N2))
+    if mx:
+        lds_a, lds_b = K // 32 + 4, K // 32 + 8
+        ea = rng.integers(126, 129, size=(T, K // 32)).astype(np.uint8)
+        eb = rng.integers(126, 129, size=(G, N2, K // 32)).astype(np.uint8)
+        _, sav = _padded(ea, lds_a, 0xFF)
+        sb_g = N2 * lds_b + 16
+        sbuf = np.full(G * sb_g + 16, 0xFF, np.uint8)
+        for g in range(G):
+            sbuf[g * sb_g + _grid(N2, K // 32, lds_b, 1)] = eb[g]
+        for g in range(G):
+            r0, r1 = int(offsets[g]), int(offsets[g + 1])
+            if r1 > r0:
+                y[r0:r1], _ = oracle.gemm_mx(qa_g[r0:r1], ea[a_rows[r0:r1]], qgu[g], eb[g])
+    else:
+        nkb, nb = K // 128, N2 // 128
+        sx = np.exp2(rng.integers(-1, 2, size=(T, nkb))).astype(np.float32)
+        sgu = np.exp2(rng.integers(-1, 2, size=(G, nb, nkb))).astype(np.float32)
+        sa_m, sa_k = nkb + 2, 1                                  # K-major, padded
+        sb_g, sb_n, sb_k = nb * nkb + 5, nkb + 1, 1
+        sa_buf = np.full(T * sa_m + 4, np.nan, np.float32)
+        sa_buf[_grid(T, nkb, sa_m, sa_k)] = sx
+        sb_buf = np.full(G * sb_g + 4, np.nan, np.float32)
+        for g in range(G):
+            sb_buf[g * sb_g + _grid(nb, nkb, sb_n, sb_k)] = sgu[g]
+        y, _ = oracle.grouped_gemm_blockscaled(qa_g, sx[a_rows], offsets, qgu, sgu)
+    h = oracle.silu_mul(oracle.f64_to_bf16(y))
+    qr, sr = oracle.mx_quant_1x32(h) if mx else oracle.quant_1x128(h)
+    groups = I // (32 if mx else 128)
+    hq = _out_u8(rows, ld_hq)
+    hs_row, hs_group = (groups + 3, 1) if mx else (1, rows + 9)
+    n = (rows - 1) * hs_row + (groups - 1) * hs_group + 1 + 8
+    hs = torch.full((n,), SENT_U8, dtype=torch.uint8, device="cuda") if mx else _out_f32(n)
+    _say("fused gate_up padded gather, mx", mx)
+    if mx:
+        ops.mxfp8_grouped_gemm_swiglu_quant(rows, I, K, G, dev(offsets), dev(a_rows), T, av, lda, sav, lds_a,
+                                            dev(bbuf), ldb, b_stride_g, dev(sbuf), lds_b, sb_g, hq, ld_hq, hs,
+                                            hs_row, hs_group)
+    else:
+        ops.fp8_grouped_gemm_swiglu_quant(rows, I, K, G, dev(offsets), dev(a_rows), T, av, lda, dev(sa_buf), sa_m,
+                                          sa_k, dev(bbuf), ldb, b_stride_g, dev(sb_buf), sb_g, sb_n, sb_k, hq, ld_hq,
+                                          hs, hs_row, hs_group)
+    _check_u8(hq, rows, I, qr)
+    idx = _grid(rows, groups, hs_row, hs_group)
+    if mx:
+        _check_bytes(hs, idx, sr)
+    else:
+        _check_scales(hs, idx, sr)
