@@ -100,16 +100,27 @@ def rate(unit, amount, ms):
     return r, r / PEAK_HBM_GBS
 
 
-def kernel_entry(unit, amount, ms):
+def kernel_entry(unit, amount, ms, p10=None, p90=None):
+    """Median time with its rate and fraction of peak; p10 and p90 of the
+    timed repetitions beside it."""
     r, f = rate(unit, amount, ms)
-    return {"ms": round(ms, 5), unit: round(r, 2), "frac_of_peak": round(f, 4)}
+    e = {"ms": round(ms, 5), unit: round(r, 2), "frac_of_peak": round(f, 4)}
+    if p10 is not None:
+        e["ms_p10"], e["ms_p90"] = round(p10, 5), round(p90, 5)
+    return e
+
+
+def spread(times):
+    """(median, p10, p90) of a list of durations."""
+    t = np.asarray(times, dtype=np.float64)
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
 def time_sequence(torch, stream, launches, reps, warmup, warm_ms=60.0):
     """Run the list of launches at least `warmup` times and for at least
     `warm_ms` of wall time (the shader clock settles under sustained load),
     then `reps` times with each launch bracketed by events; returns the
-    per-launch median ms."""
+    per-launch (median, p10, p90) ms."""
     t0 = time.perf_counter()
     i = 0
     while i < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
@@ -126,7 +137,7 @@ def time_sequence(torch, stream, launches, reps, warmup, warm_ms=60.0):
             fn(i)
         ev[i][len(launches)].record(stream)
     torch.cuda.synchronize()
-    return [float(np.median([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(reps)])) for k in range(len(launches))]
+    return [spread([ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(reps)]) for k in range(len(launches))]
 
 
 class ClockSampler:
@@ -619,8 +630,7 @@ def main():
         for i in range(args.steps):
             step(i, k, evs[i])
         torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
-        kernels[n] = kernel_entry(*work[n], ms)
+        kernels[n] = kernel_entry(*work[n], *spread([a.elapsed_time(b) for a, b in evs]))
     # The GEMMs for the roofline: events around a batch of back-to-back
     # launches of the same GEMM on the launch stream (its operands are the
     # codes the step's quantizers wrote, still in the last-level cache as in
@@ -697,8 +707,8 @@ def main():
         print("timing %s" % wname, file=sys.stderr, flush=True)
         seq, cfg = table[wname](torch, ops, inputs, to_dev, R)
         ms = time_sequence(torch, stream, [fn for _, fn, _ in seq], args.reps, min(10, args.reps), args.warm_ms)
-        ks = {n: kernel_entry(*wk, t) for (n, _, wk), t in zip(seq, ms)}
-        others[wname] = {"config": cfg, "ms_per_pass": round(float(sum(ms)), 5), "kernels": ks}
+        ks = {n: kernel_entry(*wk, *t) for (n, _, wk), t in zip(seq, ms)}
+        others[wname] = {"config": cfg, "ms_per_pass": round(float(sum(t[0] for t in ms)), 5), "kernels": ks}
         del seq
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
