@@ -129,3 +129,50 @@ def test_grouped_and_fused_epilogues_deterministic():
         return torch.cat([qh.view(-1), sh.view(-1)])
 
     _same_twice(mx_fused, "fused SiLU*mul epilogue (1x32)")
+
+
+def test_concurrent_threads_and_streams():
+    """Two host threads, each on its own stream, quantize a linear layer's
+    operands and run the block-scaled and MXFP8 GEMMs on different inputs at
+    the same time (ctypes releases the GIL, so the calls and the kernels
+    overlap).  Every result equals the same work run alone, byte for byte:
+    the library keeps no state between calls, so the streams share nothing."""
+    import threading
+
+    jobs = [(dev_bf16(_bits((2048, 2560), 60 + 2 * i, 1.0, 0.01, 30.0)), dev_bf16(_bits((4096, 2560), 61 + 2 * i, 0.02)))
+            for i in range(2)]
+
+    def work(x, w):
+        qx, sx, qw, sw = ops.quant_linear(x, w)
+        y = ops.gemm(qx, sx, qw, sw)
+        mqx, msx = ops.mx_quant(x)
+        mqw, msw = ops.mx_quant(w)
+        ym = ops.mx_gemm(mqx, msx, mqw, msw)
+        return [qx, sx.contiguous(), qw, sw, y, mqx, msx, mqw, msw, ym]
+
+    serial = [work(*j) for j in jobs]
+    torch.cuda.synchronize()
+    results, errors = [None, None], []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    r = work(*jobs[i])
+                s.synchronize()
+            results[i] = r
+        except Exception as e:     # re-raised on the main thread below
+            errors.append(e)
+
+    _say("two threads, two streams")
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        for k, (a, b) in enumerate(zip(serial[i], results[i])):
+            assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8)), \
+                "thread %d, result %d differs from the serial run" % (i, k)
