@@ -759,7 +759,11 @@ hipError_t launch_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, in
     p.q = qx; p.ld_q = ld_qx; p.s = sx; p.ssr = ssr; p.ssg = ssg; p.h = nullptr; p.ld_h = 0;
     p.runs_per_row = (int32_t)((cols + 127) / 128);
     p.total_runs = (int32_t)(rows * p.runs_per_row);
-    constexpr int U = 4;                     // as the row-group launch: one trip per 16-lane row
+    // one trip per 16-lane row, four runs per trip: unlike the separate
+    // 1x128 launch (two), here two ran the down projection's pair 40 -> 46 us
+    // (more activation workgroups beside the weight blocks); six and eight
+    // were 1-7% slower than four on both pairs
+    constexpr int U = 4;
     const int64_t rows16 = ((int64_t)p.total_runs + U - 1) / U;
     int64_t xb = (rows16 + (kThreads / 16) - 1) / (kThreads / 16);
     if (xb > 256 * 256) xb = 256 * 256;
