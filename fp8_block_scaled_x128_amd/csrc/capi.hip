@@ -221,10 +221,14 @@ static fp8bs_status check_gemm_common(int64_t M, int64_t N, int64_t K, const voi
     return FP8BS_OK;
 }
 
-fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
-                                  int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
-                                  const float* sb, int64_t sb_stride_n, int64_t sb_stride_k, fp8bs_bscale bscale,
-                                  void* c, int64_t ldc, fp8bs_out out, hipStream_t stream) {
+}  // extern "C"
+
+// Validation shared by fp8_blockscaled_gemm and its K-split form; fills g
+// (g.M = g.N = 0 when there is nothing to compute).
+static fp8bs_status blockscaled_args(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                                     int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                                     const float* sb, int64_t sb_stride_n, int64_t sb_stride_k, fp8bs_bscale bscale,
+                                     void* c, int64_t ldc, fp8bs_out out, GemmArgs* g) {
     if (bscale != FP8BS_BSCALE_BLOCK128 && bscale != FP8BS_BSCALE_ROW128)
         return fail(FP8BS_ERR_UNSUPPORTED, "bscale %d", (int)bscale);
     fp8bs_status v = check_gemm_common(M, N, K, a, lda, b, ldb, c, ldc, out, 128);
@@ -242,11 +246,58 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t
         return v;
     fp8bs_status d = check_device();
     if (d != FP8BS_OK) return d;
+    g->M = M; g->N = N; g->K = K; g->a = a; g->lda = lda; g->sa = sa; g->sa_sm = sa_stride_m; g->sa_sk = sa_stride_k;
+    g->b = b; g->ldb = ldb; g->b_sg = 0; g->sb = sb; g->sb_sg = 0; g->sb_sn = sb_stride_n; g->sb_sk = sb_stride_k;
+    g->bscale_row = bscale == FP8BS_BSCALE_ROW128; g->c = c; g->ldc = ldc; g->out_f32 = out == FP8BS_OUT_FP32;
+    return FP8BS_OK;
+}
+
+extern "C" {
+
+fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                                  int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b, int64_t ldb,
+                                  const float* sb, int64_t sb_stride_n, int64_t sb_stride_k, fp8bs_bscale bscale,
+                                  void* c, int64_t ldc, fp8bs_out out, hipStream_t stream) {
     GemmArgs g{};
-    g.M = M; g.N = N; g.K = K; g.a = a; g.lda = lda; g.sa = sa; g.sa_sm = sa_stride_m; g.sa_sk = sa_stride_k;
-    g.b = b; g.ldb = ldb; g.b_sg = 0; g.sb = sb; g.sb_sg = 0; g.sb_sn = sb_stride_n; g.sb_sk = sb_stride_k;
-    g.bscale_row = bscale == FP8BS_BSCALE_ROW128; g.c = c; g.ldc = ldc; g.out_f32 = out == FP8BS_OUT_FP32;
+    const fp8bs_status v = blockscaled_args(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, sb, sb_stride_n,
+                                            sb_stride_k, bscale, c, ldc, out, &g);
+    if (v != FP8BS_OK || g.M == 0) return v;
     return launched(launch_gemm_blockscaled(g, stream), "fp8_blockscaled_gemm");
+}
+
+fp8bs_status fp8_blockscaled_gemm_splitk(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                         const float* sa, int64_t sa_stride_m, int64_t sa_stride_k, const uint8_t* b,
+                                         int64_t ldb, const float* sb, int64_t sb_stride_n, int64_t sb_stride_k,
+                                         fp8bs_bscale bscale, void* c, int64_t ldc, fp8bs_out out, int32_t splits,
+                                         float* ws, size_t ws_bytes, hipStream_t stream) {
+    if (splits < 0) return fail(FP8BS_ERR_SHAPE, "splits %d < 0", (int)splits);
+    GemmArgs g{};
+    const fp8bs_status v = blockscaled_args(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, sb, sb_stride_n,
+                                            sb_stride_k, bscale, c, ldc, out, &g);
+    if (v != FP8BS_OK || g.M == 0) return v;
+    if (splits > K / 128) return fail(FP8BS_ERR_SHAPE, "splits %d > K / 128 = %lld", (int)splits, (long long)(K / 128));
+    if (splits == 0) splits = plan_gemm_splitk(M, N, K, out == FP8BS_OUT_FP32);
+    if (splits > 1) {
+        if (!ws) return fail(FP8BS_ERR_NULL, "ws is required when splits > 1");
+        if (!aligned(ws, 16)) return fail(FP8BS_ERR_ALIGN, "ws must be 16-byte aligned");
+        const uint64_t need = (uint64_t)splits * (uint64_t)M * (uint64_t)N * 4u;
+        if ((uint64_t)ws_bytes < need)
+            return fail(FP8BS_ERR_SHAPE, "workspace of %llu bytes, %llu needed for %d splits",
+                        (unsigned long long)ws_bytes, (unsigned long long)need, (int)splits);
+        if ((uint64_t)M * (uint64_t)N / 8 / 256 >= (1ull << 31)) return fail(FP8BS_ERR_SHAPE, "output too large");
+    }
+    return launched(launch_gemm_blockscaled_splitk(g, splits, ws, stream), "fp8_blockscaled_gemm_splitk");
+}
+
+fp8bs_status fp8_blockscaled_gemm_splitk_plan(int64_t M, int64_t N, int64_t K, fp8bs_out out, int32_t* splits,
+                                              size_t* ws_bytes) {
+    if (!splits || !ws_bytes) return fail(FP8BS_ERR_NULL, "splits and ws_bytes are required");
+    if (out != FP8BS_OUT_BF16 && out != FP8BS_OUT_FP32) return fail(FP8BS_ERR_UNSUPPORTED, "out %d", out);
+    if (M < 0 || N < 0 || K < 0 || K % 128 || N % 128) return fail(FP8BS_ERR_SHAPE, "M %lld N %lld K %lld",
+                                                                   (long long)M, (long long)N, (long long)K);
+    *splits = (M == 0 || N == 0 || K == 0) ? 1 : plan_gemm_splitk(M, N, K, out == FP8BS_OUT_FP32);
+    *ws_bytes = *splits > 1 ? (size_t)*splits * (size_t)M * (size_t)N * 4u : 0;
+    return ok();
 }
 
 fp8bs_status fp8_blockscaled_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t* plan) {

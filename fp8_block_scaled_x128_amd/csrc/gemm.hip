@@ -162,6 +162,9 @@ struct KArgs {
     void* c; int64_t ldc;
     int32_t G; const int32_t* offsets; const int32_t* a_rows;
     int32_t kinv_row;                          // MODE_KINV: sb indexed by n (1) or n / 128 (0)
+    // dense K split: grid row y takes its share of the K slices and writes
+    // its fp32 partial tile to c + y * c_split bytes (ksplit 1: no split)
+    int32_t ksplit; int64_t c_split;
     // SWIGLU (grouped gate/up GEMM with SiLU*mul and the quantization of h in
     // the epilogue): B rows [0, swi) are gate rows, [swi, 2 swi) up rows;
     // h codes hq [rows][ld_hq]; h scales hs[m * hs_sm + group * hs_sg], fp32
@@ -448,6 +451,16 @@ k_gemm(KArgs p) {
         it_items = __builtin_amdgcn_readfirstlane(s_range[2]);
         if (!take_tile(0)) return;                 // uniform: no work item for this workgroup
     }
+    // K slices of this workgroup: [kbase, kbase + nk).  Dense K split: grid
+    // row y takes the y-th of ksplit contiguous ranges (the first
+    // nk_all % ksplit ranges one slice longer).
+    const int nk_all = p.K / BK;
+    int kbase = 0, nk = nk_all;
+    if (!GROUPED && p.ksplit > 1) {
+        const int y = (int)blockIdx.y, per = nk_all / p.ksplit, extra = nk_all % p.ksplit;
+        kbase = y * per + min(y, extra);
+        nk = per + (y < extra ? 1 : 0);
+    }
     auto arow = [&](int m_local) {             // physical A row of tile row m_local (clamped)
         int m = min(m_begin + m_local, m_end - 1);
         if (GATHER) m = p.a_rows[m];
@@ -516,23 +529,25 @@ k_gemm(KArgs p) {
     auto copy_sb = [&](int kb, int stage) {
         if (!has_sb) return;
         const uint32_t st = bstage(stage) + BN * BK;
-        if (MODE == MODE_MX) dma4(sbp + kb * 4, sb_off, st + wave * 64 * 4);
-        else if (MODE == MODE_P2) dma4(sbp + (kb >> 2) * 4, sb_off, st);   // slices 4(kb/4) .. +3
-        else if (MODE == MODE_BLOCK128) dma4(sbp + kb * p.sb_sk * 4, sb_off, st);
-        else dma4(sbp + kb * p.sb_sk * 4, sb_off, st + wave * 64 * 4);
+        const int kg = kbase + kb;
+        if (MODE == MODE_MX) dma4(sbp + kg * 4, sb_off, st + wave * 64 * 4);
+        else if (MODE == MODE_P2) dma4(sbp + (kg >> 2) * 4, sb_off, st);   // slices 4(kg/4) .. +3
+        else if (MODE == MODE_BLOCK128) dma4(sbp + kg * p.sb_sk * 4, sb_off, st);
+        else dma4(sbp + kg * p.sb_sk * 4, sb_off, st + wave * 64 * 4);
     };
     auto copy_sa = [&](int kb, int buf) {
         if (!has_sa) return;
         const uint32_t st = abuf(buf) + BM * BK + wave * 64 * 4;
-        if (MODE == MODE_MX) dma4(p.sa + kb * 4, sa_off, st);
-        else if (MODE == MODE_P2) dma4(p.sa + (kb >> 2) * 4, sa_off, st);
-        else dma4(p.sa + kb * p.sa_sk * 4, sa_off, st);
+        const int kg = kbase + kb;
+        if (MODE == MODE_MX) dma4(p.sa + kg * 4, sa_off, st);
+        else if (MODE == MODE_P2) dma4(p.sa + (kg >> 2) * 4, sa_off, st);
+        else dma4(p.sa + kg * p.sa_sk * 4, sa_off, st);
     };
     auto copy_a = [&](int kb, int buf, int t) {
-        dma16(p.a + kb * BK, offA[t], abuf(buf) + (wave * C::kDmaA + t) * 8 * BK);
+        dma16(p.a + (kbase + kb) * BK, offA[t], abuf(buf) + (wave * C::kDmaA + t) * 8 * BK);
     };
     auto copy_b = [&](int kb, int stage, int t) {
-        dma16(bptr + kb * BK, offB[t], bstage(stage) + bcopy(t) * 8 * BK);
+        dma16(bptr + (kbase + kb) * BK, offB[t], bstage(stage) + bcopy(t) * 8 * BK);
     };
 
     v4f acc[NF][4];
@@ -541,7 +556,6 @@ k_gemm(KArgs p) {
     // activation slice kb + kLeadA (scales right after the barriers, tile in
     // the first n-tile steps) and then those of weight slice kb + kLeadB; the
     // prologue issues the same sequence for the steps -kLeadMax..-1.
-    const int nk = p.K / BK;
     auto prologue = [&]() {
 #pragma unroll
         for (int j = -C::kLeadMax; j < 0; ++j) {
@@ -600,7 +614,7 @@ k_gemm(KArgs p) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 if (MODE == MODE_MX) mxa[mt] = lds_readu8(sa_lds + mt * 64 + q);
-                else if (MODE == MODE_P2) mxa[mt] = lds_readu8(sa_lds + mt * 64 + (kb & 3));
+                else if (MODE == MODE_P2) mxa[mt] = lds_readu8(sa_lds + mt * 64 + ((kbase + kb) & 3));
                 else if (MODE == MODE_KINV) mxa[mt] = 0;    // constant 0: the plain (unscaled) instruction, see mfma_unit
                 else sam[mt] = lds_readf(sa_lds + mt * 64);
             }
@@ -646,7 +660,7 @@ k_gemm(KArgs p) {
             // block's copied word (chosen per n-tile as in BLOCK128)
             int pb0 = kE8M0One, pb1 = kE8M0One;
             if (MODE == MODE_P2) {
-                const uint32_t sbw = tB + BN * BK + (kb & 3);
+                const uint32_t sbw = tB + BN * BK + ((kbase + kb) & 3);
                 pb0 = lds_readu8(sbw + (NF == 8 ? wn * 4 : 0));
                 pb1 = NF == 8 ? pb0 : lds_readu8(sbw + 4);
             }
@@ -837,7 +851,7 @@ k_gemm(KArgs p) {
         ebase2 = lds_addr(s_stage2);
     }
     const uint32_t wst = (kTwoRegions && wave >= 4 ? ebase2 : ebase) + (uint32_t)((wave % kStageWaves) * kRows * kPitch);
-    uint8_t* cbase = static_cast<uint8_t*>(p.c) + (int64_t)nw0 * EB;
+    uint8_t* cbase = static_cast<uint8_t*>(p.c) + (int64_t)nw0 * EB + (GROUPED ? 0 : (int64_t)blockIdx.y * p.c_split);
     // SWIGLU tiles never leave the matrix (wave_out holds), so its barriers
     // are met by every wave
 #pragma unroll
@@ -953,7 +967,8 @@ hipError_t launch(const KArgs& p, bool out_f32, hipStream_t st) {
     using C = Cfg<WAVES, NF, false, WN>;
     dim3 grid;
     if (!GROUPED) {
-        grid = dim3((unsigned)(((int64_t)(p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN)));
+        grid = dim3((unsigned)(((int64_t)(p.M + C::BM - 1) / C::BM) * ((p.N + C::BN - 1) / C::BN)),
+                    (unsigned)(p.ksplit > 1 ? p.ksplit : 1));
     } else {
         // upper bound on the work items (row tiles over all groups x n-tiles),
         // rounded up to a multiple of the 8 XCDs
@@ -1020,9 +1035,12 @@ constexpr double kLaunchCycles = 15000;
 int64_t cfg_bn(const TileCfg& c) { return 16 * c.nf * c.wn; }
 int64_t cfg_bm(const TileCfg& c) { return 64 * c.waves / c.wn; }
 
-double region_cycles(const TileCfg& c, int64_t M, int64_t N, int64_t nk) {
-    const int64_t bm = cfg_bm(c), bn = cfg_bn(c);
-    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+int64_t cfg_tiles(const TileCfg& c, int64_t M, int64_t N) {
+    return ((M + cfg_bm(c) - 1) / cfg_bm(c)) * ((N + cfg_bn(c) - 1) / cfg_bn(c));
+}
+
+// `tiles` workgroups of nk slices each over the CUs
+double units_cycles(const TileCfg& c, int64_t tiles, int64_t nk) {
     const double round = (double)nk * c.slice_cycles + c.tile_cycles;
     if (c.per_cu != 2) return (double)((tiles + kCUs - 1) / kCUs) * round;
     const int64_t full = tiles / (2 * kCUs), rest = tiles % (2 * kCUs);
@@ -1030,19 +1048,24 @@ double region_cycles(const TileCfg& c, int64_t M, int64_t N, int64_t nk) {
     return (double)full * round + last;
 }
 
+double region_cycles(const TileCfg& c, int64_t M, int64_t N, int64_t nk) {
+    return units_cycles(c, cfg_tiles(c, M, N), nk);
+}
+
 struct DensePlan {
     int c1, c2;          // indices into kDenseCfgs; c2 < 0: one region
     int64_t split;       // first column of the second region (multiple of 128)
+    double cycles;       // the estimate it was chosen by
 };
 
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K) {
     const int64_t nk = K / BK;
-    DensePlan best{0, -1, N};
+    DensePlan best{0, -1, N, 0.0};
     double best_t = region_cycles(kDenseCfgs[0], M, N, nk);
     const int nc = (int)(sizeof(kDenseCfgs) / sizeof(kDenseCfgs[0]));
     for (int i = 0; i < nc; ++i) {
         const double t = region_cycles(kDenseCfgs[i], M, N, nk);
-        if (t < best_t) { best_t = t; best = DensePlan{i, -1, N}; }
+        if (t < best_t) { best_t = t; best = DensePlan{i, -1, N, 0.0}; }
         // region 1 in whole tiles of configuration i, on a 128-column boundary
         const int64_t bn = cfg_bn(kDenseCfgs[i]);
         for (int64_t split = bn; split < N; split += bn) {
@@ -1051,11 +1074,81 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K) {
             for (int j = 0; j < nc; ++j) {
                 if (j == i) continue;
                 const double tt = t1 + region_cycles(kDenseCfgs[j], M, N - split, nk) + kLaunchCycles;
-                if (tt < best_t) { best_t = tt; best = DensePlan{i, j, split}; }
+                if (tt < best_t) { best_t = tt; best = DensePlan{i, j, split, 0.0}; }
             }
         }
     }
+    best.cycles = best_t;
     return best;
+}
+
+// Dense K split.  With few output tiles and a long K (the decode-sized
+// GEMMs of the rollout side: M of a few hundred tokens, K 9728), most CUs
+// would idle while each tile walks every K slice.  The slices are divided
+// into `splits` contiguous ranges, one per grid row; each writes its fp32
+// partial tile to a workspace, and k_splitk_sum adds the partials in split
+// order.  Priced as the tiles times `splits` workgroups of ceil(nk / splits)
+// slices, plus the sum's traffic (read splits x M x N fp32, write M x N) at
+// ~4 TB/s and a second launch.
+constexpr double kSumBytesPerCycle = 2000.0;
+constexpr int kMaxSplits = 32;
+
+struct SplitPlan {
+    int ci;              // configuration index (-1: no split, plan_dense)
+    int splits;
+    double cycles;
+};
+
+SplitPlan plan_split_cfg(int64_t M, int64_t N, int64_t nk, int splits, int out_bytes) {
+    SplitPlan best{-1, splits, 1e300};
+    const int nc = (int)(sizeof(kDenseCfgs) / sizeof(kDenseCfgs[0]));
+    const int64_t nks = (nk + splits - 1) / splits;
+    const double sum = ((double)splits * 4.0 + out_bytes) * (double)M * (double)N / kSumBytesPerCycle;
+    for (int i = 0; i < nc; ++i) {
+        const double t = units_cycles(kDenseCfgs[i], cfg_tiles(kDenseCfgs[i], M, N) * splits, nks) + sum + kLaunchCycles;
+        if (t < best.cycles) best = SplitPlan{i, splits, t};
+    }
+    return best;
+}
+
+SplitPlan plan_splitk(int64_t M, int64_t N, int64_t K, int out_bytes) {
+    const int64_t nk = K / BK;
+    SplitPlan best{-1, 1, plan_dense(M, N, K).cycles};
+    for (int s = 2; s <= kMaxSplits && s <= nk; ++s) {
+        const SplitPlan t = plan_split_cfg(M, N, nk, s, out_bytes);
+        if (t.cycles < best.cycles) best = t;
+    }
+    return best;
+}
+
+// c[m][n] = sum over splits s (in order) of ws[s][m][n]; one thread per 8
+// consecutive outputs of a row (N % 128 == 0), rounded to bf16 or kept fp32.
+template <bool OUTF32>
+__global__ void __launch_bounds__(256) k_splitk_sum(const float* __restrict__ ws, int64_t split_elems, int32_t splits,
+                                                    int64_t chunks, int32_t cpr, void* __restrict__ c, int64_t ldc) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= chunks) return;
+    const int64_t m = i / cpr;
+    const int64_t n = (i - m * cpr) * 8;
+    const float* src = ws + m * ((int64_t)cpr * 8) + n;
+    f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
+    f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 4);
+    for (int32_t sp = 1; sp < splits; ++sp) {
+        const float* q = src + (int64_t)sp * split_elems;
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(q);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { a0[r] = a0[r] + b0[r]; a1[r] = a1[r] + b1[r]; }
+    }
+    if (OUTF32) {
+        float* dst = static_cast<float*>(c) + m * ldc + n;
+        *reinterpret_cast<f32x4*>(dst) = a0;
+        *reinterpret_cast<f32x4*>(dst + 4) = a1;
+    } else {
+        uint16_t* dst = static_cast<uint16_t*>(c) + m * ldc + n;
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]),
+                                                     pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3]));
+    }
 }
 
 template <int MODE>
@@ -1105,6 +1198,35 @@ hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st) {
     const hipError_t e = go(plan.c1, p1);
     if (e != hipSuccess) return e;
     return go(plan.c2, p2);
+}
+
+int32_t plan_gemm_splitk(int64_t M, int64_t N, int64_t K, bool out_f32) {
+    return plan_splitk(M, N, K, out_f32 ? 4 : 2).splits;
+}
+
+hipError_t launch_gemm_blockscaled_splitk(const GemmArgs& g, int32_t splits, float* ws, hipStream_t st) {
+    if (g.M == 0 || g.N == 0) return hipSuccess;
+    if (splits <= 1) return launch_gemm_blockscaled(g, st);
+    // the split GEMM: fp32 partial tiles into ws[split][M][N]
+    KArgs p = base_args(g.M, g.N, g.K, g.a, g.lda, g.sa, g.b, g.ldb, g.sb, ws, g.N);
+    p.sa_sm = g.sa_sm; p.sa_sk = g.sa_sk; p.sb_sn = g.sb_sn; p.sb_sk = g.sb_sk;
+    p.kinv_row = g.bscale_row ? 1 : 0;
+    p.ksplit = splits;
+    p.c_split = g.M * g.N * 4;
+    const int ci = plan_split_cfg(g.M, g.N, g.K / BK, splits, g.out_f32 ? 4 : 2).ci;
+    hipError_t e;
+    if (g.sa_sk == 0 && g.sb_sk == 0) e = launch_dense<MODE_KINV>(ci, p, true, st);
+    else if (g.bscale_row) e = launch_dense<MODE_ROW128>(ci, p, true, st);
+    else e = launch_dense<MODE_BLOCK128>(ci, p, true, st);
+    if (e != hipSuccess) return e;
+    const int32_t cpr = (int32_t)(g.N / 8);
+    const int64_t chunks = g.M * cpr;
+    const dim3 grid((unsigned)((chunks + 255) / 256));
+    if (g.out_f32)
+        hipLaunchKernelGGL(k_splitk_sum<true>, grid, dim3(256), 0, st, ws, g.M * g.N, splits, chunks, cpr, g.c, g.ldc);
+    else
+        hipLaunchKernelGGL(k_splitk_sum<false>, grid, dim3(256), 0, st, ws, g.M * g.N, splits, chunks, cpr, g.c, g.ldc);
+    return hipGetLastError();
 }
 
 void plan_gemm_blockscaled(int64_t M, int64_t N, int64_t K, int32_t out[5]) {

@@ -52,6 +52,11 @@ hipError_t launch_gemm_blockscaled(const GemmArgs& g, hipStream_t st);
 // Tiling of a dense BLOCK128 problem: waves and weight rows per tile of the
 // two column regions, and the first column of the second (N if one region).
 void plan_gemm_blockscaled(int64_t M, int64_t N, int64_t K, int32_t out[5]);
+// The same GEMM with its K slices divided among `splits` grid rows: fp32
+// partials into ws[splits][M][N], then their sum in split order into c.
+hipError_t launch_gemm_blockscaled_splitk(const GemmArgs& g, int32_t splits, float* ws, hipStream_t st);
+// The split count the planner chooses (1: no split).
+int32_t plan_gemm_splitk(int64_t M, int64_t N, int64_t K, bool out_f32);
 hipError_t launch_gemm_grouped(const GemmArgs& g, hipStream_t st);
 // Grouped gate/up GEMM (B = [G][2I][K], gate rows then up rows) whose epilogue
 // forms h = bf16(silu(gate) * up) from the bf16-rounded outputs and writes

@@ -25,7 +25,7 @@ OUT_BF16, OUT_FP32 = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
 EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_linear", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
-           "fp8_grouped_gemm", "fp8_grouped_gemm_ws_size", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
+           "fp8_blockscaled_gemm_splitk", "fp8_blockscaled_gemm_splitk_plan", "fp8_grouped_gemm", "fp8_grouped_gemm_ws_size", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
            "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
            "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
@@ -61,6 +61,9 @@ def load():
             "fp8_quant_tensorwise": [P, I64, I64, I64, P, I64, P, P],
             "fp8_blockscaled_gemm": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P, I64, INT, P],
             "fp8_blockscaled_gemm_plan": [I64, I64, I64, P],
+            "fp8_blockscaled_gemm_splitk": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P, I64,
+                                            INT, I32, P, ctypes.c_size_t, P],
+            "fp8_blockscaled_gemm_splitk_plan": [I64, I64, I64, INT, P, P],
             "fp8_grouped_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64,
                                  P, I64, INT, P],
             "fp8_grouped_gemm_ws_size": [I64, I32, I64, P],
@@ -156,6 +159,23 @@ def fp8_blockscaled_gemm_plan(M, N, K):
     out = (ctypes.c_int32 * 5)()
     _check("fp8_blockscaled_gemm_plan", load().fp8_blockscaled_gemm_plan(M, N, K, ctypes.cast(out, ctypes.c_void_p)))
     return (out[0], out[1]), ((out[2], out[3]) if out[2] else None), out[4]
+
+
+def fp8_blockscaled_gemm_splitk(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, sb, sb_stride_n,
+                                sb_stride_k, bscale, c, ldc, out, splits, ws, ws_bytes, stream=None,
+                                raise_on_error=True):
+    st = load().fp8_blockscaled_gemm_splitk(M, N, K, _p(a), lda, _p(sa), sa_stride_m, sa_stride_k, _p(b), ldb,
+                                            _p(sb), sb_stride_n, sb_stride_k, bscale, _p(c), ldc, out, splits,
+                                            _p(ws), ws_bytes, _stream(stream))
+    return _check("fp8_blockscaled_gemm_splitk", st, raise_on_error)
+
+
+def fp8_blockscaled_gemm_splitk_plan(M, N, K, out):
+    """(splits, workspace bytes) the K-split GEMM chooses.  Host only."""
+    sp, wb = ctypes.c_int32(0), ctypes.c_size_t(0)
+    _check("fp8_blockscaled_gemm_splitk_plan",
+           load().fp8_blockscaled_gemm_splitk_plan(M, N, K, out, ctypes.byref(sp), ctypes.byref(wb)))
+    return sp.value, wb.value
 
 
 def fp8_grouped_gemm_ws_size(max_total_rows, G, N, raise_on_error=True):
@@ -347,6 +367,22 @@ def gemm(a, sa, b, sb, bscale=BSCALE_BLOCK128, out_dtype=torch.bfloat16):
     c = torch.empty((M, N), dtype=out_dtype, device=a.device)
     fp8_blockscaled_gemm(M, N, K, a, a.stride(0), sa, sa.stride(0), sa.stride(1), b, b.stride(0), sb, sb.stride(0),
                          sb.stride(1), bscale, c, c.stride(0), OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
+    return c
+
+
+def gemm_splitk(a, sa, b, sb, bscale=BSCALE_BLOCK128, out_dtype=torch.bfloat16, splits=0):
+    """gemm() with the K slices split among grid rows (splits 0: the
+    planner's count); the fp32 workspace is allocated here with torch."""
+    M, K = a.shape
+    N = b.shape[0]
+    out = OUT_FP32 if out_dtype == torch.float32 else OUT_BF16
+    if splits == 0:
+        splits, _ = fp8_blockscaled_gemm_splitk_plan(M, N, K, out)
+    ws = torch.empty(max(splits, 1) * M * N if splits > 1 else 4, dtype=torch.float32, device=a.device)
+    c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    fp8_blockscaled_gemm_splitk(M, N, K, a, a.stride(0), sa, sa.stride(0), sa.stride(1), b, b.stride(0), sb,
+                                sb.stride(0), sb.stride(1), bscale, c, c.stride(0), out, splits, ws,
+                                ws.numel() * 4)
     return c
 
 

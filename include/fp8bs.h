@@ -221,6 +221,49 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
 fp8bs_status fp8_blockscaled_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t* plan);
 
 /* ------------------------------------------------------------------------
+ * fp8_blockscaled_gemm_splitk -- fp8_blockscaled_gemm (same formula, modes,
+ * arguments and requirements) with its 128-wide K slices divided into
+ * `splits` contiguous ranges, for problems with few output tiles and a long
+ * K: the decode-sized GEMMs of the rollout side that the pages' recipe shares
+ * with the trainer ("Low Precision RL", section "Unified training recipe"),
+ * where one range per tile would leave most of the GPU idle.  Range s (the
+ * first (K/128) % splits ranges hold one slice more) accumulates its
+ * per-slice-scaled FP32 partials, exactly as fp8_blockscaled_gemm does over
+ * all slices, into ws[s][M][N]; a second kernel adds the ranges in order
+ * s = 0, 1, ... in FP32 and rounds to c (bf16, nearest even) or stores it
+ * (fp32).  The sum differs from fp8_blockscaled_gemm only in FP32 rounding
+ * order: it is deterministic, and identical wherever every partial is exact.
+ *
+ * splits   : 1 .. K/128 (1: exactly fp8_blockscaled_gemm, ws unused), or 0:
+ *            the count fp8_blockscaled_gemm_splitk_plan gives.
+ * ws       : device fp32 workspace owned by the caller, 16-byte aligned, at
+ *            least splits * M * N * 4 bytes (ws_bytes); its contents on entry
+ *            are ignored and on return undefined.  Calls that overlap in time
+ *            need separate workspaces.
+ * Errors   : those of fp8_blockscaled_gemm; FP8BS_ERR_SHAPE for splits < 0,
+ *            splits > K/128 or ws_bytes too small; FP8BS_ERR_NULL for a NULL
+ *            ws when splits > 1.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_blockscaled_gemm_splitk(int64_t M, int64_t N, int64_t K,
+                                         const uint8_t* a, int64_t lda,
+                                         const float* sa, int64_t sa_stride_m, int64_t sa_stride_k,
+                                         const uint8_t* b, int64_t ldb,
+                                         const float* sb, int64_t sb_stride_n, int64_t sb_stride_k,
+                                         fp8bs_bscale bscale, void* c, int64_t ldc, fp8bs_out out,
+                                         int32_t splits, float* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_blockscaled_gemm_splitk_plan -- the split count the planner chooses
+ * for this shape and output type (1 when splitting does not pay: the
+ * estimate prices the extra partial traffic and the second launch against
+ * the idle compute units of one range per tile) and the workspace it needs
+ * (0 when splits == 1).  Host only: launches nothing and needs no device.
+ * Requirements: M, N, K >= 0; K % 128 == 0; N % 128 == 0.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_blockscaled_gemm_splitk_plan(int64_t M, int64_t N, int64_t K, fp8bs_out out,
+                                              int32_t* splits, size_t* ws_bytes);
+
+/* ------------------------------------------------------------------------
  * fp8_grouped_gemm -- the block-scaled GEMM over G expert groups of rows
  * (the MoE layers the pages run the recipe on, Qwen3-30B-A3B, "Low
  * Precision RL", table "Choose a precision").

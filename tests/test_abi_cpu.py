@@ -151,6 +151,24 @@ def test_host_validation_rejects_before_launch(lib):
     assert mxs(0, 128, 256) == 0
 
 
+def test_splitk_plan(lib):
+    """The K-split query (host only): no split for the MLP shapes at 4096
+    tokens, a split for decode-sized ones, the workspace it needs, and the
+    shape errors of the GEMM."""
+    from fp8_block_scaled_x128_amd import ops
+    for M, N, K in [(4096, 9728, 2560), (4096, 2560, 9728), (9728, 2560, 4096), (0, 2560, 9728), (128, 0, 9728)]:
+        assert ops.fp8_blockscaled_gemm_splitk_plan(M, N, K, ops.OUT_BF16) == (1, 0)
+    for M, N, K in [(128, 2560, 9728), (512, 2560, 9728), (128, 9728, 2560)]:
+        for out in (ops.OUT_BF16, ops.OUT_FP32):
+            s, wb = ops.fp8_blockscaled_gemm_splitk_plan(M, N, K, out)
+            assert 1 < s <= min(32, K // 128) and wb == s * M * N * 4
+    sp, wb = ctypes.c_int32(0), ctypes.c_size_t(0)
+    assert lib.fp8_blockscaled_gemm_splitk_plan(128, 100, 128, 0, ctypes.byref(sp), ctypes.byref(wb)) == 2
+    assert lib.fp8_blockscaled_gemm_splitk_plan(128, 128, 100, 0, ctypes.byref(sp), ctypes.byref(wb)) == 2
+    assert lib.fp8_blockscaled_gemm_splitk_plan(128, 128, 128, 7, ctypes.byref(sp), ctypes.byref(wb)) == 5
+    assert lib.fp8_blockscaled_gemm_splitk_plan(128, 128, 128, 0, None, ctypes.byref(wb)) == 1
+
+
 def test_dense_tile_plan(lib):
     """The tiling query (host only): regions cover N on a 128-column boundary,
     every region's tiling is one the library builds, and the MLP shapes get
