@@ -11,6 +11,14 @@
 
 using namespace fp8bs;
 
+// Scratch of fp8_blockscaled_gemm_splitk_noalloc: the fp32 partials of the
+// K ranges, in one file-scope array per device (each GPU holds its copy for
+// the life of the process).  Nothing in it needs to start at zero (every
+// partial the sum reads is written first by the same call); calls that
+// overlap in time on one GPU share it and race.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 namespace {
 
 thread_local char g_detail[512];
@@ -54,6 +62,29 @@ fp8bs_status launched(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxRuns = (int64_t)1 << 30;   // row-group kernels index runs with int32
+
+// Host code never uses the array's name (`scratch`, above) as an address:
+// the first call on a device looks up that device's copy with
+// hipGetSymbolAddress and keeps it here.
+std::atomic<float*> g_scratch[64];
+
+fp8bs_status scratch_ptr(float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(FP8BS_ERR_DEVICE, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(FP8BS_ERR_DEVICE, "device index %d out of range", dev);
+    float* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* q = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || q == nullptr)
+            return fail(FP8BS_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        p = static_cast<float*>(q);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return FP8BS_OK;
+}
 
 }  // namespace
 
@@ -287,6 +318,36 @@ fp8bs_status fp8_blockscaled_gemm_splitk(int64_t M, int64_t N, int64_t K, const 
         if ((uint64_t)M * (uint64_t)N / 8 / 256 >= (1ull << 31)) return fail(FP8BS_ERR_SHAPE, "output too large");
     }
     return launched(launch_gemm_blockscaled_splitk(g, splits, ws, stream), "fp8_blockscaled_gemm_splitk");
+}
+
+fp8bs_status fp8_blockscaled_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                                 const float* sa, int64_t sa_stride_m, int64_t sa_stride_k,
+                                                 const uint8_t* b, int64_t ldb, const float* sb, int64_t sb_stride_n,
+                                                 int64_t sb_stride_k, fp8bs_bscale bscale, void* c, int64_t ldc,
+                                                 fp8bs_out out, int32_t splits, hipStream_t stream) {
+    if (splits < 0) return fail(FP8BS_ERR_SHAPE, "splits %d < 0", (int)splits);
+    GemmArgs g{};
+    const fp8bs_status v = blockscaled_args(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, sb, sb_stride_n,
+                                            sb_stride_k, bscale, c, ldc, out, &g);
+    if (v != FP8BS_OK || g.M == 0) return v;
+    if (splits > K / 128) return fail(FP8BS_ERR_SHAPE, "splits %d > K / 128 = %lld", (int)splits, (long long)(K / 128));
+    const uint64_t per_split = (uint64_t)M * (uint64_t)N * 4u;
+    if (splits == 0) {
+        // the planner's count, capped to what the scratch holds
+        splits = plan_gemm_splitk(M, N, K, out == FP8BS_OUT_FP32);
+        const uint64_t fit = kScratchBytes / per_split;
+        if ((uint64_t)splits > fit) splits = fit >= 2 ? (int32_t)fit : 1;
+    }
+    float* ws = nullptr;
+    if (splits > 1) {
+        if ((uint64_t)splits * per_split > kScratchBytes)
+            return fail(FP8BS_ERR_SHAPE, "%d splits of a %lld x %lld output need %llu bytes of scratch; the limit is %llu",
+                        (int)splits, (long long)M, (long long)N, (unsigned long long)((uint64_t)splits * per_split),
+                        (unsigned long long)kScratchBytes);
+        const fp8bs_status e = scratch_ptr(&ws);
+        if (e != FP8BS_OK) return e;
+    }
+    return launched(launch_gemm_blockscaled_splitk(g, splits, ws, stream), "fp8_blockscaled_gemm_splitk_noalloc");
 }
 
 fp8bs_status fp8_blockscaled_gemm_splitk_plan(int64_t M, int64_t N, int64_t K, fp8bs_out out, int32_t* splits,

@@ -25,7 +25,8 @@ OUT_BF16, OUT_FP32 = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW128 = 0, 1
 
 EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_linear", "fp8_quant_rowwise", "fp8_quant_tensorwise", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_plan",
-           "fp8_blockscaled_gemm_splitk", "fp8_blockscaled_gemm_splitk_plan", "fp8_grouped_gemm", "fp8_grouped_gemm_ws_size", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
+           "fp8_blockscaled_gemm_splitk", "fp8_blockscaled_gemm_splitk_noalloc", "fp8_blockscaled_gemm_splitk_plan",
+           "fp8_grouped_gemm", "fp8_grouped_gemm_ws_size", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
            "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
            "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
@@ -64,6 +65,8 @@ def load():
             "fp8_blockscaled_gemm_splitk": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P, I64,
                                             INT, I32, P, ctypes.c_size_t, P],
             "fp8_blockscaled_gemm_splitk_plan": [I64, I64, I64, INT, P, P],
+            "fp8_blockscaled_gemm_splitk_noalloc": [I64, I64, I64, P, I64, P, I64, I64, P, I64, P, I64, I64, INT, P,
+                                                    I64, INT, I32, P],
             "fp8_grouped_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, I64, I64,
                                  P, I64, INT, P],
             "fp8_grouped_gemm_ws_size": [I64, I32, I64, P],
@@ -168,6 +171,14 @@ def fp8_blockscaled_gemm_splitk(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b
                                             _p(sb), sb_stride_n, sb_stride_k, bscale, _p(c), ldc, out, splits,
                                             _p(ws), ws_bytes, _stream(stream))
     return _check("fp8_blockscaled_gemm_splitk", st, raise_on_error)
+
+
+def fp8_blockscaled_gemm_splitk_noalloc(M, N, K, a, lda, sa, sa_stride_m, sa_stride_k, b, ldb, sb, sb_stride_n,
+                                        sb_stride_k, bscale, c, ldc, out, splits, stream=None, raise_on_error=True):
+    st = load().fp8_blockscaled_gemm_splitk_noalloc(M, N, K, _p(a), lda, _p(sa), sa_stride_m, sa_stride_k, _p(b),
+                                                    ldb, _p(sb), sb_stride_n, sb_stride_k, bscale, _p(c), ldc, out,
+                                                    splits, _stream(stream))
+    return _check("fp8_blockscaled_gemm_splitk_noalloc", st, raise_on_error)
 
 
 def fp8_blockscaled_gemm_splitk_plan(M, N, K, out):

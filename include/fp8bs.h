@@ -253,6 +253,28 @@ fp8bs_status fp8_blockscaled_gemm_splitk(int64_t M, int64_t N, int64_t K,
                                          int32_t splits, float* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_blockscaled_gemm_splitk_noalloc -- fp8_blockscaled_gemm_splitk without
+ * the workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It allocates nothing: the partials go to a scratch array of
+ * 64 MiB (67,108,864 bytes) that the library holds on each GPU for the life
+ * of the process; the first call on a device looks up that device's copy.
+ * splits * M * N * 4 bytes must fit it: splits == 0 takes the planner's count
+ * capped to what fits (1, no split, if two do not), and an explicit count
+ * that does not fit is rejected with FP8BS_ERR_SHAPE.  Results are those of
+ * fp8_blockscaled_gemm_splitk with the same split count.  Calls that overlap
+ * in time on one GPU share the scratch and race: serialize them (one stream,
+ * or events between streams).
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_blockscaled_gemm_splitk_noalloc(int64_t M, int64_t N, int64_t K,
+                                                 const uint8_t* a, int64_t lda,
+                                                 const float* sa, int64_t sa_stride_m, int64_t sa_stride_k,
+                                                 const uint8_t* b, int64_t ldb,
+                                                 const float* sb, int64_t sb_stride_n, int64_t sb_stride_k,
+                                                 fp8bs_bscale bscale, void* c, int64_t ldc, fp8bs_out out,
+                                                 int32_t splits, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_blockscaled_gemm_splitk_plan -- the split count the planner chooses
  * for this shape and output type (1 when splitting does not pay: the
  * estimate prices the extra partial traffic and the second launch against
