@@ -13,7 +13,7 @@ that the 256 MB last-level cache cannot serve them.
 The other workloads of the path are timed after it (median of --reps
 repetitions, each kernel bracketed by HIP events on the launch stream):
     tiny_linear      X [256 x 512], W [512 x 512] (quantizers, GEMM bf16/fp32)
-    mlp_backward     dY [4096 x 9728]: 1x128 and 128x1 quantization, X 128x1,
+    mlp_backward     dY [4096 x 9728]: 1x128 and 128x1 quantization in one pass, X 128x1,
                      W 128x128 with its transposed code copy, dgrad and wgrad
                      GEMMs (fp32 out)
     moe_blockwise    Qwen3-30B-A3B MoE layer (16384 tokens, 128 experts, top 8):
@@ -80,6 +80,12 @@ def parse():
 def qbytes_row(rows, cols, group=128, scale_bytes=4):
     """Quantizer algorithmic bytes: bf16 in, one code byte out, one scale per group."""
     return rows * cols * 3 + rows * ((cols + group - 1) // group) * scale_bytes
+
+
+def qbytes_dual(rows, cols, group=128, scale_bytes=4):
+    """Both axes from one read: bf16 in once, codes and scales of the row
+    groups and of the column groups out."""
+    return rows * cols * 4 + (rows * ((cols + group - 1) // group) + cols * ((rows + group - 1) // group)) * scale_bytes
 
 
 def qbytes_block2d(batch, rows, cols, transposed=False):
@@ -237,10 +243,10 @@ def wl_mlp_backward(torch, ops, inputs, to_dev, R):
     dx = torch.empty((T, I), dtype=torch.float32, device="cuda")
     dw = torch.empty((O, I), dtype=torch.float32, device="cuda")
     return [
-        ("quant_dy_1x128", lambda i: ops.fp8_quant_rowblock(dys[i % R], T, O, O, ops.AXIS_ROW, qdy, O, sdy, 1, T),
-         ("GB/s", qbytes_row(T, O))),
-        ("quant_dy_128x1", lambda i: ops.fp8_quant_rowblock(dys[i % R], T, O, O, ops.AXIS_COL, qdyt, T, sdyt, 1, O),
-         ("GB/s", qbytes_row(O, T))),
+        # dY in 1x128 groups (dgrad) and 128x1 groups along tokens (wgrad) from one read
+        ("quant_dy_dual_axis", lambda i: ops.fp8_quant_dual_axis(dys[i % R], T, O, O, 0, qdy, O, sdy, 1, T, qdyt, T,
+                                                                 sdyt, 1, O),
+         ("GB/s", qbytes_dual(T, O))),
         ("quant_x_128x1", lambda i: ops.fp8_quant_rowblock(xs[i % R], T, I, I, ops.AXIS_COL, qxt, T, sxt, 1, I),
          ("GB/s", qbytes_row(I, T))),
         ("quant_w_128x128_with_transpose", lambda i: ops.fp8_quant_block2d(w, 1, O, I, I, qw, I, qwt, O, sw),
@@ -283,8 +289,8 @@ def wl_up_proj_rowwise(torch, ops, inputs, to_dev, R):
 
 def wl_mlp_backward_mxfp8(torch, ops, inputs, to_dev, R):
     """The backward GEMMs of mlp_backward in MXFP8: dY 1x32 along O for
-    dgrad, W re-quantized 32x1 along O (transposed), dY and X re-quantized
-    32x1 along tokens (transposed) for wgrad."""
+    dgrad and 32x1 along tokens (transposed) for wgrad, in one pass; W
+    re-quantized 32x1 along O (transposed) and X 32x1 along tokens."""
     d = inputs.qwen3_4b_mlp_backward(2)
     T, O = d["dy"].shape
     I = d["x"].shape[1]
@@ -299,10 +305,9 @@ def wl_mlp_backward_mxfp8(torch, ops, inputs, to_dev, R):
     dx = torch.empty((T, I), dtype=torch.float32, device="cuda")
     dw = torch.empty((O, I), dtype=torch.float32, device="cuda")
     return [
-        ("mx_quant_dy", lambda i: ops.mxfp8_quant(dys[i % R], T, O, O, qdy, O, sdy, O // 32, 1),
-         ("GB/s", qbytes_row(T, O, 32, 1))),
-        ("mx_quant_dy_t", lambda i: ops.mxfp8_quant_t(dys[i % R], T, O, O, qdyt, T, sdyt, T // 32, 1),
-         ("GB/s", qbytes_row(O, T, 32, 1))),
+        ("mx_quant_dy_dual_axis", lambda i: ops.fp8_quant_dual_axis(dys[i % R], T, O, O, 1, qdy, O, sdy, O // 32, 1,
+                                                                    qdyt, T, sdyt, T // 32, 1),
+         ("GB/s", qbytes_dual(T, O, 32, 1))),
         ("mx_quant_x_t", lambda i: ops.mxfp8_quant_t(xs[i % R], T, I, I, qxt, T, sxt, T // 32, 1),
          ("GB/s", qbytes_row(I, T, 32, 1))),
         ("mx_quant_w_t", lambda i: ops.mxfp8_quant_t(w, O, I, I, qwt, O, swt, O // 32, 1),

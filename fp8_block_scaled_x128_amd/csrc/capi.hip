@@ -530,6 +530,34 @@ fp8bs_status mxfp8_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_
                     "mxfp8_quant_t");
 }
 
+fp8bs_status fp8_quant_dual_axis(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t mx, uint8_t* q,
+                                 int64_t ld_q, void* s, int64_t s_stride_row, int64_t s_stride_group, uint8_t* qt,
+                                 int64_t ld_qt, void* st, int64_t st_stride_row, int64_t st_stride_group,
+                                 hipStream_t stream) {
+    if (mx != 0 && mx != 1) return fail(FP8BS_ERR_UNSUPPORTED, "mx %d", (int)mx);
+    if (rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    const int64_t rmul = mx ? 32 : 16, cmul = mx ? 32 : 8;
+    if (rows % rmul || cols % cmul)
+        return fail(FP8BS_ERR_SHAPE, "rows %% %lld and cols %% %lld must be 0 (rows=%lld cols=%lld)", (long long)rmul,
+                    (long long)cmul, (long long)rows, (long long)cols);
+    // grid: 128-row tiles in x, 128-column tiles in y (at most 65535)
+    if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2 || (cols + 127) / 128 > 65535)
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || cols == 0) return ok();
+    if (!x || !q || !s || !qt || !st) return fail(FP8BS_ERR_NULL, "x, q, s, qt and st are required");
+    if (ld_x < cols || ld_q < cols || ld_qt < rows)
+        return fail(FP8BS_ERR_STRIDE, "ld_x >= cols, ld_q >= cols and ld_qt >= rows required");
+    if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
+    if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    if (ld_qt % 8 || !aligned(qt, 8)) return fail(FP8BS_ERR_ALIGN, "qt must be 8-byte aligned with ld_qt %% 8 == 0");
+    if (!mx && (!aligned(s, 4) || !aligned(st, 4))) return fail(FP8BS_ERR_ALIGN, "s and st must be 4-byte aligned");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_quant_dual(x, rows, cols, ld_x, mx != 0, q, ld_q, s, s_stride_row, s_stride_group, qt, ld_qt,
+                                      st, st_stride_row, st_stride_group, stream),
+                    "fp8_quant_dual_axis");
+}
+
 fp8bs_status fp8_quant_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block_rows, uint8_t* q,
                             int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t stream) {
     if (block_rows != 1 && block_rows != 128) return fail(FP8BS_ERR_UNSUPPORTED, "block_rows %d", (int)block_rows);

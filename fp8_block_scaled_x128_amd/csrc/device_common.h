@@ -140,6 +140,25 @@ __device__ __forceinline__ void encode8(const float v[8], float s, uint32_t& w0,
     w1 = enc4(qv[4], qv[5], qv[6], qv[7]);
 }
 
+// The same codes as encode8 with the group's reciprocal y = RN(1 / s)
+// supplied by the caller (read only when s >= kFastDivMinScale), for kernels
+// that compute each scale once and share it between lanes.
+__device__ __forceinline__ void encode8_y(const float v[8], float s, float y, uint32_t& w0, uint32_t& w1) {
+    float qv[8];
+    if (s >= kFastDivMinScale) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = div_by_scale(v[i], s, y);
+    } else if (s > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = v[i] / s;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = 0.0f;
+    }
+    w0 = enc4(qv[0], qv[1], qv[2], qv[3]);
+    w1 = enc4(qv[4], qv[5], qv[6], qv[7]);
+}
+
 __device__ __forceinline__ void unpack8(const uint4 raw, float v[8]) {
     v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x);
     v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);

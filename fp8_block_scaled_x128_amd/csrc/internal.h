@@ -21,6 +21,11 @@ hipError_t launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_
                            uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st);
 hipError_t launch_mx_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qt, int64_t ld_qt,
                              uint8_t* s, int64_t ssr, int64_t ssg, hipStream_t st);
+// Row groups (1x128, or 1x32 MX) with row-major codes and column groups
+// (128x1, or 32x1 MX) with transposed codes from one read of x.
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, bool mx, uint8_t* q,
+                             int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint8_t* qt, int64_t ld_qt, void* st,
+                             int64_t sstr, int64_t sstg, hipStream_t stream);
 hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t rows, int64_t I, int64_t ld_in, int mx, uint8_t* q,
                                  int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint16_t* h, int64_t ld_h,
                                  hipStream_t st);

@@ -343,6 +343,132 @@ __global__ void __launch_bounds__(kThreads) k_quant_col_t_lds(const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------
+// Both groupings of one tensor from one read of it: 1x128 groups along rows
+// (codes row-major) and 128x1 groups along columns (codes transposed), or,
+// with MX, 1x32 and 32x1 blocks with UE8M0 scales.  An output gradient dY
+// feeds the data-gradient GEMM through its row groups and the weight-gradient
+// GEMM through its column groups; quantized here in one pass, the two share
+// one HBM read of the bf16 tensor (2 bytes per element instead of 4).
+// One workgroup per 128 x 128 tile; thread t holds rows 8 (t / 16) .. +7 and
+// columns 8 (t % 16) .. +7 of it.
+//   Row groups: the 16 lanes of a DPP row hold one tile row, as in the
+//   row-group quantizer.
+//   Column groups: per-lane maxima of the 8 rows (bf16 magnitudes, two per
+//   word, as in the transposed quantizer), then over the wave's 4 row
+//   phases, which make a 32x1 MX block; for 128x1 the 4 waves' maxima meet
+//   in LDS, where the first 128 threads turn them into one scale and
+//   reciprocal per column.  Column codes are packed along rows, so each lane
+//   writes 8 consecutive bytes of a transposed row.
+// ---------------------------------------------------------------------------
+template <bool MX>
+__global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
+                                                         int64_t ld_x, uint8_t* __restrict__ q, int64_t ld_q,
+                                                         void* __restrict__ s, int64_t ssr, int64_t ssg,
+                                                         uint8_t* __restrict__ qt, int64_t ld_qt,
+                                                         void* __restrict__ st, int64_t sstr, int64_t sstg) {
+    __shared__ __attribute__((aligned(16))) uint4 red[MX ? 1 : 4][16];
+    __shared__ float csc[MX ? 1 : 128], cyr[MX ? 1 : 128];
+    const int t = threadIdx.x;
+    const int cc = t & 15, ph = t >> 4, wv = t >> 6;
+    const int32_t r0 = (int32_t)blockIdx.x * 128, c0 = (int32_t)blockIdx.y * 128;
+    const int32_t c = c0 + 8 * cc, rb = r0 + 8 * ph;
+    // rows % 32 == 0 (MX) or % 16 == 0, cols % 32 == 0 (MX) or % 8 == 0: a
+    // lane's 8 x 8 piece, and each 1x32 and 32x1 block, is whole or empty.
+    const bool valid = c < cols && rb < rows;
+    uint4 raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        raw[i] = make_uint4(0, 0, 0, 0);
+        if (valid) raw[i] = load_nt16(x + (int64_t)(rb + i) * ld_x + c);
+    }
+    // row groups
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float v[8];
+        unpack8(raw[i], v);
+        const int32_t r = rb + i;
+        uint32_t w0, w1;
+        if (!MX) {
+            const float amax = group16_max(absmax8(v));
+            const float sc = amax / kE4M3Max;
+            encode8(v, sc, w0, w1);
+            if (rb < rows && cc == 0)
+                static_cast<float*>(s)[(int64_t)r * ssr + (int64_t)blockIdx.y * ssg] = sc;
+        } else {
+            const float amax = group4_max(absmax8(v));
+            const int e = mx_exponent(amax);
+            const float f = pow2_neg(e);
+            if (amax == 0.0f) {
+                w0 = 0u; w1 = 0u;
+            } else {
+                w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+                w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+            }
+            if (valid && (cc & 3) == 0)
+                static_cast<uint8_t*>(s)[(int64_t)r * ssr + (int64_t)(c / 32) * ssg] = (uint8_t)(e + 127);
+        }
+        if (valid) *reinterpret_cast<uint2*>(q + (int64_t)r * ld_q + c) = make_uint2(w0, w1);
+    }
+    // column groups: maxima of |bf16| over the lane's rows, then the wave's
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) m[w] = pkmax_u16(m[w], word_at(raw[i], w) & 0x7fff7fffu);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        m[w] = pkmax_u16(m[w], (uint32_t)__shfl_xor((int)m[w], 16, 64));
+        m[w] = pkmax_u16(m[w], (uint32_t)__shfl_xor((int)m[w], 32, 64));
+    }
+    float csv[8], cyv[8];
+    if (!MX) {
+        if ((t & 63) < 16) red[wv][cc] = make_uint4(m[0], m[1], m[2], m[3]);
+        __syncthreads();
+        if (t < 128) {
+            const int j = t;                     // tile column
+            uint32_t mw = 0u;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mw = pkmax_u16(mw, word_at(red[w][j >> 3], (j & 7) >> 1));
+            const float amax = __uint_as_float((j & 1) ? (mw & 0xffff0000u) : (mw << 16));
+            const float sc = amax / kE4M3Max;
+            csc[j] = sc;
+            cyr[j] = sc >= kFastDivMinScale ? 1.0f / sc : 0.0f;
+            if (c0 + j < cols) static_cast<float*>(st)[(int64_t)(c0 + j) * sstr + (int64_t)blockIdx.x * sstg] = sc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { csv[k] = csc[8 * cc + k]; cyv[k] = cyr[8 * cc + k]; }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t wd = word_at(raw[i], k >> 1);
+            v[i] = (k & 1) ? bf16_hi(wd) : bf16_lo(wd);
+        }
+        uint32_t w0, w1;
+        if (!MX) {
+            encode8_y(v, csv[k], cyv[k], w0, w1);
+        } else {
+            const uint32_t mw = m[k >> 1];
+            const float amax = __uint_as_float((k & 1) ? (mw & 0xffff0000u) : (mw << 16));
+            const int e = mx_exponent(amax);
+            const float f = pow2_neg(e);
+            if (amax == 0.0f) {
+                w0 = 0u; w1 = 0u;
+            } else {
+                w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+                w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
+            }
+            if (valid && (t & 63) < 16)
+                static_cast<uint8_t*>(st)[(int64_t)(c + k) * sstr + (int64_t)(rb / 32) * sstg] = (uint8_t)(e + 127);
+        }
+        if (valid) *reinterpret_cast<uint2*>(qt + (int64_t)(c + k) * ld_qt + rb) = make_uint2(w0, w1);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 128x128 block quantizer, one workgroup per block, one HBM read of the
 // block.  Optional transposed copy: the block's codes are staged in LDS and
 // re-read as 4x4 byte squares that are transposed in registers (v_perm).
@@ -715,6 +841,20 @@ hipError_t launch_mx_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int6
     else
         hipLaunchKernelGGL(k_quant_col_t_lds<true>, dim3((unsigned)((cols + 63) / 64), gy), dim3(kThreads), 0, st, x,
                            (int32_t)rows, (int32_t)cols, ld_x, qt, ld_qt, (void*)s, ssr, ssg);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, bool mx, uint8_t* q,
+                             int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint8_t* qt, int64_t ld_qt, void* st,
+                             int64_t sstr, int64_t sstg, hipStream_t stream) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)((cols + 127) / 128));
+    if (mx)
+        hipLaunchKernelGGL(k_quant_dual<true>, grid, dim3(kThreads), 0, stream, x, (int32_t)rows, (int32_t)cols, ld_x,
+                           q, ld_q, s, ssr, ssg, qt, ld_qt, st, sstr, sstg);
+    else
+        hipLaunchKernelGGL(k_quant_dual<false>, grid, dim3(kThreads), 0, stream, x, (int32_t)rows, (int32_t)cols, ld_x,
+                           q, ld_q, s, ssr, ssg, qt, ld_qt, st, sstr, sstg);
     return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_linear", "fp8_q
            "fp8_blockscaled_gemm_splitk", "fp8_blockscaled_gemm_splitk_noalloc", "fp8_blockscaled_gemm_splitk_plan",
            "fp8_grouped_gemm", "fp8_grouped_gemm_ws_size", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
            "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
+           "fp8_quant_dual_axis",
            "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
 
@@ -78,6 +79,7 @@ def load():
             "fp8_moe_combine": [P, I64, I64, I64, P, P, I64, I32, P, I64, INT, P],
             "mxfp8_quant": [P, I64, I64, I64, P, I64, P, I64, I64, P],
             "mxfp8_quant_t": [P, I64, I64, I64, P, I64, P, I64, I64, P],
+            "fp8_quant_dual_axis": [P, I64, I64, I64, I32, P, I64, P, I64, I64, P, I64, P, I64, I64, P],
             "fp8_quant_pow2": [P, I64, I64, I64, I32, P, I64, P, I64, P],
             "fp8_blockscaled_gemm_pow2": [I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P, I64, INT, P],
             "mxfp8_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, INT, P],
@@ -254,6 +256,13 @@ def mxfp8_quant_t(x, rows, cols, ld_x, qt, ld_qt, s, s_stride_row, s_stride_grou
     return _check("mxfp8_quant_t", st, raise_on_error)
 
 
+def fp8_quant_dual_axis(x, rows, cols, ld_x, mx, q, ld_q, s, s_stride_row, s_stride_group, qt, ld_qt, st,
+                        st_stride_row, st_stride_group, stream=None, raise_on_error=True):
+    r = load().fp8_quant_dual_axis(_p(x), rows, cols, ld_x, mx, _p(q), ld_q, _p(s), s_stride_row, s_stride_group,
+                                   _p(qt), ld_qt, _p(st), st_stride_row, st_stride_group, _stream(stream))
+    return _check("fp8_quant_dual_axis", r, raise_on_error)
+
+
 def fp8_quant_pow2(x, rows, cols, ld_x, block_rows, q, ld_q, s, ld_s, stream=None, raise_on_error=True):
     st = load().fp8_quant_pow2(_p(x), rows, cols, ld_x, block_rows, _p(q), ld_q, _p(s), ld_s, _stream(stream))
     return _check("fp8_quant_pow2", st, raise_on_error)
@@ -306,6 +315,27 @@ def quant_rowblock(x: torch.Tensor, axis: int = AXIS_ROW, scale_layout: str = "m
         ssr, ssg = ng, 1
     fp8_quant_rowblock(x, rows, cols, x.stride(0), axis, q, ld_q, s, ssr, ssg)
     return q, s
+
+
+def quant_dual_axis(x: torch.Tensor, mx: bool = False):
+    """Row groups and column groups of a bf16 [rows, cols] tensor from one
+    read: (q [rows, cols], s, qt [cols, rows], st).  FP32 scales (mx False):
+    s is a [rows, cols/128] view of a [cols/128, rows] buffer and st a
+    [cols, rows/128] view of a [rows/128, cols] buffer (the M-major layouts
+    the GEMMs read); MX: uint8 s [rows, cols/32] and st [cols, rows/32],
+    row-major."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    q, qt = _u8((rows, cols), x.device), _u8((cols, rows), x.device)
+    if mx:
+        s, st = _u8((rows, cols // 32), x.device), _u8((cols, rows // 32), x.device)
+        fp8_quant_dual_axis(x, rows, cols, x.stride(0), 1, q, cols, s, cols // 32, 1, qt, rows, st, rows // 32, 1)
+        return q, s, qt, st
+    ng, ngt = (cols + 127) // 128, (rows + 127) // 128
+    sbuf = torch.empty((ng, rows), dtype=torch.float32, device=x.device)
+    stbuf = torch.empty((ngt, cols), dtype=torch.float32, device=x.device)
+    fp8_quant_dual_axis(x, rows, cols, x.stride(0), 0, q, cols, sbuf, 1, rows, qt, rows, stbuf, 1, cols)
+    return q, sbuf.t(), qt, stbuf.t()
 
 
 def quant_linear(x: torch.Tensor, w: torch.Tensor):

@@ -520,6 +520,40 @@ fp8bs_status mxfp8_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int64_
                            int64_t s_stride_group, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_quant_dual_axis -- both quantizations a tensor needs when one GEMM
+ * contracts over its columns and another over its rows, from one read of
+ * it.  The output gradient dY of a block-wise FP8 linear layer is the case:
+ * the data-gradient GEMM dX = dY W takes dY in per-token 1x128 groups
+ * ("Unified FP8: Beyond Mixed Precision...", section "FP8 Quantization",
+ * per-token gradients), the weight-gradient GEMM dW = dY^T X in 128x1
+ * groups along tokens; with mx == 1 the MXFP8 recipe's 1x32 blocks and
+ * their re-quantization along the other axis ("Low Precision RL", section
+ * "3. Unified MXFP8 (Blackwell)").  The results are identical to
+ *   mx == 0: fp8_quant_rowblock(x, ..., FP8BS_AXIS_ROW, q, ld_q, s, ...)
+ *            and fp8_quant_rowblock(x, ..., FP8BS_AXIS_COL, qt, ld_qt, st, ...);
+ *   mx == 1: mxfp8_quant(x, ..., q, ld_q, s, ...)
+ *            and mxfp8_quant_t(x, ..., qt, ld_qt, st, ...);
+ * the bf16 tensor is read once (2 bytes per element instead of 4).
+ *
+ * x  : bf16 [rows][ld_x].
+ * q  : [rows][ld_q] codes of the row groups; scale of (row r, group g =
+ *      col / 128, or col / 32 with mx) at s[r * s_stride_row + g * s_stride_group].
+ * qt : [cols][ld_qt] codes of the column groups, the row axis contiguous;
+ *      scale of (column c, group g = row / 128, or row / 32 with mx) at
+ *      st[c * st_stride_row + g * st_stride_group].
+ * s, st : fp32 scales (mx == 0) or UE8M0 bytes (mx == 1).
+ * Requirements: rows % 16 == 0 and cols % 8 == 0 (mx: rows % 32 == 0 and
+ * cols % 32 == 0); ceil(cols / 128) <= 65535; x 16-byte aligned with
+ * ld_x % 8 == 0, ld_x >= cols; q and qt 8-byte aligned with ld_q % 8 == 0,
+ * ld_q >= cols, ld_qt % 8 == 0, ld_qt >= rows; fp32 scales 4-byte aligned.
+ * The output buffers must not overlap one another.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_quant_dual_axis(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t mx,
+                                 uint8_t* q, int64_t ld_q, void* s, int64_t s_stride_row, int64_t s_stride_group,
+                                 uint8_t* qt, int64_t ld_qt, void* st, int64_t st_stride_row,
+                                 int64_t st_stride_group, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * mxfp8_gemm -- C = A B^T on MXFP8 operands (dense when G == 0, grouped over
  * experts when G >= 1), exact power-of-two block scaling inside gfx950's
  * scaled FP8 matrix instructions, FP32 accumulation.
