@@ -25,9 +25,10 @@ repetitions, each kernel bracketed by HIP events on the launch stream):
     moe_mxfp8_fused  the MXFP8 layer with the fused gate_up epilogue
 
 Prints ONE JSON line: value = GEMM FLOPs of the headline step / step time
-(TFLOP/s); per-kernel times with TFLOP/s or GB/s against MI355X's peaks; a
-roofline object for the dominant kernel (the block-scaled GEMM); a CPU-oracle
-baseline on a bounded sample.
+(TFLOP/s); per-kernel times with TFLOP/s or GB/s against MI355X's peaks (GB/s
+figures also against a timed 512 MiB device copy, copy_context); a roofline
+object for the dominant kernel (the block-scaled GEMM); a CPU-oracle baseline
+on a bounded sample.
 """
 from __future__ import annotations
 
@@ -719,6 +720,22 @@ def main():
         torch.cuda.empty_cache()
     if others:
         res["workloads"] = others
+
+    # streaming-copy context: a plain 512 MiB device copy, timed like the
+    # kernels; every GB/s figure also gets its fraction of this rate
+    ccount = (512 << 20) // 4
+    ca = torch.ones(ccount, dtype=torch.float32, device=dev)
+    cb = torch.empty_like(ca)
+    cms = time_sequence(torch, stream, [lambda i: cb.copy_(ca)], 20, 5, 20.0)[0]
+    crate = 2.0 * ccount * 4 / (cms[0] * 1e-3) / 1e9
+    res["copy_context"] = {"bytes_read": ccount * 4, "bytes_written": ccount * 4, "ms": round(cms[0], 5),
+                           "GB/s": round(crate, 1), "frac_of_peak": round(crate / PEAK_HBM_GBS, 4)}
+    del ca, cb
+    kernel_sets = [res["kernels"]] + [w["kernels"] for w in res.get("workloads", {}).values()]
+    for ks in kernel_sets:
+        for e in ks.values():
+            if "GB/s" in e:
+                e["frac_of_copy"] = round(e["GB/s"] / crate, 4)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
