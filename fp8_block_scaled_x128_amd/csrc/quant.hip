@@ -368,6 +368,7 @@ __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restr
                                                          void* __restrict__ st, int64_t sstr, int64_t sstg) {
     __shared__ __attribute__((aligned(16))) uint4 red[MX ? 1 : 4][16];
     __shared__ float csc[MX ? 1 : 128], cyr[MX ? 1 : 128];
+    __shared__ uint32_t cexp[MX ? 128 : 1];     // MX: the 4 row blocks' scale bytes of each column
     const int t = threadIdx.x;
     const int cc = t & 15, ph = t >> 4, wv = t >> 6;
     const int32_t r0 = (int32_t)blockIdx.x * 128, c0 = (int32_t)blockIdx.y * 128;
@@ -375,6 +376,15 @@ __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restr
     // rows % 32 == 0 (MX) or % 16 == 0, cols % 32 == 0 (MX) or % 8 == 0: a
     // lane's 8 x 8 piece, and each 1x32 and 32x1 block, is whole or empty.
     const bool valid = c < cols && rb < rows;
+    // MX scale bytes leave as one 4-byte word per row (its tile's 4 column
+    // blocks) and per column (its 4 row blocks) where the tile is whole, the
+    // 4 bytes are adjacent and the word is aligned; otherwise byte by byte.
+    // (Single bytes from different lanes and waves, each its own partial
+    // write of a scale row, cost a sixth of the kernel's time on dY.)
+    const bool row_words = MX && c0 + 128 <= cols && ssg == 1 && ssr % 4 == 0 &&
+                           (reinterpret_cast<uintptr_t>(s) & 3) == 0;
+    const bool col_words = MX && r0 + 128 <= rows && sstg == 1 && sstr % 4 == 0 &&
+                           (reinterpret_cast<uintptr_t>(st) & 3) == 0;
     uint4 raw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -404,8 +414,16 @@ __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restr
                 w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
                 w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
             }
-            if (valid && (cc & 3) == 0)
-                static_cast<uint8_t*>(s)[(int64_t)r * ssr + (int64_t)(c / 32) * ssg] = (uint8_t)(e + 127);
+            const uint32_t sb = (uint32_t)(e + 127);
+            if (row_words) {
+                // lanes 4j of the row's 16 hold column block j
+                const uint32_t wd = sb | ((uint32_t)__shfl((int)sb, 4, 16) << 8) |
+                                    ((uint32_t)__shfl((int)sb, 8, 16) << 16) | ((uint32_t)__shfl((int)sb, 12, 16) << 24);
+                if (rb < rows && cc == 0)
+                    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(s) + (int64_t)r * ssr + c0 / 32) = wd;
+            } else if (valid && (cc & 3) == 0) {
+                static_cast<uint8_t*>(s)[(int64_t)r * ssr + (int64_t)(c / 32) * ssg] = (uint8_t)sb;
+            }
         }
         if (valid) *reinterpret_cast<uint2*>(q + (int64_t)r * ld_q + c) = make_uint2(w0, w1);
     }
@@ -461,10 +479,18 @@ __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restr
                 w0 = enc4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
                 w1 = enc4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
             }
-            if (valid && (t & 63) < 16)
-                static_cast<uint8_t*>(st)[(int64_t)(c + k) * sstr + (int64_t)(rb / 32) * sstg] = (uint8_t)(e + 127);
+            if ((t & 63) < 16) {
+                if (col_words) reinterpret_cast<uint8_t*>(cexp)[(8 * cc + k) * 4 + wv] = (uint8_t)(e + 127);
+                else if (valid)
+                    static_cast<uint8_t*>(st)[(int64_t)(c + k) * sstr + (int64_t)(rb / 32) * sstg] = (uint8_t)(e + 127);
+            }
         }
         if (valid) *reinterpret_cast<uint2*>(qt + (int64_t)(c + k) * ld_qt + rb) = make_uint2(w0, w1);
+    }
+    if (col_words) {
+        __syncthreads();
+        if (t < 128 && c0 + t < cols)
+            *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(st) + (int64_t)(c0 + t) * sstr + r0 / 32) = cexp[t];
     }
 }
 

@@ -166,3 +166,25 @@ def test_dual_argument_errors_and_empty():
     assert call(0, 256, 0) == 0 and call(64, 0, 1) == 0
     torch.cuda.synchronize()
     assert torch.all(q == 0xA5) and torch.all(qt == 0xA5)
+
+
+def test_dual_mx_padded_scale_rows():
+    """MX scales in padded rows (8 bytes for 5 blocks): the whole first tile
+    writes each row's and column's 4 scale bytes as one word, the partial
+    second tile byte by byte; the padding bytes stay untouched."""
+    R = C = 160
+    x = _specials(_bits((R, C), 15), True)
+    xd = dev_bf16(x)
+    SENT = 0x5A
+    q, qt = torch.empty((R, C), dtype=torch.uint8, device="cuda"), torch.empty((C, R), dtype=torch.uint8, device="cuda")
+    s = torch.full((R, 8), SENT, dtype=torch.uint8, device="cuda")
+    st = torch.full((C, 8), SENT, dtype=torch.uint8, device="cuda")
+    ops.fp8_quant_dual_axis(xd, R, C, C, 1, q, C, s, 8, 1, qt, R, st, 8, 1)
+    torch.cuda.synchronize()
+    qr, sr = oracle.mx_quant_1x32(x)
+    qtr, str_ = oracle.mx_quant_32x1_t(x)
+    _same(q, qr, "row codes")
+    _same(qt, qtr, "column codes")
+    _same(s[:, :5], sr, "row scales")
+    _same(st[:, :5], str_, "column scales")
+    assert torch.all(s[:, 5:] == SENT) and torch.all(st[:, 5:] == SENT)
