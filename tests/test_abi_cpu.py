@@ -149,6 +149,22 @@ def test_host_validation_rejects_before_launch(lib):
     assert mxs(256, 128, 256, lds=10) == 4        # scale leading dimension % 4
     assert mxs(256, 128, 256, hs=None) == 1       # NULL h scales
     assert mxs(0, 128, 256) == 0
+    # both axes of one tensor from one read
+    dual = lambda rows, cols, mx=0, x=fake, ld_x=None, q=fake, qt=fake, ld_qt=None, st=fake: ops.fp8_quant_dual_axis(
+        x, rows, cols, cols if ld_x is None else ld_x, mx, q, cols, fake, 1, 1, qt, rows if ld_qt is None else ld_qt,
+        st, 1, 1, stream=0, raise_on_error=False)
+    assert dual(128, 128, mx=2) == 5              # bad mx
+    assert dual(120, 128) == 2                    # rows % 16
+    assert dual(128, 100) == 2                    # cols % 8
+    assert dual(80, 128, mx=1) == 2               # MX rows % 32
+    assert dual(128, 64 * 1024 * 128, ld_x=None) == 2   # more than 65535 column tiles
+    assert dual(128, 128, ld_x=64) == 3           # ld_x < cols
+    assert dual(128, 128, ld_qt=64) == 3          # ld_qt < rows
+    assert dual(128, 128, x=fake + 2) == 4        # misaligned x
+    assert dual(128, 128, qt=fake + 4) == 4       # qt not 8-byte aligned
+    assert dual(128, 128, st=fake + 2) == 4       # fp32 column scales not 4-byte aligned
+    assert dual(128, 128, q=None) == 1            # NULL row codes
+    assert dual(0, 128, x=None, q=None, qt=None, st=None) == 0
 
 
 def test_splitk_plan(lib):
@@ -194,3 +210,14 @@ def test_dense_tile_plan(lib):
     assert ops.fp8_blockscaled_gemm_plan(9728, 2560, 4096) == ((4, 128), None, 2560)
     assert lib.fp8_blockscaled_gemm_plan(128, 100, 128, ctypes.c_void_p(1 << 20)) == 2
     assert lib.fp8_blockscaled_gemm_plan(128, 128, 128, None) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with a message before any
+    device work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
