@@ -368,6 +368,8 @@ __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restr
                                                          void* __restrict__ st, int64_t sstr, int64_t sstg) {
     __shared__ __attribute__((aligned(16))) uint4 red[MX ? 1 : 4][16];
     __shared__ float csc[MX ? 1 : 128], cyr[MX ? 1 : 128];
+    __shared__ float rsc[MX ? 1 : 128], ryr[MX ? 1 : 128];          // FP32: row scales and reciprocals
+    __shared__ __attribute__((aligned(16))) float rpart[MX ? 1 : 128][MX ? 1 : 16];   // FP32: per-lane row maxima
     __shared__ uint32_t cexp[MX ? 128 : 1];     // MX: the 4 row blocks' scale bytes of each column
     const int t = threadIdx.x;
     const int cc = t & 15, ph = t >> 4, wv = t >> 6;
@@ -399,11 +401,10 @@ __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restr
         const int32_t r = rb + i;
         uint32_t w0, w1;
         if (!MX) {
-            const float amax = group16_max(absmax8(v));
-            const float sc = amax / kE4M3Max;
-            encode8(v, sc, w0, w1);
-            if (rb < rows && cc == 0)
-                static_cast<float*>(s)[(int64_t)r * ssr + (int64_t)blockIdx.y * ssg] = sc;
+            // FP32: the lane's part of the row maximum; the row's scale is
+            // formed once, by one thread, below
+            rpart[8 * ph + i][cc] = absmax8(v);
+            continue;
         } else {
             const float amax = group4_max(absmax8(v));
             const int e = mx_exponent(amax);
@@ -452,10 +453,32 @@ __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restr
             csc[j] = sc;
             cyr[j] = sc >= kFastDivMinScale ? 1.0f / sc : 0.0f;
             if (c0 + j < cols) static_cast<float*>(st)[(int64_t)(c0 + j) * sstr + (int64_t)blockIdx.x * sstg] = sc;
+        } else {
+            const int j = t - 128;               // tile row
+            const float4* pr = reinterpret_cast<const float4*>(&rpart[j][0]);
+            float amax = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 w4 = pr[u];
+                amax = fmaxf(amax, fmaxf(fmaxf(w4.x, w4.y), fmaxf(w4.z, w4.w)));
+            }
+            const float sc = amax / kE4M3Max;
+            rsc[j] = sc;
+            ryr[j] = sc >= kFastDivMinScale ? 1.0f / sc : 0.0f;
+            if (r0 + j < rows) static_cast<float*>(s)[(int64_t)(r0 + j) * ssr + (int64_t)blockIdx.y * ssg] = sc;
         }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < 8; ++k) { csv[k] = csc[8 * cc + k]; cyv[k] = cyr[8 * cc + k]; }
+        // row codes
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v[8];
+            unpack8(raw[i], v);
+            uint32_t w0, w1;
+            encode8_y(v, rsc[8 * ph + i], ryr[8 * ph + i], w0, w1);
+            if (valid) *reinterpret_cast<uint2*>(q + (int64_t)(rb + i) * ld_q + c) = make_uint2(w0, w1);
+        }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
