@@ -14,7 +14,7 @@ The other workloads of the path are timed after it (median of --reps
 repetitions, each kernel bracketed by HIP events on the launch stream):
     tiny_linear      X [256 x 512], W [512 x 512] (quantizers, GEMM bf16/fp32)
     mlp_backward     dY [4096 x 9728]: 1x128 and 128x1 quantization in one pass, X 128x1,
-                     W 128x128 with its transposed code copy, dgrad and wgrad
+                     W 128x128 (transposed codes only), dgrad and wgrad
                      GEMMs (fp32 out)
     moe_blockwise    Qwen3-30B-A3B MoE layer (16384 tokens, 128 experts, top 8):
                      X 1x128, W_gu / W_d 128x128, grouped gate_up GEMM, SiLU*mul
@@ -240,7 +240,7 @@ def wl_mlp_backward(torch, ops, inputs, to_dev, R):
     qdy, sdy = u8(T, O), f32(O // 128, T)                  # 1x128, M-major scales
     qdyt, sdyt = u8(O, T), f32(T // 128, O)                # 128x1 along tokens, transposed codes
     qxt, sxt = u8(I, T), f32(T // 128, I)
-    qw, qwt, sw = u8(O, I), u8(I, O), f32(O // 128, I // 128)
+    qwt, sw = u8(I, O), f32(O // 128, I // 128)
     dx = torch.empty((T, I), dtype=torch.float32, device="cuda")
     dw = torch.empty((O, I), dtype=torch.float32, device="cuda")
     return [
@@ -250,8 +250,9 @@ def wl_mlp_backward(torch, ops, inputs, to_dev, R):
          ("GB/s", qbytes_dual(T, O))),
         ("quant_x_128x1", lambda i: ops.fp8_quant_rowblock(xs[i % R], T, I, I, ops.AXIS_COL, qxt, T, sxt, 1, I),
          ("GB/s", qbytes_row(I, T))),
-        ("quant_w_128x128_with_transpose", lambda i: ops.fp8_quant_block2d(w, 1, O, I, I, qw, I, qwt, O, sw),
-         ("GB/s", qbytes_block2d(1, O, I, transposed=True))),
+        # dgrad reads W only through its transposed codes (the forward's quantization wrote the others)
+        ("quant_w_128x128_transposed", lambda i: ops.fp8_quant_block2d(w, 1, O, I, I, None, 0, qwt, O, sw),
+         ("GB/s", qbytes_block2d(1, O, I))),
         # dX [T, I] = dY [T, O] W [O, I]: B = W^T codes [I, O], scales sw read transposed
         ("gemm_dgrad_fp32", lambda i: ops.fp8_blockscaled_gemm(T, I, O, qdy, O, sdy, 1, T, qwt, O, sw, 1, I // 128,
                                                               ops.BSCALE_BLOCK128, dx, I, ops.OUT_FP32),
@@ -370,7 +371,7 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R, fused=False):
     f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
     qx, sx = u8(T, H), f32(H // 128, T)
     qgu, sgu = u8(E, N2, H), f32(E, N2 // 128, H // 128)
-    qd, qdt, sd = u8(E, I, H), u8(E, H, I), f32(E, I // 128, H // 128)
+    qdt, sd = u8(E, H, I), f32(E, I // 128, H // 128)
     gu = None if fused else torch.empty((rows, N2), dtype=torch.bfloat16, device="cuda")
     qh, sh = u8(rows, I), f32(I // 128, rows)
     y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
@@ -397,8 +398,9 @@ def wl_moe_blockwise(torch, ops, inputs, to_dev, R, fused=False):
          ("GB/s", qbytes_row(T, H))),
         ("quant_w_gate_up_128x128", lambda i: ops.fp8_quant_block2d(wgu, E, N2, H, H, qgu, H, None, 0, sgu),
          ("GB/s", qbytes_block2d(E, N2, H))),
-        ("quant_w_down_128x128_with_transpose", lambda i: ops.fp8_quant_block2d(wd, E, I, H, H, qd, H, qdt, I, sd),
-         ("GB/s", qbytes_block2d(E, I, H, transposed=True))),
+        # W_d is stored [in][out]: the down GEMM reads only its transposed codes
+        ("quant_w_down_128x128_transposed", lambda i: ops.fp8_quant_block2d(wd, E, I, H, H, None, 0, qdt, I, sd),
+         ("GB/s", qbytes_block2d(E, I, H))),
     ] + gate_up_steps + [
         # B[n = hidden, k = inter] = W_d[e]^T codes; scales sd[e][k/128][n/128] read transposed
         ("grouped_gemm_down", lambda i: ops.fp8_grouped_gemm(

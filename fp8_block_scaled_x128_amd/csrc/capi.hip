@@ -211,11 +211,11 @@ fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, i
     if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2 || batch > 65535 || (rows + 127) / 128 > 65535)
         return fail(FP8BS_ERR_SHAPE, "tensor too large");
     if (rows == 0 || cols == 0) return ok();
-    if (!w || !q || !s) return fail(FP8BS_ERR_NULL, "w, q and s are required");
-    if (ld_w < cols || ld_q < cols) return fail(FP8BS_ERR_STRIDE, "ld_w and ld_q must be >= cols");
+    if (!w || !s || (!q && !q_t)) return fail(FP8BS_ERR_NULL, "w, s and at least one of q and q_t are required");
+    if (ld_w < cols || (q && ld_q < cols)) return fail(FP8BS_ERR_STRIDE, "ld_w and ld_q must be >= cols");
     if (q_t && ld_qt < rows) return fail(FP8BS_ERR_STRIDE, "ld_qt < rows");
     if (ld_w % 8 || !aligned(w, 16)) return fail(FP8BS_ERR_ALIGN, "w must be 16-byte aligned with ld_w %% 8 == 0");
-    if (ld_q % 8 || !aligned(q, 8)) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
+    if (q && (ld_q % 8 || !aligned(q, 8))) return fail(FP8BS_ERR_ALIGN, "q must be 8-byte aligned with ld_q %% 8 == 0");
     if (q_t && (ld_qt % 16 || !aligned(q_t, 16))) return fail(FP8BS_ERR_ALIGN, "q_t must be 16-byte aligned with ld_qt %% 16 == 0");
     if (!aligned(s, 4)) return fail(FP8BS_ERR_ALIGN, "s must be 4-byte aligned");
     fp8bs_status d = check_device();

@@ -547,8 +547,9 @@ __device__ __forceinline__ void block2d_body(const uint16_t* __restrict__ w, int
     __shared__ float red[kThreads / 64];
     __shared__ __attribute__((aligned(16))) uint32_t ctile[TRANS ? 128 : 1][33];
     const int t = threadIdx.x;
+    const bool wq = q != nullptr;         // TRANS: the row-major codes may be skipped
     w += bz * (int64_t)rows * ld_w;
-    q += bz * (int64_t)rows * ld_q;
+    if (wq) q += bz * (int64_t)rows * ld_q;
     if (TRANS) qt += bz * (int64_t)cols * ld_qt;
     const int64_t s_idx = bz * (int64_t)nbr * lds + (int64_t)by * lds + bx;
     const int32_t r0 = by * 128, c0 = bx * 128;
@@ -593,7 +594,7 @@ __device__ __forceinline__ void block2d_body(const uint16_t* __restrict__ w, int
         }
         const int rl = (t >> 4) + 16 * i;
         const int32_t r = r0 + rl, c = c0 + cc * 8;
-        if (r < rows && c < cols) {
+        if (wq && r < rows && c < cols) {
             uint8_t* dst = q + (int64_t)r * ld_q + c;
             if (NT) store_nt8(dst, w0, w1);
             else *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);

@@ -127,14 +127,16 @@ fp8bs_status fp8_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols,
  * "2. Unified block-wise FP8 (DeepSeek-style)").
  *
  * w   : bf16 [batch][rows][ld_w]; matrix b starts at w + b * rows * ld_w.
- * q   : [batch][rows][ld_q] codes.
+ * q   : [batch][rows][ld_q] codes; may be NULL when q_t is given (a caller
+ *       that needs only the transposed copy, e.g. a weight stored [in][out]
+ *       or the data-gradient operand, then writes no row-major codes).
  * q_t : nullable; if given, the transposed codes [batch][cols][ld_qt]
  *       (the same codes, so a GEMM contracting over `rows` reads them with
- *       the same block scales transposed).
+ *       the same block scales transposed).  At least one of q and q_t.
  * s   : [batch][ceil(rows/128)][ceil(cols/128)] fp32, contiguous; the scale of
  *       block (i, j) of matrix b is s[(b * nbr + i) * nbc + j].
  * Requirements: batch >= 1; rows, cols >= 0; cols % 8 == 0 and ld_w % 8 == 0;
- * w 16-byte aligned; ld_q >= cols, ld_q % 8 == 0; if q_t: rows % 16 == 0,
+ * w 16-byte aligned; if q: ld_q >= cols, ld_q % 8 == 0; if q_t: rows % 16 == 0,
  * ld_qt >= rows, ld_qt % 16 == 0, q_t 16-byte aligned.
  * ------------------------------------------------------------------------ */
 fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, int64_t cols, int64_t ld_w,

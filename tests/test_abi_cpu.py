@@ -149,6 +149,12 @@ def test_host_validation_rejects_before_launch(lib):
     assert mxs(256, 128, 256, lds=10) == 4        # scale leading dimension % 4
     assert mxs(256, 128, 256, hs=None) == 1       # NULL h scales
     assert mxs(0, 128, 256) == 0
+    # 128x128 blocks: the row-major codes may be skipped only when the
+    # transposed copy is written
+    b2 = lambda q, qt: ops.fp8_quant_block2d(fake, 1, 128, 128, 128, q, 128, qt, 128, fake, stream=0,
+                                             raise_on_error=False)
+    assert b2(None, None) == 1
+    assert b2(None, fake + 8) == 4                # q_t must be 16-byte aligned
     # both axes of one tensor from one read
     dual = lambda rows, cols, mx=0, x=fake, ld_x=None, q=fake, qt=fake, ld_qt=None, st=fake: ops.fp8_quant_dual_axis(
         x, rows, cols, cols if ld_x is None else ld_x, mx, q, cols, fake, 1, 1, qt, rows if ld_qt is None else ld_qt,

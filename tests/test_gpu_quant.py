@@ -211,6 +211,25 @@ def test_block2d_qwen3_4b_weight_full():
     _assert_same_codes(qt, np.ascontiguousarray(qr.T))
 
 
+@pytest.mark.parametrize("shape", [(272, 200), (3, 384, 256), (768, 2048)])
+def test_block2d_transposed_codes_only(shape):
+    """q = NULL with q_t given: only the transposed codes and the scales are
+    written (a weight stored [in][out], or the data-gradient operand), equal
+    to the oracle's; a batch of matrices included."""
+    _say("block2d transposed only", shape)
+    w = _bits(shape, 6, 0.02, 0.0, 1.0)
+    ws = w if w.ndim == 3 else w[None]
+    B, R, C = ws.shape
+    qt = torch.full((B, C, R), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.empty((B, (R + 127) // 128, (C + 127) // 128), dtype=torch.float32, device="cuda")
+    ops.fp8_quant_block2d(dev_bf16(ws), B, R, C, C, None, 0, qt, R, s)
+    torch.cuda.synchronize()
+    for b in range(B):
+        qr, sr = oracle.quant_128x128(ws[b])
+        _assert_same_codes(qt[b], np.ascontiguousarray(qr.T))
+        _assert_same_scales(s[b], sr)
+
+
 # ------------------------------------------- both operands in one launch
 def _linear_check(x, w, qx, sx, qw, sw):
     qr, sr = oracle.quant_1x128(x)
