@@ -14,7 +14,7 @@ The other workloads of the path are timed after it (median of --reps
 repetitions, each kernel bracketed by HIP events on the launch stream):
     tiny_linear      X [256 x 512], W [512 x 512] (quantizers, GEMM bf16/fp32)
     mlp_backward     dY [4096 x 9728]: 1x128 and 128x1 quantization in one pass, X 128x1,
-                     W 128x128 (transposed codes only), dgrad and wgrad
+                     the transposed copy of the forward's W codes, dgrad and wgrad
                      GEMMs (fp32 out)
     moe_blockwise    Qwen3-30B-A3B MoE layer (16384 tokens, 128 experts, top 8):
                      X 1x128, W_gu / W_d 128x128, grouped gate_up GEMM, SiLU*mul
@@ -241,6 +241,10 @@ def wl_mlp_backward(torch, ops, inputs, to_dev, R):
     qdyt, sdyt = u8(O, T), f32(T // 128, O)                # 128x1 along tokens, transposed codes
     qxt, sxt = u8(I, T), f32(T // 128, I)
     qwt, sw = u8(I, O), f32(O // 128, I // 128)
+    # W's 128x128 codes and scales as the forward step leaves them (its
+    # fp8_quant_linear); the backward needs their transposed copy
+    qw = u8(O, I)
+    ops.fp8_quant_block2d(w, 1, O, I, I, qw, I, None, 0, sw)
     dx = torch.empty((T, I), dtype=torch.float32, device="cuda")
     dw = torch.empty((O, I), dtype=torch.float32, device="cuda")
     return [
@@ -250,9 +254,9 @@ def wl_mlp_backward(torch, ops, inputs, to_dev, R):
          ("GB/s", qbytes_dual(T, O))),
         ("quant_x_128x1", lambda i: ops.fp8_quant_rowblock(xs[i % R], T, I, I, ops.AXIS_COL, qxt, T, sxt, 1, I),
          ("GB/s", qbytes_row(I, T))),
-        # dgrad reads W only through its transposed codes (the forward's quantization wrote the others)
-        ("quant_w_128x128_transposed", lambda i: ops.fp8_quant_block2d(w, 1, O, I, I, None, 0, qwt, O, sw),
-         ("GB/s", qbytes_block2d(1, O, I))),
+        # dgrad reads W through the transposed copy of the forward's codes (128x128 blocks are
+        # transpose-invariant: the same scales, read with swapped strides)
+        ("transpose_w_codes", lambda i: ops.fp8_transpose_codes(qw, 1, O, I, I, qwt, O), ("GB/s", 2 * O * I)),
         # dX [T, I] = dY [T, O] W [O, I]: B = W^T codes [I, O], scales sw read transposed
         ("gemm_dgrad_fp32", lambda i: ops.fp8_blockscaled_gemm(T, I, O, qdy, O, sdy, 1, T, qwt, O, sw, 1, I // 128,
                                                               ops.BSCALE_BLOCK128, dx, I, ops.OUT_FP32),

@@ -224,6 +224,24 @@ fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, i
                     "fp8_quant_block2d");
 }
 
+fp8bs_status fp8_transpose_codes(const uint8_t* q, int64_t batch, int64_t rows, int64_t cols, int64_t ld_q,
+                                 uint8_t* q_t, int64_t ld_qt, hipStream_t stream) {
+    if (batch < 1 || rows < 0 || cols < 0) return fail(FP8BS_ERR_SHAPE, "batch=%lld rows=%lld cols=%lld",
+                                                      (long long)batch, (long long)rows, (long long)cols);
+    if (rows % 16 || cols % 16) return fail(FP8BS_ERR_SHAPE, "rows %% 16 and cols %% 16 must be 0");
+    if (rows > INT32_MAX / 2 || cols > INT32_MAX / 2 || batch > 65535 || (rows + 127) / 128 > 65535)
+        return fail(FP8BS_ERR_SHAPE, "tensor too large");
+    if (rows == 0 || cols == 0) return ok();
+    if (!q || !q_t) return fail(FP8BS_ERR_NULL, "q and q_t are required");
+    if (ld_q < cols || ld_qt < rows) return fail(FP8BS_ERR_STRIDE, "ld_q >= cols and ld_qt >= rows required");
+    if (ld_q % 16 || !aligned(q, 16)) return fail(FP8BS_ERR_ALIGN, "q must be 16-byte aligned with ld_q %% 16 == 0");
+    if (ld_qt % 16 || !aligned(q_t, 16))
+        return fail(FP8BS_ERR_ALIGN, "q_t must be 16-byte aligned with ld_qt %% 16 == 0");
+    fp8bs_status d = check_device();
+    if (d != FP8BS_OK) return d;
+    return launched(launch_transpose_codes(q, batch, rows, cols, ld_q, q_t, ld_qt, stream), "fp8_transpose_codes");
+}
+
 // The kernels address a scale array with 32-bit byte offsets within one
 // group: the largest offset (rows - 1) * s_row + (slices - 1) * s_slice, in
 // elements of `bytes`, must stay below 4 GiB, and strides must not be negative.

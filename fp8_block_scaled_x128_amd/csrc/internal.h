@@ -26,6 +26,9 @@ hipError_t launch_mx_quant_t(const uint16_t* x, int64_t rows, int64_t cols, int6
 hipError_t launch_quant_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, bool mx, uint8_t* q,
                              int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint8_t* qt, int64_t ld_qt, void* st,
                              int64_t sstr, int64_t sstg, hipStream_t stream);
+// Transposed copy of E4M3 codes, `batch` matrices [rows][ld_q] -> [cols][ld_qt].
+hipError_t launch_transpose_codes(const uint8_t* q, int64_t batch, int64_t rows, int64_t cols, int64_t ld_q,
+                                  uint8_t* qt, int64_t ld_qt, hipStream_t st);
 hipError_t launch_silu_mul_quant(const uint16_t* gu, int64_t rows, int64_t I, int64_t ld_in, int mx, uint8_t* q,
                                  int64_t ld_q, void* s, int64_t ssr, int64_t ssg, uint16_t* h, int64_t ld_h,
                                  hipStream_t st);

@@ -644,6 +644,63 @@ __global__ void __launch_bounds__(kThreads) k_quant_128x128(const uint16_t* __re
                                 (int32_t)blockIdx.y, (int32_t)blockIdx.z);
 }
 
+// ---------------------------------------------------------------------------
+// Transpose of E4M3 codes, one workgroup per 128 x 128 tile of matrix bz: the
+// tile's rows are staged in LDS as words and re-read as 4x4 byte squares,
+// transposed in registers (as for the quantizer's transposed copy).  The
+// backward pass of a layer whose weight the forward quantized in 128 x 128
+// blocks gets W's transposed operand from the forward's codes this way (the
+// block scales are the same, read with swapped strides), without reading
+// the bf16 weight again.  rows % 16 == 0 and cols % 16 == 0: every 16-byte
+// piece is whole or absent.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) k_transpose_codes(const uint8_t* __restrict__ q, int32_t rows,
+                                                              int32_t cols, int64_t ld_q, uint8_t* __restrict__ qt,
+                                                              int64_t ld_qt) {
+    __shared__ __attribute__((aligned(16))) uint32_t ctile[128][33];
+    const int t = threadIdx.x;
+    const int64_t bz = blockIdx.z;
+    q += bz * (int64_t)rows * ld_q;
+    qt += bz * (int64_t)cols * ld_qt;
+    const int32_t r0 = (int32_t)blockIdx.y * 128, c0 = (int32_t)blockIdx.x * 128;
+    // thread t: 16-byte piece t % 8 of rows t / 8 + 32 i
+    const int cp = t & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rl = (t >> 3) + 32 * i;
+        const int32_t r = r0 + rl, c = c0 + 16 * cp;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(q + (int64_t)r * ld_q + c);
+        ctile[rl][4 * cp] = v.x;
+        ctile[rl][4 * cp + 1] = v.y;
+        ctile[rl][4 * cp + 2] = v.z;
+        ctile[rl][4 * cp + 3] = v.w;
+    }
+    __syncthreads();
+    // thread -> 4 columns (cb) x 16 rows (rb); 8 consecutive lanes cover one
+    // 128-byte piece of a transposed row
+    const int rb = t & 7, cb = t >> 3;
+    uint32_t col[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rr = rb * 16 + 4 * j;
+        uint32_t o[4];
+        transpose4x4(ctile[rr][cb], ctile[rr + 1][cb], ctile[rr + 2][cb], ctile[rr + 3][cb], o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) col[k][j] = o[k];
+    }
+    const int32_t rs = r0 + rb * 16;
+    if (rs < rows) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int32_t c = c0 + cb * 4 + k;
+            if (c < cols)
+                *reinterpret_cast<uint4*>(qt + (int64_t)c * ld_qt + rs) =
+                    make_uint4(col[k][0], col[k][1], col[k][2], col[k][3]);
+        }
+    }
+}
+
 // The two operands of one linear layer in one launch: workgroups [0, w_blocks)
 // quantize 128 x 128 blocks of the weight W (row-major block order), the rest
 // run the 1x128 row-group quantizer over the activation X.  Both parts are
@@ -929,6 +986,15 @@ hipError_t launch_quant_128x128(const uint16_t* w, int64_t batch, int64_t rows, 
         if (nt) go(std::false_type{}, std::true_type{});
         else go(std::false_type{}, std::false_type{});
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_codes(const uint8_t* q, int64_t batch, int64_t rows, int64_t cols, int64_t ld_q,
+                                  uint8_t* qt, int64_t ld_qt, hipStream_t st) {
+    if (rows == 0 || cols == 0 || batch == 0) return hipSuccess;
+    const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128), (unsigned)batch);
+    hipLaunchKernelGGL(k_transpose_codes, grid, dim3(kThreads), 0, st, q, (int32_t)rows, (int32_t)cols, ld_q, qt,
+                       ld_qt);
     return hipGetLastError();
 }
 

@@ -144,6 +144,24 @@ fp8bs_status fp8_quant_block2d(const uint16_t* w, int64_t batch, int64_t rows, i
                                float* s, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_transpose_codes -- the transposed copy of `batch` matrices of E4M3
+ * codes: q_t[b][c][r] = q[b][r][c].  A 128x128 block scale is the same for a
+ * block and its transpose, so the codes and scales that fp8_quant_block2d or
+ * fp8_quant_linear wrote for a weight W in the forward pass give the
+ * data-gradient GEMM dX = dY W its operand W^T (codes from here, the same
+ * scales read with swapped strides) without reading the bf16 weight again
+ * ("Low Precision RL", section "2. Unified block-wise FP8 (DeepSeek-style)":
+ * 128x128 weight blocks, used by the forward and the backward GEMMs).
+ *
+ * q   : [batch][rows][ld_q] codes.   q_t : [batch][cols][ld_qt] codes.
+ * Requirements: batch >= 1; rows % 16 == 0 and cols % 16 == 0; q and q_t
+ * 16-byte aligned with ld_q % 16 == 0, ld_q >= cols, ld_qt % 16 == 0,
+ * ld_qt >= rows; q and q_t must not overlap.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_transpose_codes(const uint8_t* q, int64_t batch, int64_t rows, int64_t cols, int64_t ld_q,
+                                 uint8_t* q_t, int64_t ld_qt, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_quant_linear -- both operands of one block-wise FP8 linear layer in
  * one launch: the activation X [rows][cols] in 1x128 per-token groups and
  * the weight W [w_rows][cols] in 128x128 blocks, each with the scale

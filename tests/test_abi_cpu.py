@@ -155,6 +155,18 @@ def test_host_validation_rejects_before_launch(lib):
                                              raise_on_error=False)
     assert b2(None, None) == 1
     assert b2(None, fake + 8) == 4                # q_t must be 16-byte aligned
+    # transposed copy of codes
+    tr = lambda rows, cols, q=fake, qt=fake, ld_q=None, ld_qt=None, batch=1: ops.fp8_transpose_codes(
+        q, batch, rows, cols, cols if ld_q is None else ld_q, qt, rows if ld_qt is None else ld_qt, stream=0,
+        raise_on_error=False)
+    assert tr(128, 120) == 2                      # cols % 16
+    assert tr(120, 128) == 2                      # rows % 16
+    assert tr(128, 128, batch=0) == 2
+    assert tr(128, 128, ld_qt=112) == 3           # ld_qt < rows
+    assert tr(128, 128, q=fake + 8) == 4          # q not 16-byte aligned
+    assert tr(128, 128, ld_qt=136) == 4           # ld_qt % 16
+    assert tr(128, 128, qt=None) == 1
+    assert tr(0, 128, q=None, qt=None) == 0
     # both axes of one tensor from one read
     dual = lambda rows, cols, mx=0, x=fake, ld_x=None, q=fake, qt=fake, ld_qt=None, st=fake: ops.fp8_quant_dual_axis(
         x, rows, cols, cols if ld_x is None else ld_x, mx, q, cols, fake, 1, 1, qt, rows if ld_qt is None else ld_qt,

@@ -230,6 +230,30 @@ def test_block2d_transposed_codes_only(shape):
         _assert_same_scales(s[b], sr)
 
 
+@pytest.mark.parametrize("shape", [(9728, 2560), (272, 208), (16, 16), (2, 400, 144), (128, 4096)])
+def test_transpose_codes(shape):
+    """fp8_transpose_codes on codes of the oracle's 128x128 quantization:
+    the result equals the transposed codes fp8_quant_block2d writes (and the
+    oracle's codes transposed), partial 128-tiles and a batch included; the
+    padding of the output rows stays untouched."""
+    w = _bits(shape, 8, 0.02, 0.0, 1.0)
+    ws = w if w.ndim == 3 else w[None]
+    B, R, C = ws.shape
+    _say("transpose codes", shape)
+    qr = np.stack([oracle.quant_128x128(ws[b])[0] for b in range(B)])
+    SENT = 0xA5
+    qt = torch.full((B, C, R + 16), SENT, dtype=torch.uint8, device="cuda")
+    ops.fp8_transpose_codes(dev(qr), B, R, C, C, qt, R + 16)
+    torch.cuda.synchronize()
+    for b in range(B):
+        _assert_same_codes(qt[b, :, :R], np.ascontiguousarray(qr[b].T))
+    assert torch.all(qt[:, :, R:] == SENT)
+    if B == 1:
+        _, _, qt2 = ops.quant_block2d(dev_bf16(ws[0]), transposed=True)
+        torch.cuda.synchronize()
+        assert torch.equal(qt2, qt[0, :, :R])
+
+
 # ------------------------------------------- both operands in one launch
 def _linear_check(x, w, qx, sx, qw, sw):
     qr, sr = oracle.quant_1x128(x)
