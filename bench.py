@@ -340,10 +340,10 @@ def wl_up_proj_pow2(torch, ops, inputs, to_dev, R):
     qx, sx, qw, sw = u8(M, K), u8(M, lds), u8(N, K), u8(N // 128, lds)
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     return [
-        ("quant_x_1x128_pow2", lambda i: ops.fp8_quant_pow2(xs[i % R], M, K, K, 1, qx, K, sx, lds),
-         ("GB/s", qbytes_row(M, K, 128, 1))),
-        ("quant_w_128x128_pow2", lambda i: ops.fp8_quant_pow2(w, N, K, K, 128, qw, K, sw, lds),
-         ("GB/s", N * K * 3 + (N // 128) * (K // 128))),
+        # X in 1x128 groups and W in 128x128 blocks, one launch, as fp8_quant_linear with FP32 scales
+        ("quant_linear_pow2", lambda i: ops.fp8_quant_linear_pow2(xs[i % R], M, K, K, qx, K, sx, lds, w, N, K, qw, K,
+                                                                 sw, lds),
+         ("GB/s", qbytes_row(M, K, 128, 1) + N * K * 3 + (N // 128) * (K // 128))),
         ("gemm_pow2_bf16", lambda i: ops.fp8_blockscaled_gemm_pow2(M, N, K, qx, K, sx, lds, qw, K, sw, lds, y, N,
                                                                   ops.OUT_BF16),
          ("TFLOP/s", 2.0 * M * N * K)),

@@ -38,6 +38,12 @@ hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols
                                    int64_t ld_q, float* s, hipStream_t st);
 hipError_t launch_quant_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int block_rows, uint8_t* q,
                              int64_t ld_q, uint8_t* s, int64_t ld_s, hipStream_t st);
+// Both operands with power-of-two block scales in one launch (as the two
+// launch_quant_pow2 calls, block_rows 1 for X and 128 for W).
+hipError_t launch_quant_linear_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx,
+                                    int64_t ld_qx, uint8_t* sx, int64_t ld_sx, const uint16_t* w, int64_t w_rows,
+                                    int64_t ld_w, uint8_t* qw, int64_t ld_qw, uint8_t* sw, int64_t ld_sw,
+                                    hipStream_t st);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st);
 
 // moe.hip

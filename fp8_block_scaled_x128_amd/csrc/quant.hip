@@ -710,11 +710,12 @@ struct LinearArgs {
     RowArgs x;
     int32_t x_blocks;
     const uint16_t* w; int32_t w_rows, cols; int64_t ld_w;
-    uint8_t* qw; int64_t ld_qw; float* sw;
-    int32_t nbr, nbc, w_blocks;
+    uint8_t* qw; int64_t ld_qw; void* sw;
+    int32_t nbr, nbc, lds_w, w_blocks;      // lds_w: row stride of W's block scales
 };
 
-template <bool ROW_FAST>
+// P2: power-of-two scales (UE8M0 bytes) for both operands, as fp8_quant_pow2.
+template <bool ROW_FAST, bool P2 = false>
 __global__ void __launch_bounds__(kThreads) k_quant_linear(LinearArgs a) {
     const int32_t b = (int32_t)blockIdx.x;
     // W blocks and X workgroups dealt in proportion (workgroup b is a W block
@@ -724,10 +725,10 @@ __global__ void __launch_bounds__(kThreads) k_quant_linear(LinearArgs a) {
     const int64_t n = (int64_t)a.w_blocks + a.x_blocks;
     const int32_t wb = (int32_t)((int64_t)b * a.w_blocks / n);
     if ((int32_t)(((int64_t)b + 1) * a.w_blocks / n) > wb)
-        block2d_body<false, false, false>(a.w, a.w_rows, a.cols, a.ld_w, a.qw, a.ld_qw, nullptr, 0, a.sw, a.nbr, a.nbc,
-                                          wb % a.nbc, wb / a.nbc, 0);
+        block2d_body<false, false, P2>(a.w, a.w_rows, a.cols, a.ld_w, a.qw, a.ld_qw, nullptr, 0, a.sw, a.nbr, a.lds_w,
+                                       wb % a.nbc, wb / a.nbc, 0);
     else
-        rowgroup_body<false, false, ROW_FAST, 4, false, false>(a.x, b - wb, a.x_blocks);
+        rowgroup_body<false, false, ROW_FAST, 4, false, P2>(a.x, b - wb, a.x_blocks);
 }
 
 __global__ void __launch_bounds__(kThreads) k_e4m3_encode(const float* __restrict__ in, uint8_t* __restrict__ out,
@@ -998,17 +999,10 @@ hipError_t launch_transpose_codes(const uint8_t* q, int64_t batch, int64_t rows,
     return hipGetLastError();
 }
 
-hipError_t launch_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx, int64_t ld_qx,
-                               float* sx, int64_t ssr, int64_t ssg, const uint16_t* w, int64_t w_rows, int64_t ld_w,
-                               uint8_t* qw, int64_t ld_qw, float* sw, hipStream_t st) {
-    // Tensors past the 256 MB last-level cache take the streaming policies of
-    // the separate kernels; the fused kernel serves the cached sizes.
-    const bool big = rows * cols > ((int64_t)256 << 20) || w_rows * cols * 2 > ((int64_t)256 << 20);
-    if (big || rows == 0 || w_rows == 0 || cols == 0) {
-        hipError_t e = launch_quant_128x128(w, 1, w_rows, cols, ld_w, qw, ld_qw, nullptr, 0, sw, st);
-        if (e != hipSuccess) return e;
-        return launch_quant_1x128(x, rows, cols, ld_x, qx, ld_qx, sx, ssr, ssg, st);
-    }
+static hipError_t launch_linear_pair(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx,
+                                     int64_t ld_qx, void* sx, int64_t ssr, int64_t ssg, const uint16_t* w,
+                                     int64_t w_rows, int64_t ld_w, uint8_t* qw, int64_t ld_qw, void* sw,
+                                     int64_t lds_w, bool p2, hipStream_t st) {
     LinearArgs a{};
     RowArgs& p = a.x;
     p.x = x; p.ld_x = ld_x; p.rows = (int32_t)rows; p.cols = (int32_t)cols; p.up_off = 0;
@@ -1028,13 +1022,48 @@ hipError_t launch_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, in
     a.qw = qw; a.ld_qw = ld_qw; a.sw = sw;
     a.nbr = (int32_t)((w_rows + 127) / 128);
     a.nbc = (int32_t)((cols + 127) / 128);
+    a.lds_w = (int32_t)lds_w;
     a.w_blocks = a.nbr * a.nbc;
     const dim3 grid((unsigned)(a.w_blocks + a.x_blocks));
-    if (ssr == 1 && ssg != 1)
+    if (p2)
+        hipLaunchKernelGGL((k_quant_linear<false, true>), grid, dim3(kThreads), 0, st, a);
+    else if (ssr == 1 && ssg != 1)
         hipLaunchKernelGGL(k_quant_linear<true>, grid, dim3(kThreads), 0, st, a);
     else
         hipLaunchKernelGGL(k_quant_linear<false>, grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
+}
+
+// Tensors past the 256 MB last-level cache take the streaming policies of
+// the separate kernels; the fused kernel serves the cached sizes.
+static bool linear_pair_fits(int64_t rows, int64_t w_rows, int64_t cols) {
+    const bool big = rows * cols > ((int64_t)256 << 20) || w_rows * cols * 2 > ((int64_t)256 << 20);
+    return !big && rows > 0 && w_rows > 0 && cols > 0;
+}
+
+hipError_t launch_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx, int64_t ld_qx,
+                               float* sx, int64_t ssr, int64_t ssg, const uint16_t* w, int64_t w_rows, int64_t ld_w,
+                               uint8_t* qw, int64_t ld_qw, float* sw, hipStream_t st) {
+    if (!linear_pair_fits(rows, w_rows, cols)) {
+        hipError_t e = launch_quant_128x128(w, 1, w_rows, cols, ld_w, qw, ld_qw, nullptr, 0, sw, st);
+        if (e != hipSuccess) return e;
+        return launch_quant_1x128(x, rows, cols, ld_x, qx, ld_qx, sx, ssr, ssg, st);
+    }
+    return launch_linear_pair(x, rows, cols, ld_x, qx, ld_qx, sx, ssr, ssg, w, w_rows, ld_w, qw, ld_qw, sw,
+                              (cols + 127) / 128, false, st);
+}
+
+hipError_t launch_quant_linear_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx,
+                                    int64_t ld_qx, uint8_t* sx, int64_t ld_sx, const uint16_t* w, int64_t w_rows,
+                                    int64_t ld_w, uint8_t* qw, int64_t ld_qw, uint8_t* sw, int64_t ld_sw,
+                                    hipStream_t st) {
+    if (!linear_pair_fits(rows, w_rows, cols)) {
+        hipError_t e = launch_quant_pow2(w, w_rows, cols, ld_w, 128, qw, ld_qw, sw, ld_sw, st);
+        if (e != hipSuccess) return e;
+        return launch_quant_pow2(x, rows, cols, ld_x, 1, qx, ld_qx, sx, ld_sx, st);
+    }
+    return launch_linear_pair(x, rows, cols, ld_x, qx, ld_qx, sx, ld_sx, 1, w, w_rows, ld_w, qw, ld_qw, sw, ld_sw, true,
+                              st);
 }
 
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, int64_t ld_q,

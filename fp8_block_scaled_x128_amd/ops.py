@@ -28,7 +28,7 @@ EXPORTS = ["fp8_quant_rowblock", "fp8_quant_block2d", "fp8_quant_linear", "fp8_q
            "fp8_blockscaled_gemm_splitk", "fp8_blockscaled_gemm_splitk_noalloc", "fp8_blockscaled_gemm_splitk_plan",
            "fp8_grouped_gemm", "fp8_grouped_gemm_ws_size", "fp8_grouped_gemm_swiglu_quant", "mxfp8_grouped_gemm_swiglu_quant",
            "fp8_silu_mul_quant", "fp8_moe_combine", "mxfp8_quant", "mxfp8_quant_t",
-           "fp8_quant_dual_axis", "fp8_transpose_codes",
+           "fp8_quant_dual_axis", "fp8_transpose_codes", "fp8_quant_linear_pow2",
            "fp8_quant_pow2", "fp8_blockscaled_gemm_pow2", "mxfp8_gemm", "fp8bs_e4m3_encode",
            "fp8bs_status_string", "fp8bs_last_error_detail"]
 
@@ -81,6 +81,7 @@ def load():
             "mxfp8_quant_t": [P, I64, I64, I64, P, I64, P, I64, I64, P],
             "fp8_quant_dual_axis": [P, I64, I64, I64, I32, P, I64, P, I64, I64, P, I64, P, I64, I64, P],
             "fp8_transpose_codes": [P, I64, I64, I64, I64, P, I64, P],
+            "fp8_quant_linear_pow2": [P, I64, I64, I64, P, I64, P, I64, P, I64, I64, P, I64, P, I64, P],
             "fp8_quant_pow2": [P, I64, I64, I64, I32, P, I64, P, I64, P],
             "fp8_blockscaled_gemm_pow2": [I64, I64, I64, P, I64, P, I64, P, I64, P, I64, P, I64, INT, P],
             "mxfp8_gemm": [I64, I64, I64, I32, P, P, I64, P, I64, P, I64, P, I64, I64, P, I64, I64, P, I64, INT, P],
@@ -262,6 +263,13 @@ def fp8_quant_dual_axis(x, rows, cols, ld_x, mx, q, ld_q, s, s_stride_row, s_str
     r = load().fp8_quant_dual_axis(_p(x), rows, cols, ld_x, mx, _p(q), ld_q, _p(s), s_stride_row, s_stride_group,
                                    _p(qt), ld_qt, _p(st), st_stride_row, st_stride_group, _stream(stream))
     return _check("fp8_quant_dual_axis", r, raise_on_error)
+
+
+def fp8_quant_linear_pow2(x, rows, cols, ld_x, qx, ld_qx, sx, ld_sx, w, w_rows, ld_w, qw, ld_qw, sw, ld_sw,
+                          stream=None, raise_on_error=True):
+    r = load().fp8_quant_linear_pow2(_p(x), rows, cols, ld_x, _p(qx), ld_qx, _p(sx), ld_sx, _p(w), w_rows, ld_w,
+                                     _p(qw), ld_qw, _p(sw), ld_sw, _stream(stream))
+    return _check("fp8_quant_linear_pow2", r, raise_on_error)
 
 
 def fp8_transpose_codes(q, batch, rows, cols, ld_q, q_t, ld_qt, stream=None, raise_on_error=True):

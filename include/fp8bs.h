@@ -500,6 +500,23 @@ fp8bs_status fp8_blockscaled_gemm_pow2(int64_t M, int64_t N, int64_t K, const ui
                                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_quant_linear_pow2 -- both operands of a linear layer with power-of-two
+ * block scales in one launch: X [rows][cols] in 1x128 groups and W
+ * [w_rows][cols] in 128x128 blocks, each scale the UE8M0 byte of
+ * fp8_quant_pow2 (same section of the same page).  The results are identical
+ * to fp8_quant_pow2(x, ..., block_rows 1, qx, ld_qx, sx, ld_sx) followed by
+ * fp8_quant_pow2(w, ..., block_rows 128, qw, ld_qw, sw, ld_sw); one grid
+ * carries both, as fp8_quant_linear does for FP32 scales.
+ * Either operand may be empty (rows == 0 or w_rows == 0; its pointers are
+ * then not read).  Requirements: as the two calls; the buffers of the two
+ * operands must not overlap.
+ * ------------------------------------------------------------------------ */
+fp8bs_status fp8_quant_linear_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx,
+                                   int64_t ld_qx, uint8_t* sx, int64_t ld_sx, const uint16_t* w, int64_t w_rows,
+                                   int64_t ld_w, uint8_t* qw, int64_t ld_qw, uint8_t* sw, int64_t ld_sw,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * mxfp8_quant -- MXFP8 quantization: 32 consecutive values along a row share
  * one UE8M0 scale ("Low Precision RL", section "3. Unified MXFP8
  * (Blackwell)").  The block exponent is the smallest integer e with

@@ -155,6 +155,16 @@ def test_host_validation_rejects_before_launch(lib):
                                              raise_on_error=False)
     assert b2(None, None) == 1
     assert b2(None, fake + 8) == 4                # q_t must be 16-byte aligned
+    # both operands with power-of-two scales
+    lp = lambda rows, w_rows, cols, ld_sx=None, ld_sw=None, sx=fake, sw=fake: ops.fp8_quant_linear_pow2(
+        fake, rows, cols, cols, fake, cols, sx, (cols + 127) // 128 if ld_sx is None else ld_sx, fake, w_rows, cols,
+        fake, cols, sw, (cols + 127) // 128 if ld_sw is None else ld_sw, stream=0, raise_on_error=False)
+    assert lp(4, 128, 100) == 2                   # cols % 8
+    assert lp(4, 128, 512, ld_sx=3) == 3          # ld_sx < ceil(cols / 128)
+    assert lp(4, 128, 512, ld_sw=3) == 3
+    assert lp(4, 128, 512, sw=None) == 1
+    assert lp(0, 128, 512, sx=None) != 1          # an empty X's pointers are not checked (no NULL error)
+    assert lp(0, 0, 512, sx=None, sw=None) == 0
     # transposed copy of codes
     tr = lambda rows, cols, q=fake, qt=fake, ld_q=None, ld_qt=None, batch=1: ops.fp8_transpose_codes(
         q, batch, rows, cols, cols if ld_q is None else ld_q, qt, rows if ld_qt is None else ld_qt, stream=0,

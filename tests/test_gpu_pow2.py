@@ -49,6 +49,37 @@ def test_quant_1x128_pow2(shape):
     _same(q, s, *oracle.quant_1x128_pow2(x))
 
 
+@pytest.mark.parametrize("rows,w_rows,cols", [(4096, 9728, 2560), (300, 200, 1000), (7, 130, 264), (0, 256, 512),
+                                             (256, 0, 512)])
+def test_quant_linear_pow2(rows, w_rows, cols):
+    """Both operands in one launch with power-of-two scales: codes and scale
+    bytes of X (1x128) and W (128x128) equal to the oracle's, with padded
+    scale rows (ld 4 * ceil(cols / 512), as the GEMM wants them); an empty
+    operand's buffers are left alone."""
+    _say("pow2 operand pair", rows, w_rows, cols)
+    x, w = _bits((max(rows, 1), cols), 72), _bits((max(w_rows, 1), cols), 73, 0.02)
+    g = (cols + 127) // 128
+    lds = 4 * ((cols + 511) // 512)
+    SENT = 0xA5
+    qx = torch.full((max(rows, 1), cols), SENT, dtype=torch.uint8, device="cuda")
+    sx = torch.full((max(rows, 1), lds), SENT, dtype=torch.uint8, device="cuda")
+    qw = torch.full((max(w_rows, 1), cols), SENT, dtype=torch.uint8, device="cuda")
+    sw = torch.full(((max(w_rows, 1) + 127) // 128, lds), SENT, dtype=torch.uint8, device="cuda")
+    ops.fp8_quant_linear_pow2(dev_bf16(x), rows, cols, cols, qx, cols, sx, lds, dev_bf16(w), w_rows, cols, qw, cols,
+                              sw, lds)
+    torch.cuda.synchronize()
+    if rows:
+        _same(qx, sx, *oracle.quant_1x128_pow2(x))
+        assert torch.all(sx[:, g:] == SENT)
+    else:
+        assert torch.all(qx == SENT) and torch.all(sx == SENT)
+    if w_rows:
+        _same(qw, sw, *oracle.quant_128x128_pow2(w))
+        assert torch.all(sw[:, g:] == SENT)
+    else:
+        assert torch.all(qw == SENT) and torch.all(sw == SENT)
+
+
 @pytest.mark.parametrize("shape", [(512, 512), (200, 264), (9728, 2560)])
 def test_quant_128x128_pow2(shape):
     _say("pow2 128x128", shape)
