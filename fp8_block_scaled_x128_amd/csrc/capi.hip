@@ -135,43 +135,14 @@ fp8bs_status fp8_quant_rowblock(const uint16_t* x, int64_t rows, int64_t cols, i
                     "fp8_quant_rowblock");
 }
 
-fp8bs_status fp8_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx, int64_t ld_qx,
-                              float* sx, int64_t sx_stride_row, int64_t sx_stride_group, const uint16_t* w,
-                              int64_t w_rows, int64_t ld_w, uint8_t* qw, int64_t ld_qw, float* sw,
-                              hipStream_t stream) {
-    if (rows < 0 || cols < 0 || w_rows < 0)
-        return fail(FP8BS_ERR_SHAPE, "rows=%lld cols=%lld w_rows=%lld", (long long)rows, (long long)cols,
-                    (long long)w_rows);
-    if (cols % 8) return fail(FP8BS_ERR_SHAPE, "cols %% 8 != 0 (cols=%lld)", (long long)cols);
-    if (rows * ((cols + 127) / 128) > kMaxRuns || rows > INT32_MAX / 2 || cols > INT32_MAX / 2 ||
-        w_rows > INT32_MAX / 2 || (w_rows + 127) / 128 > 65535 || ((w_rows + 127) / 128) * ((cols + 127) / 128) > kMaxRuns)
-        return fail(FP8BS_ERR_SHAPE, "tensor too large");
-    if (cols == 0 || (rows == 0 && w_rows == 0)) return ok();
-    if (rows > 0) {
-        if (!x || !qx || !sx) return fail(FP8BS_ERR_NULL, "x, qx and sx are required");
-        if (ld_x < cols || ld_qx < cols) return fail(FP8BS_ERR_STRIDE, "ld_x and ld_qx must be >= cols");
-        if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
-        if (ld_qx % 8 || !aligned(qx, 8)) return fail(FP8BS_ERR_ALIGN, "qx must be 8-byte aligned with ld_qx %% 8 == 0");
-        if (!aligned(sx, 4)) return fail(FP8BS_ERR_ALIGN, "sx must be 4-byte aligned");
-    }
-    if (w_rows > 0) {
-        if (!w || !qw || !sw) return fail(FP8BS_ERR_NULL, "w, qw and sw are required");
-        if (ld_w < cols || ld_qw < cols) return fail(FP8BS_ERR_STRIDE, "ld_w and ld_qw must be >= cols");
-        if (ld_w % 8 || !aligned(w, 16)) return fail(FP8BS_ERR_ALIGN, "w must be 16-byte aligned with ld_w %% 8 == 0");
-        if (ld_qw % 8 || !aligned(qw, 8)) return fail(FP8BS_ERR_ALIGN, "qw must be 8-byte aligned with ld_qw %% 8 == 0");
-        if (!aligned(sw, 4)) return fail(FP8BS_ERR_ALIGN, "sw must be 4-byte aligned");
-    }
-    fp8bs_status d = check_device();
-    if (d != FP8BS_OK) return d;
-    return launched(launch_quant_linear(x, rows, cols, ld_x, qx, ld_qx, sx, sx_stride_row, sx_stride_group, w, w_rows,
-                                        ld_w, qw, ld_qw, sw, stream),
-                    "fp8_quant_linear");
-}
-
-fp8bs_status fp8_quant_linear_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx,
-                                   int64_t ld_qx, uint8_t* sx, int64_t ld_sx, const uint16_t* w, int64_t w_rows,
-                                   int64_t ld_w, uint8_t* qw, int64_t ld_qw, uint8_t* sw, int64_t ld_sw,
-                                   hipStream_t stream) {
+// The checks both operand-pair entry points make: each operand as its own
+// quantizer call would check it (an empty operand's pointers are not read).
+// pow2: UE8M0 scale bytes with row strides ld_sx / ld_sw; otherwise fp32
+// scales, 4-byte aligned.
+static fp8bs_status linear_pair_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const uint8_t* qx,
+                                     int64_t ld_qx, const void* sx, int64_t ld_sx, const uint16_t* w, int64_t w_rows,
+                                     int64_t ld_w, const uint8_t* qw, int64_t ld_qw, const void* sw, int64_t ld_sw,
+                                     bool pow2) {
     if (rows < 0 || cols < 0 || w_rows < 0)
         return fail(FP8BS_ERR_SHAPE, "rows=%lld cols=%lld w_rows=%lld", (long long)rows, (long long)cols,
                     (long long)w_rows);
@@ -183,21 +154,42 @@ fp8bs_status fp8_quant_linear_pow2(const uint16_t* x, int64_t rows, int64_t cols
     const int64_t groups = (cols + 127) / 128;
     if (rows > 0) {
         if (!x || !qx || !sx) return fail(FP8BS_ERR_NULL, "x, qx and sx are required");
-        if (ld_x < cols || ld_qx < cols || ld_sx < groups)
-            return fail(FP8BS_ERR_STRIDE, "ld_x, ld_qx >= cols and ld_sx >= ceil(cols / 128) required");
+        if (ld_x < cols || ld_qx < cols) return fail(FP8BS_ERR_STRIDE, "ld_x and ld_qx must be >= cols");
+        if (pow2 && ld_sx < groups) return fail(FP8BS_ERR_STRIDE, "ld_sx must be >= ceil(cols / 128)");
         if (ld_x % 8 || !aligned(x, 16)) return fail(FP8BS_ERR_ALIGN, "x must be 16-byte aligned with ld_x %% 8 == 0");
         if (ld_qx % 8 || !aligned(qx, 8)) return fail(FP8BS_ERR_ALIGN, "qx must be 8-byte aligned with ld_qx %% 8 == 0");
+        if (!pow2 && !aligned(sx, 4)) return fail(FP8BS_ERR_ALIGN, "sx must be 4-byte aligned");
     }
     if (w_rows > 0) {
         if (!w || !qw || !sw) return fail(FP8BS_ERR_NULL, "w, qw and sw are required");
-        if (ld_w < cols || ld_qw < cols || ld_sw < groups)
-            return fail(FP8BS_ERR_STRIDE, "ld_w, ld_qw >= cols and ld_sw >= ceil(cols / 128) required");
-        if (ld_sw > INT32_MAX / 2) return fail(FP8BS_ERR_SHAPE, "ld_sw too large");
+        if (ld_w < cols || ld_qw < cols) return fail(FP8BS_ERR_STRIDE, "ld_w and ld_qw must be >= cols");
+        if (pow2 && ld_sw < groups) return fail(FP8BS_ERR_STRIDE, "ld_sw must be >= ceil(cols / 128)");
+        if (pow2 && ld_sw > INT32_MAX / 2) return fail(FP8BS_ERR_SHAPE, "ld_sw too large");
         if (ld_w % 8 || !aligned(w, 16)) return fail(FP8BS_ERR_ALIGN, "w must be 16-byte aligned with ld_w %% 8 == 0");
         if (ld_qw % 8 || !aligned(qw, 8)) return fail(FP8BS_ERR_ALIGN, "qw must be 8-byte aligned with ld_qw %% 8 == 0");
+        if (!pow2 && !aligned(sw, 4)) return fail(FP8BS_ERR_ALIGN, "sw must be 4-byte aligned");
     }
-    fp8bs_status d = check_device();
-    if (d != FP8BS_OK) return d;
+    return check_device();
+}
+
+fp8bs_status fp8_quant_linear(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx, int64_t ld_qx,
+                              float* sx, int64_t sx_stride_row, int64_t sx_stride_group, const uint16_t* w,
+                              int64_t w_rows, int64_t ld_w, uint8_t* qw, int64_t ld_qw, float* sw,
+                              hipStream_t stream) {
+    fp8bs_status v = linear_pair_args(x, rows, cols, ld_x, qx, ld_qx, sx, 0, w, w_rows, ld_w, qw, ld_qw, sw, 0, false);
+    if (v != FP8BS_OK || cols == 0 || (rows == 0 && w_rows == 0)) return v;
+    return launched(launch_quant_linear(x, rows, cols, ld_x, qx, ld_qx, sx, sx_stride_row, sx_stride_group, w, w_rows,
+                                        ld_w, qw, ld_qw, sw, stream),
+                    "fp8_quant_linear");
+}
+
+fp8bs_status fp8_quant_linear_pow2(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* qx,
+                                   int64_t ld_qx, uint8_t* sx, int64_t ld_sx, const uint16_t* w, int64_t w_rows,
+                                   int64_t ld_w, uint8_t* qw, int64_t ld_qw, uint8_t* sw, int64_t ld_sw,
+                                   hipStream_t stream) {
+    fp8bs_status v = linear_pair_args(x, rows, cols, ld_x, qx, ld_qx, sx, ld_sx, w, w_rows, ld_w, qw, ld_qw, sw, ld_sw,
+                                      true);
+    if (v != FP8BS_OK || cols == 0 || (rows == 0 && w_rows == 0)) return v;
     return launched(launch_quant_linear_pow2(x, rows, cols, ld_x, qx, ld_qx, sx, ld_sx, w, w_rows, ld_w, qw, ld_qw, sw,
                                              ld_sw, stream),
                     "fp8_quant_linear_pow2");
