@@ -35,7 +35,10 @@
  *    s[r * s_stride_row + g * s_stride_group].  The GEMMs read activation
  *    scales fastest when s_stride_row == 1 ("M-major", [groups][rows]).
  *  - Calls are thread-safe and keep no state between calls apart from the
- *    per-device code-object load on first use.
+ *    per-device code-object load on first use.  The one exception is
+ *    fp8_blockscaled_gemm_splitk_noalloc: its partials live in a device array
+ *    that the library holds on each GPU, shared by every such call there
+ *    (calls that overlap on one GPU race; see its declaration).
  */
 #ifndef FP8BS_H
 #define FP8BS_H
