@@ -1090,7 +1090,10 @@ hipError_t launch_quant_tensorwise(const uint16_t* x, int64_t rows, int64_t cols
     }
     const int64_t chunks = rows * (cols / 8);
     int64_t blocks = (chunks + kThreads * 8 - 1) / (kThreads * 8);
-    if (blocks > 256 * 2) blocks = 256 * 2;
+    // one workgroup per CU at most, each ending in one atomic on the scale
+    // cell: against 512 (and 2048) workgroups, X_up 22.8 -> 20.4 us, W_up
+    // 34.0 -> 33.4 us, 4096 x 9728 unchanged; 128 lost on the larger tensors
+    if (blocks > 256) blocks = 256;
     hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(1), 0, st, s);
     // 32-bit chunk indices when every index of the grid-stride loop fits
     if (chunks + (int64_t)blocks * kThreads * 8 < ((int64_t)1 << 32))
