@@ -351,14 +351,18 @@ __global__ void __launch_bounds__(kThreads) k_quant_col_t_lds(const uint16_t* __
 // one HBM read of the bf16 tensor (2 bytes per element instead of 4).
 // One workgroup per 128 x 128 tile; thread t holds rows 8 (t / 16) .. +7 and
 // columns 8 (t % 16) .. +7 of it.
-//   Row groups: the 16 lanes of a DPP row hold one tile row, as in the
-//   row-group quantizer.
+//   Row groups: the 16 lanes of a DPP row hold one tile row.  MX: the 1x32
+//   maxima by lane shuffles, as in the row-group quantizer.  FP32: each lane
+//   leaves its part of the row maximum in LDS, and after the barrier the
+//   column groups need, threads 128..255 form one row's scale and reciprocal
+//   each (not all 16 lanes of the row: two IEEE divisions saved per lane and
+//   row); the row codes are encoded after the second barrier.
 //   Column groups: per-lane maxima of the 8 rows (bf16 magnitudes, two per
 //   word, as in the transposed quantizer), then over the wave's 4 row
 //   phases, which make a 32x1 MX block; for 128x1 the 4 waves' maxima meet
-//   in LDS, where the first 128 threads turn them into one scale and
-//   reciprocal per column.  Column codes are packed along rows, so each lane
-//   writes 8 consecutive bytes of a transposed row.
+//   in LDS, where threads 0..127 turn them into one scale and reciprocal per
+//   column.  Column codes are packed along rows, so each lane writes 8
+//   consecutive bytes of a transposed row.
 // ---------------------------------------------------------------------------
 template <bool MX>
 __global__ void __launch_bounds__(kThreads) k_quant_dual(const uint16_t* __restrict__ x, int32_t rows, int32_t cols,
