@@ -254,6 +254,22 @@ def test_transpose_codes(shape):
         assert torch.equal(qt2, qt[0, :, :R])
 
 
+def test_transpose_codes_every_byte_value():
+    """The transpose moves bytes: random bytes (every value 0..255, the NaN
+    codes 0x7f and 0xff included) through strided views come out transposed
+    unchanged."""
+    rng = np.random.default_rng(9)
+    B, R, C = 2, 528, 400
+    q = rng.integers(0, 256, size=(B, R, C + 48), dtype=np.uint8)
+    qt = torch.zeros((B, C, R), dtype=torch.uint8, device="cuda")
+    qd = dev(q)
+    # the matrices start (C + 48) * R bytes apart; fp8_transpose_codes takes
+    # batch stride rows * ld_q, which this layout has
+    ops.fp8_transpose_codes(qd, B, R, C, C + 48, qt, R)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qt), np.ascontiguousarray(np.transpose(q[:, :, :C], (0, 2, 1))))
+
+
 # ------------------------------------------- both operands in one launch
 def _linear_check(x, w, qx, sx, qw, sw):
     qr, sr = oracle.quant_1x128(x)
