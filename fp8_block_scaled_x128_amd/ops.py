@@ -425,6 +425,34 @@ def gemm(a, sa, b, sb, bscale=BSCALE_BLOCK128, out_dtype=torch.bfloat16):
     return c
 
 
+def linear_forward(x: torch.Tensor, w: torch.Tensor, out_dtype=torch.bfloat16):
+    """Y = X W^T of the block-wise FP8 linear layer: X [T, in] in 1x128 groups
+    and W [out, in] in 128x128 blocks (one launch), then the block-scaled GEMM.
+    Returns (y, saved); saved = (qw, sw, x) is what linear_backward reads: the
+    weight's codes and scales (dgrad's operand is their transpose) and the
+    bf16 activation (quantized along tokens for wgrad)."""
+    qx, sx, qw, sw = quant_linear(x, w)
+    return gemm(qx, sx, qw, sw, BSCALE_BLOCK128, out_dtype), (qw, sw, x)
+
+
+def linear_backward(dy: torch.Tensor, saved):
+    """dX = dY W and dW = dY^T X, both fp32, of the layer linear_forward ran:
+    dY [T, out] in 1x128 groups (dgrad) and 128x1 groups along tokens (wgrad)
+    from one read, X in 128x1 groups along tokens, and W^T as the transposed
+    copy of the forward's codes with W's 128x128 scales read transposed."""
+    qw, sw, x = saved
+    assert dy.dtype == torch.bfloat16 and dy.dim() == 2 and dy.is_contiguous()
+    T, O = dy.shape
+    I = x.shape[1]
+    qdy, sdy, qdyt, sdyt = quant_dual_axis(dy)
+    qxt, sxt = quant_rowblock(x, AXIS_COL, "m_major")
+    qwt = _u8((I, O), dy.device)
+    fp8_transpose_codes(qw, 1, O, I, qw.stride(0), qwt, O)
+    dx = gemm(qdy, sdy, qwt, sw.t(), BSCALE_BLOCK128, torch.float32)
+    dw = gemm(qdyt, sdyt, qxt, sxt, BSCALE_ROW128, torch.float32)
+    return dx, dw
+
+
 def gemm_splitk(a, sa, b, sb, bscale=BSCALE_BLOCK128, out_dtype=torch.bfloat16, splits=0):
     """gemm() with the K slices split among grid rows (splits 0: the
     planner's count); the fp32 workspace is allocated here with torch."""
