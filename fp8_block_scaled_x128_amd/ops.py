@@ -453,6 +453,36 @@ def linear_backward(dy: torch.Tensor, saved):
     return dx, dw
 
 
+def moe_forward(x, qgu, sgu, qdt, sdt, offsets, row_token, token_rows, weights, out_dtype=torch.bfloat16):
+    """One block-wise FP8 MoE layer forward: X [T, H] in 1x128 groups; the
+    grouped gate/up GEMM over the experts' rows (gathered by row_token), with
+    SiLU*mul and the 1x128 requantization of h in its epilogue; the grouped
+    down GEMM; the routing-weighted combine.  Weights come quantized:
+    qgu [G, 2I, H] codes with sgu [G, 2I/128, H/128] (gate rows [0, I), up
+    rows [I, 2I)), qdt [G, H, I] codes of the down weights ([out][in]) with
+    sdt [G, I/128, H/128] (the blocks of the [in][out] stack, read transposed).
+    offsets int32 [G + 1] (device), row_token int32 [rows], token_rows int32
+    [T, k] (grouped row of each token's slot), weights fp32 [T, k]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous()
+    T, H = x.shape
+    G, N2, _ = qgu.shape
+    I = N2 // 2
+    rows = row_token.numel()
+    qx, sx = quant_rowblock(x, AXIS_ROW, "m_major")
+    qh = _u8((rows, I), x.device)
+    shb = torch.empty((I // 128, rows), dtype=torch.float32, device=x.device)
+    fp8_grouped_gemm_swiglu_quant(rows, I, H, G, offsets, row_token, T, qx, H, sx, sx.stride(0), sx.stride(1), qgu, H,
+                                  N2 * H, sgu, sgu.stride(0), sgu.stride(1), sgu.stride(2), qh, I, shb, 1, rows)
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device=x.device)
+    fp8_grouped_gemm(rows, H, I, G, offsets, None, rows, qh, I, shb, 1, rows, qdt, I, H * I, sdt, sdt.stride(0),
+                     sdt.stride(2), sdt.stride(1), y, H, OUT_BF16)
+    k = token_rows.shape[1]
+    out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    fp8_moe_combine(y, rows, H, H, token_rows.contiguous(), weights.contiguous(), T, k, out, H,
+                    OUT_FP32 if out_dtype == torch.float32 else OUT_BF16)
+    return out
+
+
 def gemm_splitk(a, sa, b, sb, bscale=BSCALE_BLOCK128, out_dtype=torch.bfloat16, splits=0):
     """gemm() with the K slices split among grid rows (splits 0: the
     planner's count); the fp32 workspace is allocated here with torch."""

@@ -54,3 +54,42 @@ def test_linear_forward_backward_match_the_entry_points():
     qwt_r = np.ascontiguousarray(qw_r.T)
     swt_r = np.ascontiguousarray(sw_r.T)
     verify(qd_r, sd_r, qwt_r, swt_r, host(dx))
+
+
+def test_moe_forward_matches_the_entry_points():
+    """ops.moe_forward on a scaled-down MoE layer (skewed routing with empty
+    experts): byte-identical to the chain of entry points it orders (X 1x128,
+    gathered gate/up GEMM with SiLU*mul and requantization, grouped down GEMM,
+    combine)."""
+    d = inputs.small_moe(seed=33, tokens=512, hidden=256, experts=8, inter=128, top_k=2)
+    r = d["routing"]
+    T, H = d["x"].shape
+    G, N2, _ = d["w_gu"].shape
+    I = N2 // 2
+    rows = int(r.offsets[-1])
+    x = dev_bf16(d["x"])
+    qgu, sgu, _ = ops.quant_block2d(dev_bf16(d["w_gu"]))
+    wd = dev_bf16(d["w_d"])
+    qdt = torch.empty((G, H, I), dtype=torch.uint8, device="cuda")
+    sdt = torch.empty((G, I // 128, H // 128), dtype=torch.float32, device="cuda")
+    ops.fp8_quant_block2d(wd, G, I, H, H, None, 0, qdt, I, sdt)
+    offs = torch.from_numpy(r.offsets).cuda()
+    a_rows = torch.from_numpy(r.row_token).cuda()
+    pos = torch.from_numpy(r.token_rows).cuda()
+    wts = torch.from_numpy(r.weights).cuda()
+    out = ops.moe_forward(x, qgu, sgu, qdt, sdt, offs, a_rows, pos, wts)
+    # the explicit chain
+    qx = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+    sx = torch.empty((H // 128, T), dtype=torch.float32, device="cuda")
+    ops.fp8_quant_rowblock(x, T, H, H, ops.AXIS_ROW, qx, H, sx, 1, T)
+    qh = torch.empty((rows, I), dtype=torch.uint8, device="cuda")
+    sh = torch.empty((I // 128, rows), dtype=torch.float32, device="cuda")
+    ops.fp8_grouped_gemm_swiglu_quant(rows, I, H, G, offs, a_rows, T, qx, H, sx, 1, T, qgu, H, N2 * H, sgu,
+                                      (N2 // 128) * (H // 128), H // 128, 1, qh, I, sh, 1, rows)
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    ops.fp8_grouped_gemm(rows, H, I, G, offs, None, rows, qh, I, sh, 1, rows, qdt, I, H * I, sdt,
+                         (I // 128) * (H // 128), 1, H // 128, y, H, ops.OUT_BF16)
+    out2 = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ops.fp8_moe_combine(y, rows, H, H, pos, wts, T, r.token_rows.shape[1], out2, H, ops.OUT_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
